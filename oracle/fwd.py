@@ -1,0 +1,226 @@
+"""Plain fp64 reference for the flexible-mask attention forward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed (MagiAttention quickstart, "Single-GPU Flex-Flash-Attention";
+FlagAttention user guide, "FlashAttention"):
+
+  For query token i and query head h, with key/value head g = h // (Hq // Hkv)
+  (contiguous GQA groups; the pages only require Hq % Hkv == 0):
+
+    V(i)      = union over slices s with qs <= i < qe of the keys
+                  j in [ks, ke)                         if s is FULL  (type 0)
+                  j in [ks, ke - (qe - 1 - i))          if s is CAUSAL (type 1)
+                (causal is bottom-right aligned: local row m of an M x N slice
+                 sees local keys n <= N - M + m)
+    s_ij      = scale * sum_d q[i,h,d] * k[j,g,d]          scale defaults to 1/sqrt(D)
+    lse[i,h]  = ln sum_{j in V(i)} exp(s_ij)                -inf when V(i) is empty
+    out[i,h]  = sum_{j in V(i)} exp(s_ij - lse[i,h]) v[j,g]  0 when V(i) is empty
+
+Ranges are half-open [start, end).  Slices may overlap here (the mask is the
+union); the HIP library rejects overlapping slices instead.
+
+The computation materialises the explicit boolean mask for a block of query
+rows, restricts the key axis to columns that some row of the block can see
+(exact: the others are zero in the mask), and evaluates softmax attention in
+float64 with numpy BLAS.  The row max is subtracted before exp only to avoid
+overflow; that is rounding order, not a different result.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+FULL = 0
+CAUSAL = 1
+
+
+def slice_row_interval(i: int, qs: int, qe: int, ks: int, ke: int, mask_type: int) -> Tuple[int, int]:
+    """Keys [a, b) that query row i sees through one slice (empty: a >= b).
+
+    FULL: every key of the slice.  CAUSAL: bottom-right aligned, so the last
+    query row of the slice sees every key and each earlier row one key fewer.
+    """
+    if not (qs <= i < qe):
+        return (0, 0)
+    if mask_type == FULL:
+        return (ks, ke)
+    if mask_type == CAUSAL:
+        return (ks, ke - (qe - 1 - i))
+    raise ValueError(f"unknown mask type {mask_type}")
+
+
+def row_intervals(i: int, q_ranges, k_ranges, mask_types) -> List[Tuple[int, int]]:
+    """Non-empty key intervals row i sees, one per slice covering the row."""
+    out = []
+    for (qs, qe), (ks, ke), t in zip(np.asarray(q_ranges).tolist(), np.asarray(k_ranges).tolist(),
+                                     np.asarray(mask_types).tolist()):
+        a, b = slice_row_interval(i, qs, qe, ks, ke, t)
+        if b > a:
+            out.append((a, b))
+    return out
+
+
+def mask_rows(rows: Sequence[int], q_ranges, k_ranges, mask_types, total_k: int) -> np.ndarray:
+    """Explicit boolean mask [len(rows), total_k]; True = key visible."""
+    rows = np.asarray(rows, dtype=np.int64)
+    m = np.zeros((rows.shape[0], total_k), dtype=bool)
+    cols = np.arange(total_k, dtype=np.int64)[None, :]
+    for (qs, qe), (ks, ke), t in zip(np.asarray(q_ranges).tolist(), np.asarray(k_ranges).tolist(),
+                                     np.asarray(mask_types).tolist()):
+        inside = (rows >= qs) & (rows < qe)
+        if not inside.any():
+            continue
+        if t == FULL:
+            end = np.full(rows.shape, ke, dtype=np.int64)
+        elif t == CAUSAL:
+            end = ke - (qe - 1 - rows)
+        else:
+            raise ValueError(f"unknown mask type {t}")
+        vis = (cols >= ks) & (cols < end[:, None]) & inside[:, None]
+        m |= vis
+    return m
+
+
+def dense_mask(q_ranges, k_ranges, mask_types, total_q: int, total_k: int) -> np.ndarray:
+    """The whole [total_q, total_k] boolean mask (small problems only)."""
+    return mask_rows(np.arange(total_q), q_ranges, k_ranges, mask_types, total_k)
+
+
+def count_visible_pairs(q_ranges, k_ranges, mask_types, total_q: int, total_k: int) -> int:
+    """Number of visible (query, key) pairs per head: the size of the union of intervals, row by row."""
+    total = 0
+    qr = np.asarray(q_ranges).tolist()
+    kr = np.asarray(k_ranges).tolist()
+    ty = np.asarray(mask_types).tolist()
+    # rows only change their interval set at slice q boundaries; walk rows explicitly
+    # but skip rows no slice covers.
+    covered = np.zeros(total_q, dtype=bool)
+    for (qs, qe) in qr:
+        covered[max(qs, 0):min(qe, total_q)] = True
+    for i in np.nonzero(covered)[0].tolist():
+        ivs = []
+        for (qs, qe), (ks, ke), t in zip(qr, kr, ty):
+            a, b = slice_row_interval(i, qs, qe, ks, ke, t)
+            a, b = max(a, 0), min(b, total_k)
+            if b > a:
+                ivs.append((a, b))
+        if not ivs:
+            continue
+        ivs.sort()
+        cur_a, cur_b = ivs[0]
+        for a, b in ivs[1:]:
+            if a > cur_b:
+                total += cur_b - cur_a
+                cur_a, cur_b = a, b
+            else:
+                cur_b = max(cur_b, b)
+        total += cur_b - cur_a
+    return total
+
+
+def _as_f64(x) -> np.ndarray:
+    """bf16/float torch tensor or numpy array -> float64 numpy (exact for bf16)."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return x.detach().to(torch.float64).cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def attend(q, k, v, q_ranges, k_ranges, mask_types, softmax_scale: Optional[float] = None,
+           rows: Optional[Sequence[int]] = None, block_rows: int = 256):
+    """Reference forward.  Returns (out [R,Hq,D] float64, lse [R,Hq] float64).
+
+    q [Tq,Hq,D], k/v [Tk,Hkv,D] (torch or numpy, any float dtype; converted
+    exactly to float64).  `rows` selects query rows (default: all).
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    if dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    grp = hq // hkv
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    rows = np.arange(tq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.shape[0], hq, d), dtype=np.float64)
+    lse = np.full((rows.shape[0], hq), -np.inf, dtype=np.float64)
+    for b0 in range(0, rows.shape[0], block_rows):
+        rb = rows[b0:b0 + block_rows]
+        mask = mask_rows(rb, q_ranges, k_ranges, mask_types, tk)
+        cols = np.nonzero(mask.any(axis=0))[0]
+        if cols.size == 0:
+            continue
+        mk = mask[:, cols]  # [B, C]
+        for g in range(hkv):
+            kg = k[cols, g, :]  # [C, D]
+            vg = v[cols, g, :]
+            for hh in range(grp):
+                h = g * grp + hh
+                s = (q[rb, h, :] @ kg.T) * scale  # [B, C]
+                s = np.where(mk, s, -np.inf)
+                mx = s.max(axis=1)
+                safe = np.where(np.isfinite(mx), mx, 0.0)
+                p = np.exp(s - safe[:, None])  # masked entries -> exp(-inf) = 0
+                den = p.sum(axis=1)
+                nonempty = den > 0
+                l = np.where(nonempty, safe + np.log(np.where(nonempty, den, 1.0)), -np.inf)
+                o = (p @ vg) / np.where(nonempty, den, 1.0)[:, None]
+                out[b0:b0 + rb.shape[0], h, :] = np.where(nonempty[:, None], o, 0.0)
+                lse[b0:b0 + rb.shape[0], h] = l
+    return out, lse
+
+
+def attend_dense(q, k, v, mask: np.ndarray, softmax_scale: Optional[float] = None):
+    """Softmax attention under an explicit [Tq, Tk] boolean mask (fp64)."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = np.zeros((tq, hq, d))
+    lse = np.full((tq, hq), -np.inf)
+    for h in range(hq):
+        g = h // grp
+        s = (q[:, h, :] @ k[:, g, :].T) * scale
+        s = np.where(mask, s, -np.inf)
+        mx = s.max(axis=1)
+        safe = np.where(np.isfinite(mx), mx, 0.0)
+        p = np.exp(s - safe[:, None])
+        den = p.sum(axis=1)
+        ne = den > 0
+        lse[:, h] = np.where(ne, safe + np.log(np.where(ne, den, 1.0)), -np.inf)
+        out[:, h, :] = np.where(ne[:, None], (p @ v[:, g, :]) / np.where(ne, den, 1.0)[:, None], 0.0)
+    return out, lse
+
+
+def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):
+    """Combine partial (out, lse) over disjoint key sets with a global logsumexp.
+
+    FlagAttention user guide, "Split-KV and paged attention": each split gives a
+    partial output and log-normalizer, and the partials merge through a global
+    logsumexp:  lse = ln sum_j exp(lse_j);  out = sum_j exp(lse_j - lse) out_j.
+    Partials whose lse is -inf (no visible key) carry no weight.
+    """
+    L = np.stack([np.asarray(x, dtype=np.float64) for x in lses])  # [n, ...]
+    O = np.stack([np.asarray(x, dtype=np.float64) for x in outs])  # [n, ..., D]
+    mx = L.max(axis=0)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    w = np.exp(L - safe)  # -inf -> 0
+    den = w.sum(axis=0)
+    ne = den > 0
+    lse = np.where(ne, safe + np.log(np.where(ne, den, 1.0)), -np.inf)
+    wn = np.where(ne, w / np.where(ne, den, 1.0), 0.0)
+    out = (wn[..., None] * O).sum(axis=0)
+    return out, lse
