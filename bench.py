@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the flexible-mask attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload packed_docs]
+                    [--no-cpu-baseline] [--split-tiles S]
+
+A step is one ffa_fwd call (main kernel, plus the split-K combine when the plan
+splits) over the whole workload, inputs resident in HBM.  The metric counts
+only unmasked FLOPs: 4 * D * Hq * (visible (q, k) pairs per head).  Timing uses
+HIP events recorded on the stream the kernels are launched on.
+
+Prints one JSON line.  `roofline` refers to the dominant kernel (ffa_fwd_main,
+bound by bf16 MFMA); `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+METRIC = "masked-attn fwd TFLOPS (unmasked FLOPs) and % of MI355X bf16 MFMA peak"
+WORKLOADS = {name: i for i, name in __import__("workloads").CONFIG_NAMES.items()}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="packed_docs", choices=sorted(WORKLOADS))
+    ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(p, q, k, v, budget_s: float):
+    """Time the fp64 oracle on whole 256-row blocks of the workload until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(1234)
+    nblk = (p.total_q + 255) // 256
+    order = rng.permutation(nblk)
+    # q, k, v as float64 once (conversion is not part of the timed oracle work)
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    done_rows, pairs, t_used = 0, 0, 0.0
+    for bi in order:
+        rows = np.arange(bi * 256, min(p.total_q, bi * 256 + 256))
+        t0 = time.perf_counter()
+        oracle.attend(qd, kd, vd, p.q_ranges, p.k_ranges, p.mask_types, rows=rows)
+        t_used += time.perf_counter() - t0
+        m = oracle.mask_rows(rows, p.q_ranges, p.k_ranges, p.mask_types, p.total_k)
+        pairs += int(m.sum())
+        done_rows += rows.size
+        if t_used >= budget_s:
+            break
+    flops = 4.0 * p.head_dim * p.heads_q * pairs
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done_rows} of {p.total_q} query rows ({done_rows // 256} seeded random 256-row blocks), "
+                  f"all heads, fp64 numpy BLAS; {t_used:.1f} s",
+        "seconds": t_used,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import flexible_mask_flash_amd as ffa
+    import workloads as W
+
+    ffa.load_library()
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    cfg = WORKLOADS[args.workload]
+    p = W.config(cfg)
+    q, k, v = W.make_qkv(p)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+
+    t0 = time.perf_counter()
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, split_tiles=args.split_tiles)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan.device_meta(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((p.total_q, p.heads_q), dtype=torch.float32, device=dev)
+    strides = {"q": (0, qd.stride(0), qd.stride(1)), "k": (0, kd.stride(0), kd.stride(1)),
+               "v": (0, vd.stride(0), vd.stride(1)), "out": (0, out.stride(0), out.stride(1)),
+               "lse": (0, lse.stride(0), lse.stride(1))}
+    scale = 1.0 / math.sqrt(p.head_dim)
+
+    def step():
+        ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)  # the stream ffa_fwd launches on
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_step = total_ms / args.steps
+    flops = 4.0 * p.head_dim * p.heads_q * plan.info["visible_pairs"]
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    med = float(np.median(per))
+
+    props = torch.cuda.get_device_properties(dev)
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": p.name,
+            **{k_: v_ for k_, v_ in p.describe().items() if k_ != "workload"},
+            "visible_pairs_per_head": int(plan.info["visible_pairs"]),
+            "flops_per_step": flops,
+            "plan": {k_: int(v_) for k_, v_ in plan.info.items()},
+            "plan_ms": round(plan_ms, 2),
+            "split_tiles": args.split_tiles,
+        },
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_median": round(med, 4),
+        "ms_min": round(min(per), 4),
+        "ms_max": round(max(per), 4),
+        "wall_s_timed": round(wall, 3),
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "ffa_fwd_main",
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(p, q, k, v, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

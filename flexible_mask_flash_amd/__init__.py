@@ -1,0 +1,371 @@
+"""Flexible-mask flash-attention forward for MI355X (gfx950).
+
+A thin ctypes binding over ``libffa.so`` (C ABI declared in ``include/ffa.h``).
+Python marshals arguments only: validation of the slices, planning and every
+step of the computation run in the library and its HIP kernels.  PyTorch is used
+for device memory and streams.  There is no fallback: if the library is missing
+or cannot be loaded, every entry point raises.
+
+API (names follow the pages):
+  flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, softmax_scale=None)
+      MagiAttention's single-GPU FFA interface, forward only; packed THD
+      tensors q [Tq,Hq,D], k/v [Tk,Hkv,D] (bf16) -> (out [Tq,Hq,D] bf16,
+      lse [Tq,Hq] fp32).
+  flash_attention(q, k, v, causal=False, sm_scale=None, ...)
+      FlagAttention's dense contract on [B,H,M,D] tensors (GQA, bottom-right
+      causal); returns out, or the 5-tuple (out, lse [B,Hq,M], None, None,
+      None) when an auxiliary flag is set.
+  Plan(...)  a reusable host plan (ffa_plan) with its device metadata.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from collections import OrderedDict
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "FFAError",
+    "Plan",
+    "flex_flash_attn_fwd",
+    "flash_attention",
+    "load_library",
+    "library_path",
+    "FULL",
+    "CAUSAL",
+]
+
+FULL = 0
+CAUSAL = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libffa.so")
+_lib = None
+_lib_lock = threading.Lock()
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+
+class FFAError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({detail})" if detail else f"{what}: status {status}")
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("split_tiles", _i32), ("max_splits", _i32), ("num_cus", _i32), ("flags", ctypes.c_uint32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("meta_bytes", _i64),
+        ("workspace_bytes", _i64),
+        ("visible_pairs", _i64),
+        ("computed_pairs", _i64),
+        ("num_items", _i32),
+        ("num_runs", _i32),
+        ("num_combine", _i32),
+        ("num_split_items", _i32),
+        ("heads_per_item", _i32),
+        ("rows_per_item", _i32),
+        ("block_n", _i32),
+        ("max_item_tiles", _i32),
+        ("total_tiles", _i64),
+    ]
+
+
+# (name, restype, argtypes) of every function in include/ffa.h
+_SIGNATURES = [
+    ("ffa_abi_version", _i32, []),
+    ("ffa_status_string", ctypes.c_char_p, [_i32]),
+    ("ffa_last_error", ctypes.c_char_p, []),
+    ("ffa_plan", _i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PlanOpts),
+                        ctypes.POINTER(_vp)]),
+    ("ffa_plan_info_get", _i32, [_vp, ctypes.POINTER(PlanInfo)]),
+    ("ffa_plan_upload", _i32, [_vp, _vp, _sz, _vp]),
+    ("ffa_plan_export", _i32, [_vp, _vp, _sz]),
+    ("ffa_fwd", _i32, [_vp, _vp, _i32,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _f32, _vp, _sz, _vp]),
+    ("ffa_plan_destroy", None, [_vp]),
+]
+
+ABI_VERSION = 1
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libffa.so (built by ``python -m flexible_mask_flash_amd.build``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise FFAError(-1, "libffa.so is not built",
+                           f"expected {_LIB_PATH}; run `python -m flexible_mask_flash_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, res, args in _SIGNATURES:
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if lib.ffa_abi_version() != ABI_VERSION:
+            raise FFAError(-1, "libffa.so ABI mismatch", f"{lib.ffa_abi_version()} != {ABI_VERSION}")
+        _lib = lib
+        return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = load_library()
+        detail = lib.ffa_last_error().decode(errors="replace")
+        name = lib.ffa_status_string(status).decode(errors="replace")
+        raise FFAError(status, what, f"{name}: {detail}")
+
+
+def _host_i32(x, shape_tail) -> np.ndarray:
+    """Ranges / types as a contiguous host int32 array (device tensors are copied: this syncs)."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu").numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+    a = a.reshape((-1,) + shape_tail) if a.size else np.zeros((0,) + shape_tail, dtype=np.int64)
+    if a.size and (a.min() < -(2 ** 31) or a.max() >= 2 ** 31):
+        raise ValueError("range values do not fit int32")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+class Plan:
+    """A validated work plan for one mask and problem shape (ffa_plan)."""
+
+    def __init__(self, q_ranges, k_ranges, mask_types, total_q: int, total_k: int, heads_q: int,
+                 heads_kv: int, head_dim: int, split_tiles: int = 0, max_splits: int = 0,
+                 num_cus: int = 0, natural_order: bool = False):
+        lib = load_library()
+        qr = _host_i32(q_ranges, (2,))
+        kr = _host_i32(k_ranges, (2,))
+        ty = _host_i32(mask_types, ())
+        if not (qr.shape[0] == kr.shape[0] == ty.shape[0]):
+            raise ValueError("q_ranges, k_ranges and mask types must have the same number of slices")
+        self.q_ranges, self.k_ranges, self.mask_types = qr, kr, ty
+        self.total_q, self.total_k = int(total_q), int(total_k)
+        self.heads_q, self.heads_kv, self.head_dim = int(heads_q), int(heads_kv), int(head_dim)
+        opts = PlanOpts(int(split_tiles), int(max_splits), int(num_cus), 1 if natural_order else 0)
+        h = _vp()
+        st = lib.ffa_plan(qr.ctypes.data if qr.size else None, kr.ctypes.data if kr.size else None,
+                          ty.ctypes.data if ty.size else None, int(qr.shape[0]), self.total_q, self.total_k,
+                          self.heads_q, self.heads_kv, self.head_dim, ctypes.byref(opts), ctypes.byref(h))
+        _check(st, "ffa_plan")
+        self._h = h
+        inf = PlanInfo()
+        _check(lib.ffa_plan_info_get(self._h, ctypes.byref(inf)), "ffa_plan_info_get")
+        self.info = {name: getattr(inf, name) for name, _ in PlanInfo._fields_}
+        self._meta = {}  # device index -> torch int32 tensor
+        self._ws = {}    # device index -> torch uint8 tensor
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.ffa_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def meta_host(self) -> np.ndarray:
+        """The plan metadata as the device sees it (ffa_plan_export)."""
+        lib = load_library()
+        n = int(self.info["meta_bytes"])
+        buf = np.zeros(n // 4, dtype=np.int32)
+        _check(lib.ffa_plan_export(self._h, buf.ctypes.data, n), "ffa_plan_export")
+        return buf
+
+    def device_meta(self, device, stream=None):
+        """Device copy of the metadata (ffa_plan_upload), cached per device."""
+        import torch
+
+        dev = torch.device(device)
+        key = dev.index if dev.index is not None else torch.cuda.current_device()
+        t = self._meta.get(key)
+        if t is None:
+            n = int(self.info["meta_bytes"])
+            t = torch.empty(max(1, n // 4), dtype=torch.int32, device=torch.device("cuda", key))
+            s = torch.cuda.current_stream(key) if stream is None else stream
+            _check(load_library().ffa_plan_upload(self._h, t.data_ptr(), n, s.cuda_stream), "ffa_plan_upload")
+            self._meta[key] = t
+        return t
+
+    def workspace(self, device, batch: int = 1):
+        import torch
+
+        need = int(self.info["workspace_bytes"]) * int(batch)
+        if need == 0:
+            return None, 0
+        dev = torch.device(device)
+        key = dev.index if dev.index is not None else torch.cuda.current_device()
+        t = self._ws.get(key)
+        if t is None or t.numel() < need:
+            t = torch.empty(need, dtype=torch.uint8, device=torch.device("cuda", key))
+            self._ws[key] = t
+        return t, need
+
+
+_plan_cache: "OrderedDict[tuple, Plan]" = OrderedDict()
+_PLAN_CACHE_MAX = 16
+
+
+def _cached_plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles) -> Plan:
+    key = (qr.tobytes(), kr.tobytes(), ty.tobytes(), tq, tk, hq, hkv, d, split_tiles)
+    p = _plan_cache.get(key)
+    if p is None:
+        p = Plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles=split_tiles)
+        _plan_cache[key] = p
+        if len(_plan_cache) > _PLAN_CACHE_MAX:
+            _plan_cache.popitem(last=False)
+    else:
+        _plan_cache.move_to_end(key)
+    return p
+
+
+def _require_bf16_cuda(name, t, ndim):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous head_dim")
+
+
+def run_fwd(plan: Plan, q, k, v, out, lse, strides, batch: int, softmax_scale: float):
+    """Call ffa_fwd.  strides: dict of (sb, st, sh) per tensor, in elements."""
+    import torch
+
+    dev = q.device
+    s = torch.cuda.current_stream(dev)
+    meta = plan.device_meta(dev, s)
+    ws, ws_bytes = plan.workspace(dev, batch)
+    lib = load_library()
+    qs, ks, vs, os_, ls = strides["q"], strides["k"], strides["v"], strides["out"], strides["lse"]
+    st = lib.ffa_fwd(plan.handle, meta.data_ptr(), int(batch),
+                     q.data_ptr(), *qs,
+                     k.data_ptr(), *ks,
+                     v.data_ptr(), *vs,
+                     out.data_ptr(), *os_,
+                     lse.data_ptr(), *ls,
+                     float(softmax_scale), ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
+    _check(st, "ffa_fwd")
+
+
+def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
+                        softmax_scale: Optional[float] = None, softcap: float = 0.0,
+                        plan: Optional[Plan] = None, split_tiles: int = 0):
+    """Forward of flexible-mask attention on packed THD tensors -> (out, lse).
+
+    q [Tq,Hq,D], k/v [Tk,Hkv,D] bf16 device tensors (head_dim contiguous);
+    q_ranges / k_ranges int32 [S,2], attn_type_map int32 [S] (0 full, 1 causal),
+    host or device (device ranges are copied to the host, which synchronises).
+    Returns out [Tq,Hq,D] bf16 and lse [Tq,Hq] fp32 (natural log; -inf and a
+    zero output for rows that see no key).
+    """
+    import torch
+
+    if sink is not None:
+        raise NotImplementedError("attention sink is not supported by this forward")
+    if softcap:
+        raise NotImplementedError("softcap is not supported by this forward")
+    _require_bf16_cuda("q", q, 3)
+    _require_bf16_cuda("k", k, 3)
+    _require_bf16_cuda("v", v, 3)
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    if v.shape != k.shape or dk != d:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if plan is None:
+        qr = _host_i32(q_ranges, (2,))
+        kr = _host_i32(k_ranges, (2,))
+        ty = _host_i32(attn_type_map, ())
+        plan = _cached_plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles)
+    elif (plan.total_q, plan.total_k, plan.heads_q, plan.heads_kv, plan.head_dim) != (tq, tk, hq, hkv, d):
+        raise ValueError("plan was built for another shape")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    strides = {
+        "q": (0, q.stride(0), q.stride(1)),
+        "k": (0, k.stride(0), k.stride(1)),
+        "v": (0, v.stride(0), v.stride(1)),
+        "out": (0, out.stride(0), out.stride(1)),
+        "lse": (0, lse.stride(0), lse.stride(1)),
+    }
+    run_fwd(plan, q, k, v, out, lse, strides, 1, scale)
+    return out, lse
+
+
+def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = None, dropout_p: float = 0.0,
+                    return_log_normalizer: bool = False, return_total_attention: bool = False,
+                    return_seed_offset: bool = False, split_tiles: int = 0):
+    """FlagAttention-style dense attention forward on [B, H, M, D] tensors.
+
+    q [B,Hq,M,D], k/v [B,Hkv,N,D] bf16; Hq % Hkv == 0; causal is bottom-right
+    aligned.  Every batch element is one slice of a shared plan; the kernels
+    read the [B,H,M,D] layout through strides (no copies).
+    """
+    import torch
+
+    if dropout_p:
+        raise NotImplementedError("dropout is not supported by this forward")
+    if return_total_attention:
+        raise NotImplementedError("return_total_attention is not supported by this forward")
+    if return_seed_offset:
+        raise NotImplementedError("return_seed_offset needs dropout, which is not supported")
+    _require_bf16_cuda("q", q, 4)
+    _require_bf16_cuda("k", k, 4)
+    _require_bf16_cuda("v", v, 4)
+    b, hq, m, d = q.shape
+    bk, hkv, n, dk = k.shape
+    if v.shape != k.shape or bk != b or dk != d:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    ty = CAUSAL if causal else FULL
+    plan = _cached_plan(np.array([[0, m]], np.int32), np.array([[0, n]], np.int32), np.array([ty], np.int32),
+                        m, n, hq, hkv, d, split_tiles)
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    out = torch.empty((b, hq, m, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((b, hq, m), dtype=torch.float32, device=q.device)
+    strides = {
+        "q": (q.stride(0), q.stride(2), q.stride(1)),
+        "k": (k.stride(0), k.stride(2), k.stride(1)),
+        "v": (v.stride(0), v.stride(2), v.stride(1)),
+        "out": (out.stride(0), out.stride(2), out.stride(1)),
+        "lse": (lse.stride(0), lse.stride(2), lse.stride(1)),
+    }
+    run_fwd(plan, q, k, v, out, lse, strides, b, scale)
+    if return_log_normalizer:
+        return out, lse, None, None, None
+    return out

@@ -1,0 +1,72 @@
+"""Build libffa.so for gfx950 with hipcc (in-tree, no JIT cache).
+
+    python -m flexible_mask_flash_amd.build [--asm]
+
+--asm also writes the device assembly next to the library (for inspection of
+register use, waitcnt placement and MFMA scheduling).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libffa.so")
+ARCH = "gfx950"
+
+SOURCES = ["ffa_plan.cpp", "ffa_fwd.hip"]
+
+# Packed fp32 VALU ops are disabled: the compiler must not form v_pk_{add,mul,fma}_f32.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libffa.so)")
+
+
+def build(verbose: bool = False, asm: bool = False) -> str:
+    """Compile every source and link libffa.so; returns the library path."""
+    cc = hipcc()
+    objs = []
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    common = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(bdir, src + ".o")
+        cmd = [cc, *common]
+        if src.endswith(".hip"):
+            cmd += DEVICE_FLAGS
+        else:
+            cmd += ["-x", "c++"]
+        cmd += ["-c", path, "-o", obj]
+        _run(cmd, verbose)
+        objs.append(obj)
+        if asm and src.endswith(".hip"):
+            s_out = os.path.join(bdir, src + f".{ARCH}.s")
+            _run([cc, *common, *DEVICE_FLAGS, "--cuda-device-only", "-S", path, "-o", s_out], verbose)
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "is not a recognized feature for this target" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, asm="--asm" in sys.argv))

@@ -1,0 +1,625 @@
+// gfx950 (MI355X) kernels and the C ABI of the flexible-mask attention forward.
+//
+// Main kernel (one workgroup = 4 wavefronts per plan item):
+//   * wavefront w covers 32 query rows of one query head; the workgroup covers
+//     rows_per_item rows x heads_per_item heads that share one kv head, so a
+//     K/V tile staged in LDS serves 128 (row, head) pairs.
+//   * S^T = K Q^T per 64-key tile with v_mfma_f32_32x32x16_bf16: K is the A
+//     operand (read from LDS), Q^T the B operand (held in registers for the
+//     whole item).  Each lane then owns one query column and 16 keys per
+//     32-key block, so the row max needs one cross-half exchange
+//     (v_permlane32_swap) and the row sum stays per lane until the end.
+//   * O^T += V^T P^T with the same MFMA: P^T comes straight from the S^T
+//     registers (bf16), V^T from LDS with ds_read_b64_tr_b16 (4 keys of one
+//     head-dim column per lane, two reads per MFMA operand).
+//   * online softmax in fp32, base 2 (scale * log2 e folded into one FMA);
+//     the running max is only moved when it grows by more than 2^8, so the
+//     rescale of the accumulator is rare (the result is the same: every term
+//     uses one reference point per row).
+//   * K and V tiles are double-buffered in LDS and filled by
+//     global_load_lds_dwordx4 (HBM -> LDS without registers), XOR-swizzled by
+//     key row so that both the K row reads and the V transposed reads are
+//     free of bank conflicts.
+//   * causal / ragged edges are masked only on tiles past the item's n_full.
+//   * the epilogue writes bf16 out and fp32 lse, or -- for split items --
+//     fp32 partial (out, lse) that ffa_combine merges with a global logsumexp
+//     (FlagAttention user guide, "Split-KV and paged attention").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <type_traits>
+
+#include "ffa_internal.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+#define FFA_LDS __attribute__((address_space(3)))
+// plan records are read-only for the kernels: reading them through the constant
+// address space lets the compiler use scalar loads
+#define FFA_CONST __attribute__((address_space(4)))
+
+namespace {
+
+using ffa::kBlockN;
+using ffa::kRec;
+using ffa::kSlotsPerItem;
+
+struct FwdArgs {
+  const int32_t* items;
+  const int32_t* runs;
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* out;
+  float* lse;
+  int64_t q_sb, q_st, q_sh;
+  int64_t k_sb, k_st, k_sh;
+  int64_t v_sb, v_st, v_sh;
+  int64_t o_sb, o_st, o_sh;
+  int64_t l_sb, l_st, l_sh;
+  float* ws_o;       // [batch][slots][D]
+  float* ws_lse;     // [batch][slots]
+  int64_t ws_slots;  // slots per batch element
+  float scale_log2;  // softmax_scale * log2(e)
+  int32_t total_k;
+  int32_t batch;
+  int32_t heads_per_item;
+  int32_t kv_ratio;  // heads_q / heads_kv
+};
+
+struct CombineArgs {
+  const int32_t* combine;
+  const float* ws_o;
+  const float* ws_lse;
+  int64_t ws_slots;
+  __bf16* out;
+  float* lse;
+  int64_t o_sb, o_st, o_sh;
+  int64_t l_sb, l_st, l_sh;
+  int32_t batch;
+  int32_t heads_per_item;
+};
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: the running max may lag by up to 2^8
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// LDS row swizzles (16-byte chunk index XOR), see the header comment.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4 of
+// the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12 of the group.
+// Pointing lane j at row (key0 + j/4), columns (c0 + 4*(j%4) .. +3) therefore
+// hands lane i the column c0 + i of rows key0 .. key0+3.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
+  s16x4_t r;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const FFA_LDS char*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+// Workgroup barrier without a memory fence (the LDS waits are explicit), but a
+// compiler barrier for memory operations on both sides.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float partner_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float partner_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
+  constexpr int BN = kBlockN;          // 64 keys per tile
+  constexpr int CH = D / 8;            // 16-byte chunks per K/V row
+  constexpr int KSTEPS = D / 16;       // MFMA k-steps of Q K^T
+  constexpr int DBLK = D / 32;         // 32-wide head-dim blocks of O
+  constexpr int TILE = BN * D * 2;     // bytes of one K or V tile
+  constexpr int NLD = TILE / 4096;     // 16-byte DMA loads per thread per tile (K or V)
+  static_assert(BN == 64, "tile shape");
+  // Four distinct LDS objects (not one array): with the buffer chosen at compile
+  // time the compiler can tell a DMA into one buffer from reads of the other and
+  // does not drain the prefetch before every LDS read.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+
+  const int bid = blockIdx.x;
+  const int item_idx = bid / a.batch;
+  const int b = bid - item_idx * a.batch;
+  const FFA_CONST int32_t* itp = (const FFA_CONST int32_t*)(a.items + (int64_t)item_idx * kRec);
+  const int q0 = itp[0], nrows = itp[1], h0 = itp[2], run_off = itp[3], n_runs = itp[4];
+  const int slot = itp[5], total_tiles = itp[6];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5;            // which half of the 64 lanes
+  const int G = a.heads_per_item;
+  const int g = wave % G, rsub = wave / G;
+  const int h = h0 + g;
+  const int hk = h0 / a.kv_ratio;
+  const int lrow = rsub * 32 + (lane & 31);
+  const int row = q0 + lrow;
+  const bool row_ok = lrow < nrows;
+
+  const __bf16* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
+  const __bf16* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
+
+  // ---- Q^T operand: lane holds query `row`, head-dim half hh (contiguous D/2 values)
+  bf16x8_t qf[KSTEPS];
+  if (row_ok && n_runs > 0) {
+    const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh +
+                                                           (int64_t)row * a.q_st + hh * (D / 2));
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = qp[s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[s][j] = (__bf16)0.0f;
+  }
+
+  f32x16_t o[DBLK];
+#pragma unroll
+  for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[d][i] = 0.0f;
+  float m_run = -INFINITY;  // running max, log2 units (already scaled)
+  float l_run = 0.0f;       // this lane's part of the row sum
+
+  // ---- tile loader: K and V tile at key `kstart` into buffer BUF
+  auto load_tile = [&](auto buf_tag, int kstart) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    char* kdst = BUF == 0 ? k_lds0 : k_lds1;
+    char* vdst = BUF == 0 ? v_lds0 : v_lds1;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int blk = i * 4 + wave;     // this wave's 1 KB block of the tile
+      const int lin = blk * 64 + lane;  // 16-byte chunk index in the tile
+      const int r = lin / CH, p = lin % CH;
+      const int key = min(kstart + r, a.total_k - 1);  // rows past the data are masked later
+      const __bf16* ks = kbase + (int64_t)key * a.k_st + ((p ^ swz_k<D>(r)) * 8);
+      const __bf16* vs = vbase + (int64_t)key * a.v_st + ((p ^ swz_v<D>(r)) * 8);
+      __builtin_amdgcn_global_load_lds((const void*)ks, (FFA_LDS void*)(kdst + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vs, (FFA_LDS void*)(vdst + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  // ---- run iterator (wave-uniform)
+  const FFA_CONST int32_t* rp = (const FFA_CONST int32_t*)(a.runs + (int64_t)run_off * kRec);
+  int ri = 0, ti = 0;
+  int r_k0 = 0, r_nt = 0, r_nf = 0, r_khi = 0, r_eb = 0;
+  if (total_tiles > 0) {
+    r_k0 = rp[0]; r_nt = rp[1]; r_nf = rp[2]; r_khi = rp[3]; r_eb = rp[4];
+    load_tile(std::integral_constant<int, 0>{}, r_k0);
+  }
+
+  const float c2 = a.scale_log2;
+  const int grp = lane >> 4, jl = lane & 15;
+
+  // One pipeline step: prefetch tile it+1 into the other buffer, then compute
+  // tile `it` from buffer BUF.
+  auto step = [&](auto buf_tag, int it) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const char* ks = BUF == 0 ? k_lds0 : k_lds1;
+    const char* vs = BUF == 0 ? v_lds0 : v_lds1;
+    // next tile position
+    int n_ri = ri, n_ti = ti + 1, n_k0 = r_k0;
+    if (n_ti >= r_nt && it + 1 < total_tiles) {
+      n_ri = ri + 1;
+      n_ti = 0;
+      n_k0 = rp[n_ri * kRec + 0];
+    }
+    if (it + 1 < total_tiles) {
+      load_tile(std::integral_constant<int, 1 - BUF>{}, n_k0 + n_ti * BN);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NLD));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    wg_barrier();
+
+    const int kstart = r_k0 + ti * BN;
+
+    // ---- S^T = K Q^T  (two 32-key blocks)
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.0f;
+      const int r = kb * 32 + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int c = (D / 16) * hh + s;
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + r * (D * 2) + ((c ^ swz_k<D>(r)) * 16));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- edge mask: key j (absolute) visible iff j < min(k_hi, row + edge_base)
+    if (ti >= r_nf) {
+      const int lim = min(r_khi, row + r_eb) - kstart;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rel = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (rel >= lim) sacc[kb][i] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (base 2)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = partner_max(mx) * c2;
+    const float m_new = fmaxf(m_run, mx);
+    const bool need = m_new > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      if (need) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
+    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c2, -msub));
+        l_run += p;
+        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
+      }
+
+    // ---- O^T += V^T P^T
+    // The transposed reads go through inline asm: the compiler has no alias
+    // information for them and would otherwise drain the in-flight prefetch of
+    // the other buffer before the first one.  Their results are waited for
+    // explicitly (lgkmcnt) before the MFMAs use them.
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {  // 16 keys per MFMA
+      const int key_lo = 16 * t + 4 * hh + (jl >> 2);
+      s16x4_t vlo[DBLK], vhi[DBLK];
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) {
+        const int dcol = 32 * d + 16 * (grp & 1) + 4 * (jl & 3);
+        const int c = dcol >> 3, half = (dcol >> 2) & 1;
+        const int r0 = key_lo, r1 = key_lo + 8;
+        vlo[d] = lds_read_tr16(vs + r0 * (D * 2) + ((c ^ swz_v<D>(r0)) * 16) + half * 8);
+        vhi[d] = lds_read_tr16(vs + r1 * (D * 2) + ((c ^ swz_v<D>(r1)) * 16) + half * 8);
+      }
+      // wait for the transposed reads, and make every result depend on that
+      // wait so that no MFMA can be scheduled above it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) asm volatile("" : "+v"(vlo[d]), "+v"(vhi[d]));
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) {
+        const s16x8_t vv = {vlo[d][0], vlo[d][1], vlo[d][2], vlo[d][3], vhi[d][0], vhi[d][1], vhi[d][2], vhi[d][3]};
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[t], o[d], 0, 0, 0);
+      }
+    }
+
+    // every LDS read of this buffer has returned before the barrier that lets
+    // the next prefetch overwrite it
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();
+
+    // advance the iterator
+    if (n_ri != ri) {
+      ri = n_ri;
+      r_k0 = rp[ri * kRec + 0]; r_nt = rp[ri * kRec + 1]; r_nf = rp[ri * kRec + 2];
+      r_khi = rp[ri * kRec + 3]; r_eb = rp[ri * kRec + 4];
+    }
+    ti = n_ti;
+  };
+
+  for (int it = 0; it < total_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < total_tiles) step(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  // ---- epilogue
+  const float lsum = partner_sum(l_run);
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  const float lse_v = lsum > 0.0f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+  if (!row_ok) return;
+  if (slot < 0) {
+    __bf16* op = a.out + (int64_t)b * a.o_sb + (int64_t)row * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[d][4 * gq + e] * inv);
+        *reinterpret_cast<bf16x4_t*>(op + 32 * d + 8 * gq + 4 * hh) = w;
+      }
+    if (hh == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)h * a.l_sh] = lse_v;
+  } else {
+    const int64_t sidx = (int64_t)b * a.ws_slots + slot + lrow * G + g;
+    float* op = a.ws_o + sidx * D;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = o[d][4 * gq + e] * inv;
+        *reinterpret_cast<f32x4_t*>(op + 32 * d + 8 * gq + 4 * hh) = w;
+      }
+    if (hh == 0) a.ws_lse[sidx] = lse_v;
+  }
+}
+
+// Merge split partials: lse = ln sum_c exp(lse_c); out = sum_c exp(lse_c - lse) out_c.
+// One workgroup per combine entry (up to 128 (row, head) pairs); D/4 lanes per pair.
+template <int D>
+__global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
+  constexpr int TPP = D / 4;          // threads per (row, head) pair
+  constexpr int PPP = 256 / TPP;      // pairs per pass
+  const int bid = blockIdx.x;
+  const int ci = bid / a.batch;
+  const int b = bid - ci * a.batch;
+  const FFA_CONST int32_t* cp = (const FFA_CONST int32_t*)(a.combine + (int64_t)ci * kRec);
+  const int q0 = cp[0], nrows = cp[1], h0 = cp[2], nch = cp[3], slot0 = cp[4];
+  const int G = a.heads_per_item;
+  const int npairs = nrows * G;
+  const int t = threadIdx.x;
+  const int dq = (t % TPP) * 4;
+  for (int p = t / TPP; p < npairs; p += PPP) {
+    const int64_t base = (int64_t)b * a.ws_slots + slot0 + p;
+    float mx = -INFINITY;
+    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.ws_lse[base + (int64_t)c * kSlotsPerItem]);
+    const float msafe = mx == -INFINITY ? 0.0f : mx;
+    float den = 0.0f;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < nch; ++c) {
+      const int64_t s = base + (int64_t)c * kSlotsPerItem;
+      const float w = __expf(a.ws_lse[s] - msafe);
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.ws_o + s * D + dq);
+      den += w;
+      acc += w * x;
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    const int row = q0 + p / G, h = h0 + p % G;
+    bf16x4_t w4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x4_t*>(a.out + (int64_t)b * a.o_sb + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + dq) = w4;
+    if (dq == 0)
+      a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)h * a.l_sh] =
+          den > 0.0f ? msafe + __logf(den) : -INFINITY;
+  }
+}
+
+
+}  // namespace
+
+struct ffa_plan_s {
+  ffa::Plan plan;
+};
+
+static ffa_status hip_fail(hipError_t e, const char* what) {
+  return ffa::set_error(FFA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+extern "C" {
+
+int32_t ffa_abi_version(void) { return FFA_ABI_VERSION; }
+
+const char* ffa_status_string(ffa_status s) {
+  switch (s) {
+    case FFA_OK: return "ok";
+    case FFA_ERR_NULL: return "null pointer";
+    case FFA_ERR_SHAPE: return "unsupported shape";
+    case FFA_ERR_GQA: return "heads_q not a multiple of heads_kv";
+    case FFA_ERR_RANGE: return "range out of bounds";
+    case FFA_ERR_MASK_TYPE: return "unsupported mask type";
+    case FFA_ERR_OVERLAP: return "overlapping slices";
+    case FFA_ERR_WORKSPACE: return "buffer missing or too small";
+    case FFA_ERR_HIP: return "HIP runtime error";
+    case FFA_ERR_HOST_OOM: return "host out of memory";
+    case FFA_ERR_ALIGN: return "misaligned tensor or stride";
+    case FFA_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+const char* ffa_last_error(void) { return ffa::last_error(); }
+
+ffa_status ffa_plan(const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* mask_types,
+                    int32_t num_slices, int32_t total_q, int32_t total_k, int32_t heads_q, int32_t heads_kv,
+                    int32_t head_dim, const ffa_plan_opts* opts, ffa_plan_t* plan_out) {
+  ffa::clear_error();
+  if (!plan_out) return ffa::set_error(FFA_ERR_NULL, "plan_out is NULL");
+  *plan_out = nullptr;
+  ffa_plan_opts o = {};
+  if (opts) o = *opts;
+  int32_t cus = o.num_cus;
+  if (cus < 0) return ffa::set_error(FFA_ERR_ARG, "num_cus must be >= 0 (0: query the device)");
+  if (cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  ffa_plan_s* p = new (std::nothrow) ffa_plan_s;
+  if (!p) return ffa::set_error(FFA_ERR_HOST_OOM, "host allocation of the plan failed");
+  ffa_status st;
+  try {
+    st = ffa::build_plan(q_ranges, k_ranges, mask_types, num_slices, total_q, total_k, heads_q, heads_kv, head_dim,
+                         o.split_tiles, o.max_splits, cus, o.flags, &p->plan);
+  } catch (const std::bad_alloc&) {
+    st = ffa::set_error(FFA_ERR_HOST_OOM, "host allocation failed while planning");
+  }
+  if (st != FFA_OK) {
+    delete p;
+    return st;
+  }
+  *plan_out = p;
+  return FFA_OK;
+}
+
+ffa_status ffa_plan_info_get(ffa_plan_t plan, ffa_plan_info* info) {
+  ffa::clear_error();
+  if (!plan || !info) return ffa::set_error(FFA_ERR_NULL, "plan or info is NULL");
+  const ffa::Plan& p = plan->plan;
+  info->meta_bytes = p.meta_bytes();
+  info->workspace_bytes = p.workspace_bytes();
+  info->visible_pairs = p.visible_pairs;
+  info->computed_pairs = p.computed_pairs;
+  info->num_items = p.num_items;
+  info->num_runs = p.num_runs;
+  info->num_combine = p.num_combine;
+  info->num_split_items = p.num_split_items;
+  info->heads_per_item = p.heads_per_item;
+  info->rows_per_item = p.rows_per_item;
+  info->block_n = kBlockN;
+  info->max_item_tiles = p.max_item_tiles;
+  info->total_tiles = p.total_tiles;
+  return FFA_OK;
+}
+
+ffa_status ffa_plan_upload(ffa_plan_t plan, void* d_meta, size_t meta_bytes, void* stream) {
+  ffa::clear_error();
+  if (!plan || !d_meta) return ffa::set_error(FFA_ERR_NULL, "plan or d_meta is NULL");
+  const size_t need = (size_t)plan->plan.meta_bytes();
+  if (meta_bytes < need)
+    return ffa::set_error(FFA_ERR_WORKSPACE, "meta buffer of " + std::to_string(meta_bytes) + " bytes, plan needs " +
+                                                 std::to_string(need));
+  hipError_t e = hipMemcpyAsync(d_meta, plan->plan.meta.data(), need, hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(meta)");
+  return FFA_OK;
+}
+
+ffa_status ffa_plan_export(ffa_plan_t plan, void* h_meta, size_t meta_bytes) {
+  ffa::clear_error();
+  if (!plan || !h_meta) return ffa::set_error(FFA_ERR_NULL, "plan or h_meta is NULL");
+  const size_t need = (size_t)plan->plan.meta_bytes();
+  if (meta_bytes < need) return ffa::set_error(FFA_ERR_WORKSPACE, "host buffer too small for the plan metadata");
+  std::memcpy(h_meta, plan->plan.meta.data(), need);
+  return FFA_OK;
+}
+
+void ffa_plan_destroy(ffa_plan_t plan) { delete plan; }
+
+ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const void* q, int64_t q_sb, int64_t q_st,
+                   int64_t q_sh, const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh, const void* v, int64_t v_sb,
+                   int64_t v_st, int64_t v_sh, void* out, int64_t o_sb, int64_t o_st, int64_t o_sh, float* lse,
+                   int64_t l_sb, int64_t l_st, int64_t l_sh, float softmax_scale, void* d_workspace,
+                   size_t workspace_bytes, void* stream) {
+  ffa::clear_error();
+  if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
+  const ffa::Plan& p = plan->plan;
+  if (batch < 1) return ffa::set_error(FFA_ERR_ARG, "batch must be >= 1");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return ffa::set_error(FFA_ERR_ARG, "softmax_scale must be finite and > 0");
+  if (!d_meta) return ffa::set_error(FFA_ERR_NULL, "d_meta is NULL");
+  if (p.total_q > 0 && (!q || !out || !lse)) return ffa::set_error(FFA_ERR_NULL, "q, out and lse must be non-NULL");
+  const bool need_kv = p.total_tiles > 0;
+  if (need_kv && (!k || !v)) return ffa::set_error(FFA_ERR_NULL, "k and v must be non-NULL");
+  const int64_t ws_need = (int64_t)batch * p.workspace_bytes();
+  if (ws_need > 0 && (!d_workspace || (int64_t)workspace_bytes < ws_need))
+    return ffa::set_error(FFA_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                                 " bytes, plan needs " + std::to_string(ws_need));
+  auto al16 = [](const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; };
+  auto st8 = [](int64_t s) { return (s & 7) == 0; };
+  if (!al16(q) || !al16(out) || (need_kv && (!al16(k) || !al16(v))))
+    return ffa::set_error(FFA_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (!st8(q_sb) || !st8(q_st) || !st8(q_sh) || !st8(k_sb) || !st8(k_st) || !st8(k_sh) || !st8(v_sb) ||
+      !st8(v_st) || !st8(v_sh) || !st8(o_sb) || !st8(o_st) || !st8(o_sh))
+    return ffa::set_error(FFA_ERR_ALIGN, "q, k, v and out strides must be multiples of 8 elements");
+  if (p.num_items == 0) return FFA_OK;
+  if ((int64_t)p.num_items * batch > INT32_MAX || (int64_t)p.num_combine * batch > INT32_MAX)
+    return ffa::set_error(FFA_ERR_ARG, "grid too large");
+
+  const int32_t* meta = static_cast<const int32_t*>(d_meta);
+  FwdArgs fa;
+  fa.items = meta + ffa::kHdr;
+  fa.runs = fa.items + (size_t)p.num_items * kRec;
+  fa.q = static_cast<const __bf16*>(q);
+  fa.k = static_cast<const __bf16*>(k);
+  fa.v = static_cast<const __bf16*>(v);
+  fa.out = static_cast<__bf16*>(out);
+  fa.lse = lse;
+  fa.q_sb = q_sb; fa.q_st = q_st; fa.q_sh = q_sh;
+  fa.k_sb = k_sb; fa.k_st = k_st; fa.k_sh = k_sh;
+  fa.v_sb = v_sb; fa.v_st = v_st; fa.v_sh = v_sh;
+  fa.o_sb = o_sb; fa.o_st = o_st; fa.o_sh = o_sh;
+  fa.l_sb = l_sb; fa.l_st = l_st; fa.l_sh = l_sh;
+  fa.ws_o = static_cast<float*>(d_workspace);
+  fa.ws_lse = fa.ws_o ? fa.ws_o + (size_t)batch * p.num_slots * p.head_dim : nullptr;
+  fa.ws_slots = p.num_slots;
+  fa.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  fa.total_k = p.total_k;
+  fa.batch = batch;
+  fa.heads_per_item = p.heads_per_item;
+  fa.kv_ratio = p.heads_q / p.heads_kv;
+
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)((int64_t)p.num_items * batch));
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(ffa_fwd_main<128>, grid, dim3(256), 0, s, fa);
+  else
+    hipLaunchKernelGGL(ffa_fwd_main<64>, grid, dim3(256), 0, s, fa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch ffa_fwd_main");
+
+  if (p.num_combine > 0) {
+    CombineArgs ca;
+    ca.combine = fa.runs + (size_t)p.num_runs * kRec;
+    ca.ws_o = fa.ws_o;
+    ca.ws_lse = fa.ws_lse;
+    ca.ws_slots = p.num_slots;
+    ca.out = fa.out;
+    ca.lse = lse;
+    ca.o_sb = o_sb; ca.o_st = o_st; ca.o_sh = o_sh;
+    ca.l_sb = l_sb; ca.l_st = l_st; ca.l_sh = l_sh;
+    ca.batch = batch;
+    ca.heads_per_item = p.heads_per_item;
+    const dim3 cgrid((unsigned)((int64_t)p.num_combine * batch));
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL(ffa_combine<128>, cgrid, dim3(256), 0, s, ca);
+    else
+      hipLaunchKernelGGL(ffa_combine<64>, cgrid, dim3(256), 0, s, ca);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch ffa_combine");
+  }
+  return FFA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the host planner and the HIP launcher.
+//
+// The plan is a worklist of fixed-size int32 records uploaded to the device
+// once per mask and read by the kernels:
+//
+//   header  [16]             magic, version, counts, tile shape (see kHdr*)
+//   items   [num_items][8]   one main-kernel workgroup each (per batch element)
+//   runs    [num_runs][8]    a contiguous range of key tiles of one slice
+//   combine [num_combine][8] one split row block to merge
+//
+// Item:    q0, nrows, h0, run_off, n_runs, slot (-1: final output), tiles, 0
+//          rows [q0, q0 + nrows) and query heads [h0, h0 + heads_per_item)
+//          share one kv head; the item walks runs[run_off .. run_off + n_runs)
+//          in order; `tiles` is the total key-tile count of those runs.
+// Run:     k0, n_tiles, n_full, k_hi, edge_base, 0, 0, 0
+//          key tile t covers [k0 + t*BN, k0 + (t+1)*BN); row i sees key j iff
+//          j < min(k_hi, i + edge_base) (edge_base = ke - qe + 1 for a causal
+//          slice, kNoEdge for a full one); the first n_full tiles are visible
+//          to every row of the item, so they need no mask.
+// Combine: q0, nrows, h0, n_chunks, slot0, 0, 0, 0
+//          chunk c of row (q0 + r), head (h0 + g) is partial slot
+//          slot0 + c * kSlotsPerItem + r * heads_per_item + g.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/ffa.h"
+
+namespace ffa {
+
+constexpr int32_t kMagic = 0x46464131;  // "FFA1"
+constexpr int32_t kBlockN = 64;         // keys per tile
+constexpr int32_t kWaveRows = 32;       // query rows per wavefront (one 32x32 MFMA block)
+constexpr int32_t kWaves = 4;           // wavefronts per workgroup
+constexpr int32_t kSlotsPerItem = kWaveRows * kWaves;  // (row, head) pairs one workgroup covers
+constexpr int32_t kNoEdge = 0x3fffffff; // edge_base of a full slice: never limits
+constexpr int kRec = 8;                 // int32 per record
+constexpr int kHdr = 16;                // int32 in the header
+
+enum HeaderField {
+  kHdrMagic = 0, kHdrVersion, kHdrItems, kHdrRuns, kHdrCombine, kHdrHeadsPerItem, kHdrRowsPerItem,
+  kHdrBlockN, kHdrHeadDim, kHdrHeadsQ, kHdrHeadsKv, kHdrTotalQ, kHdrTotalK, kHdrSlots
+};
+
+struct Plan {
+  int32_t total_q = 0, total_k = 0, heads_q = 0, heads_kv = 0, head_dim = 0;
+  int32_t heads_per_item = 1, rows_per_item = 0;
+  int32_t num_items = 0, num_runs = 0, num_combine = 0, num_split_items = 0;
+  int32_t num_slots = 0, max_item_tiles = 0;
+  int64_t visible_pairs = 0, computed_pairs = 0, total_tiles = 0;
+  std::vector<int32_t> meta;  // header + items + runs + combine
+  int64_t meta_bytes() const { return (int64_t)meta.size() * 4; }
+  int64_t workspace_bytes() const { return (int64_t)num_slots * (head_dim + 1) * 4; }
+  const int32_t* items() const { return meta.data() + kHdr; }
+  const int32_t* runs() const { return items() + (size_t)num_items * kRec; }
+  const int32_t* combine() const { return runs() + (size_t)num_runs * kRec; }
+};
+
+// Validates the problem and fills `plan`.  Returns FFA_OK or an error code
+// (message in last_error()).  num_cus must be > 0.
+ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* mask_types,
+                      int32_t num_slices, int32_t total_q, int32_t total_k, int32_t heads_q,
+                      int32_t heads_kv, int32_t head_dim, int32_t split_tiles, int32_t max_splits,
+                      int32_t num_cus, uint32_t flags, Plan* plan);
+
+ffa_status set_error(ffa_status st, const std::string& msg);
+void clear_error();
+const char* last_error();
+
+}  // namespace ffa

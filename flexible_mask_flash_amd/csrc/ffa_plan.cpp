@@ -1,0 +1,343 @@
+// Host-side validation and slice planner (no HIP calls; unit-tested on the CPU).
+//
+// Turns the slice list of the MagiAttention FFA interface (quickstart page,
+// "Single-GPU Flex-Flash-Attention": q_ranges, k_ranges, attn_type_map) into
+// the worklist described in ffa_internal.h:
+//
+//  1. q segments: the query axis is cut at every slice boundary, so inside a
+//     segment each row is covered by the same set of slices.
+//  2. q tiles: a segment is cut into tiles of rows_per_item rows, aligned to
+//     the segment start (the last tile may be short).
+//  3. key runs: for each slice covering a tile, the visible end of a row is
+//     ke (full) or ke - (qe - 1 - i) (causal, bottom-right aligned; the
+//     kv-interval formula of the MagiAttention blog page "Calculate KV Interval
+//     Boundaries for Mask Types").  It is nondecreasing in i, so the first and
+//     last rows of the tile bound it: tiles of BN keys from ks up to the last
+//     row's end are needed, those ending before the first row's end need no
+//     mask, and a slice the last row cannot see is skipped.
+//  4. split-K: long items are cut into chunks of key tiles that write float32
+//     partial (out, lse); the combine kernel merges them with a global
+//     logsumexp (FlagAttention user guide, "Split-KV and paged attention").
+//     The automatic rule splits only when an item is longer than a fair share
+//     of the device (few items or very long rows), as FlagAttention picks its
+//     split-KV path by occupancy.
+//  5. order: longest items first, so the hardware dispatcher fills the device
+//     with long work and ends on short work.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "ffa_internal.h"
+
+namespace ffa {
+
+namespace {
+thread_local std::string g_last_error;
+
+struct Slice {
+  int32_t qs, qe, ks, ke, type, id;
+};
+
+// Visible key end of row i through slice s (may be <= ks: nothing visible).
+inline int64_t row_end(const Slice& s, int64_t i) {
+  return s.type == FFA_MASK_CAUSAL ? (int64_t)s.ke - ((int64_t)s.qe - 1 - i) : (int64_t)s.ke;
+}
+
+int64_t slice_visible_pairs(const Slice& s) {
+  const int64_t M = s.qe - s.qs, N = s.ke - s.ks;
+  if (M <= 0 || N <= 0) return 0;
+  if (s.type == FFA_MASK_FULL) return M * N;
+  // causal: local row m sees clamp(N - M + 1 + m, 0, N) keys
+  const int64_t c = N - M + 1;
+  const int64_t m0 = std::max<int64_t>(0, 1 - c);
+  if (m0 >= M) return 0;
+  return (c + m0 + N) * (M - m0) / 2;
+}
+
+struct TileRun {
+  int32_t k0, n_tiles, n_full, k_hi, edge_base;
+};
+
+struct QTile {
+  int32_t q0, nrows;
+  std::vector<TileRun> runs;
+  int64_t tiles = 0;
+};
+
+constexpr int32_t kMinChunkTiles = 16;   // never split below 1024 keys per chunk
+constexpr int32_t kItemOverhead = 2;     // prologue / epilogue cost of an item, in tiles
+constexpr int32_t kResidentPerCu = 2;    // main-kernel workgroups resident per CU
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
+}  // namespace
+
+ffa_status set_error(ffa_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+void clear_error() { g_last_error.clear(); }
+const char* last_error() { return g_last_error.c_str(); }
+
+ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* mask_types,
+                      int32_t num_slices, int32_t total_q, int32_t total_k, int32_t heads_q,
+                      int32_t heads_kv, int32_t head_dim, int32_t split_tiles, int32_t max_splits,
+                      int32_t num_cus, uint32_t flags, Plan* plan) {
+  // ---------------------------------------------------------------- validation
+  if (!plan) return set_error(FFA_ERR_NULL, "plan output pointer is NULL");
+  if (num_slices < 0) return set_error(FFA_ERR_ARG, "num_slices < 0");
+  if (num_slices > 0 && (!q_ranges || !k_ranges || !mask_types))
+    return set_error(FFA_ERR_NULL, "q_ranges, k_ranges and mask_types must be non-NULL when num_slices > 0");
+  if (total_q < 0 || total_k < 0 || total_q > kMaxTokens || total_k > kMaxTokens)
+    return set_error(FFA_ERR_SHAPE, "total_q and total_k must be in [0, 2^30]");
+  if (heads_q <= 0 || heads_kv <= 0) return set_error(FFA_ERR_SHAPE, "head counts must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return set_error(FFA_ERR_SHAPE, "head_dim must be 64 or 128, got " + std::to_string(head_dim));
+  if (heads_q % heads_kv != 0)
+    return set_error(FFA_ERR_GQA, "heads_q (" + std::to_string(heads_q) + ") must be a multiple of heads_kv (" +
+                                      std::to_string(heads_kv) + ")");
+  if (num_cus <= 0) return set_error(FFA_ERR_ARG, "num_cus must be positive");
+  if (max_splits <= 0) max_splits = 64;
+
+  std::vector<Slice> slices;
+  slices.reserve(num_slices);
+  int64_t visible = 0;
+  for (int32_t s = 0; s < num_slices; ++s) {
+    Slice x{q_ranges[2 * s], q_ranges[2 * s + 1], k_ranges[2 * s], k_ranges[2 * s + 1], mask_types[s], s};
+    if (x.qs < 0 || x.qe > total_q || x.qs > x.qe)
+      return set_error(FFA_ERR_RANGE, "slice " + std::to_string(s) + ": q_range [" + std::to_string(x.qs) + ", " +
+                                          std::to_string(x.qe) + ") outside [0, " + std::to_string(total_q) + "]");
+    if (x.ks < 0 || x.ke > total_k || x.ks > x.ke)
+      return set_error(FFA_ERR_RANGE, "slice " + std::to_string(s) + ": k_range [" + std::to_string(x.ks) + ", " +
+                                          std::to_string(x.ke) + ") outside [0, " + std::to_string(total_k) + "]");
+    if (x.type != FFA_MASK_FULL && x.type != FFA_MASK_CAUSAL)
+      return set_error(FFA_ERR_MASK_TYPE, "slice " + std::to_string(s) + ": mask type " + std::to_string(x.type) +
+                                              " (supported: 0 full, 1 causal)");
+    const int64_t vp = slice_visible_pairs(x);
+    if (vp == 0) continue;  // a slice that makes nothing visible is a no-op
+    visible += vp;
+    slices.push_back(x);
+  }
+
+  // overlap: two slices share a visible pair iff they do on the last row both cover,
+  // because visible ends are nondecreasing in the row and starts are constant.
+  {
+    std::vector<int> ord(slices.size());
+    std::iota(ord.begin(), ord.end(), 0);
+    std::sort(ord.begin(), ord.end(), [&](int a, int b) { return slices[a].qs < slices[b].qs; });
+    for (size_t ia = 0; ia < ord.size(); ++ia) {
+      const Slice& a = slices[ord[ia]];
+      for (size_t ib = ia + 1; ib < ord.size(); ++ib) {
+        const Slice& b = slices[ord[ib]];
+        if (b.qs >= a.qe) break;
+        const int64_t last = std::min(a.qe, b.qe) - 1;
+        const int64_t ea = std::min<int64_t>(row_end(a, last), a.ke);
+        const int64_t eb = std::min<int64_t>(row_end(b, last), b.ke);
+        if (std::max(a.ks, b.ks) < std::min(ea, eb))
+          return set_error(FFA_ERR_OVERLAP, "slices " + std::to_string(a.id) + " and " + std::to_string(b.id) +
+                                                " overlap (row " + std::to_string(last) + ")");
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- shape of a workgroup
+  const int32_t ratio = heads_q / heads_kv;
+  int32_t G = 1;
+  for (int32_t g : {4, 2}) {
+    if (ratio % g == 0) {
+      G = g;
+      break;
+    }
+  }
+  const int32_t rows_per_item = kSlotsPerItem / G;
+  const int32_t n_groups = heads_q / G;
+
+  // ---------------------------------------------------------------- segments and q tiles
+  std::vector<int32_t> bounds = {0, total_q};
+  for (const Slice& s : slices) {
+    bounds.push_back(s.qs);
+    bounds.push_back(s.qe);
+  }
+  std::sort(bounds.begin(), bounds.end());
+  bounds.erase(std::unique(bounds.begin(), bounds.end()), bounds.end());
+
+  std::vector<int> by_qs(slices.size());
+  std::iota(by_qs.begin(), by_qs.end(), 0);
+  std::sort(by_qs.begin(), by_qs.end(), [&](int a, int b) { return slices[a].qs < slices[b].qs; });
+
+  std::vector<QTile> tiles;
+  std::vector<int> active;
+  size_t next_slice = 0;
+  for (size_t bi = 0; bi + 1 < bounds.size(); ++bi) {
+    const int32_t a = bounds[bi], b = bounds[bi + 1];
+    if (b <= a) continue;
+    while (next_slice < by_qs.size() && slices[by_qs[next_slice]].qs <= a) active.push_back(by_qs[next_slice++]);
+    active.erase(std::remove_if(active.begin(), active.end(), [&](int s) { return slices[s].qe <= a; }),
+                 active.end());
+    for (int32_t r0 = a; r0 < b; r0 += rows_per_item) {
+      QTile t;
+      t.q0 = r0;
+      t.nrows = std::min(rows_per_item, b - r0);
+      const int64_t r_last = (int64_t)r0 + t.nrows - 1;
+      for (int si : active) {
+        const Slice& s = slices[si];
+        const int64_t e_last = std::min<int64_t>(row_end(s, r_last), s.ke);
+        if (e_last <= s.ks) continue;  // no row of the tile sees this slice
+        const int64_t e_first = std::max<int64_t>(std::min<int64_t>(row_end(s, r0), s.ke), s.ks);
+        TileRun run;
+        run.k0 = s.ks;
+        run.n_tiles = (int32_t)((e_last - s.ks + kBlockN - 1) / kBlockN);
+        run.n_full = (int32_t)((e_first - s.ks) / kBlockN);
+        run.k_hi = s.ke;
+        run.edge_base = s.type == FFA_MASK_CAUSAL ? s.ke - s.qe + 1 : kNoEdge;
+        t.runs.push_back(run);
+        t.tiles += run.n_tiles;
+      }
+      std::sort(t.runs.begin(), t.runs.end(), [](const TileRun& x, const TileRun& y) { return x.k0 < y.k0; });
+      tiles.push_back(std::move(t));
+    }
+  }
+
+  // ---------------------------------------------------------------- split-K decision
+  int64_t total_cost = 0, max_tiles = 0;
+  for (const QTile& t : tiles) {
+    total_cost += (t.tiles + (t.runs.empty() ? 0 : kItemOverhead)) * n_groups;
+    max_tiles = std::max(max_tiles, t.tiles);
+  }
+  int64_t chunk_target = 0;  // 0: no split
+  if (split_tiles > 0) {
+    chunk_target = split_tiles;
+  } else if (split_tiles == 0) {
+    const int64_t slots = (int64_t)num_cus * kResidentPerCu;
+    const int64_t fair = (total_cost + slots - 1) / slots;
+    const int64_t target = std::max<int64_t>(kMinChunkTiles, fair);
+    if (max_tiles > target) chunk_target = target;
+  }
+
+  // ---------------------------------------------------------------- emit
+  struct ItemRec {
+    int32_t q0, nrows, h0, run_off, n_runs, slot, tiles;
+  };
+  std::vector<ItemRec> items;
+  std::vector<int32_t> runs;      // flattened run records (kRec each)
+  std::vector<int32_t> combine;   // flattened combine records
+  int32_t n_slots = 0, n_split_items = 0;
+  int64_t computed = 0, all_tiles = 0;
+  auto push_run = [&](int32_t k0, int32_t nt, int32_t nf, int32_t khi, int32_t eb) {
+    const int32_t rec[kRec] = {k0, nt, nf, khi, eb, 0, 0, 0};
+    runs.insert(runs.end(), rec, rec + kRec);
+  };
+
+  for (const QTile& t : tiles) {
+    computed += (int64_t)rows_per_item * t.tiles * kBlockN;
+    all_tiles += t.tiles * n_groups;
+    int64_t n_chunks = 1;
+    if (chunk_target > 0 && t.tiles > chunk_target) {
+      n_chunks = std::min<int64_t>({(int64_t)max_splits, (t.tiles + chunk_target - 1) / chunk_target, t.tiles});
+    }
+    if (n_chunks <= 1) {
+      const int32_t off = (int32_t)(runs.size() / kRec);
+      for (const TileRun& r : t.runs) push_run(r.k0, r.n_tiles, r.n_full, r.k_hi, r.edge_base);
+      for (int32_t g = 0; g < n_groups; ++g)
+        items.push_back({t.q0, t.nrows, g * G, off, (int32_t)t.runs.size(), -1, (int32_t)t.tiles});
+      continue;
+    }
+    // split: chunk c covers item tiles [c*T/n, (c+1)*T/n) across the runs in order
+    std::vector<int32_t> chunk_off(n_chunks), chunk_nruns(n_chunks), chunk_tiles(n_chunks);
+    for (int64_t c = 0; c < n_chunks; ++c) {
+      const int64_t ta = c * t.tiles / n_chunks, tb = (c + 1) * t.tiles / n_chunks;
+      chunk_off[c] = (int32_t)(runs.size() / kRec);
+      chunk_tiles[c] = (int32_t)(tb - ta);
+      int32_t nr = 0;
+      int64_t cs = 0;
+      for (const TileRun& r : t.runs) {
+        const int64_t a = std::max(ta, cs), b = std::min(tb, cs + r.n_tiles);
+        if (b > a) {
+          const int32_t skip = (int32_t)(a - cs);
+          const int32_t nt = (int32_t)(b - a);
+          push_run(r.k0 + skip * kBlockN, nt, std::max(0, std::min(nt, r.n_full - skip)), r.k_hi, r.edge_base);
+          ++nr;
+        }
+        cs += r.n_tiles;
+      }
+      chunk_nruns[c] = nr;
+    }
+    for (int32_t g = 0; g < n_groups; ++g) {
+      const int32_t slot0 = n_slots;
+      n_slots += (int32_t)n_chunks * kSlotsPerItem;
+      for (int64_t c = 0; c < n_chunks; ++c) {
+        items.push_back({t.q0, t.nrows, g * G, chunk_off[c], chunk_nruns[c], slot0 + (int32_t)c * kSlotsPerItem,
+                         chunk_tiles[c]});
+        ++n_split_items;
+      }
+      const int32_t rec[kRec] = {t.q0, t.nrows, g * G, (int32_t)n_chunks, slot0, 0, 0, 0};
+      combine.insert(combine.end(), rec, rec + kRec);
+    }
+  }
+
+  if (!(flags & 1u)) {
+    std::stable_sort(items.begin(), items.end(), [](const ItemRec& x, const ItemRec& y) {
+      const int32_t cx = x.tiles + (x.n_runs ? kItemOverhead : 0), cy = y.tiles + (y.n_runs ? kItemOverhead : 0);
+      return cx > cy;
+    });
+  }
+
+  if (items.size() > (size_t)INT32_MAX / kRec || runs.size() > (size_t)INT32_MAX)
+    return set_error(FFA_ERR_ARG, "plan too large");
+
+  Plan p;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.heads_q = heads_q;
+  p.heads_kv = heads_kv;
+  p.head_dim = head_dim;
+  p.heads_per_item = G;
+  p.rows_per_item = rows_per_item;
+  p.num_items = (int32_t)items.size();
+  p.num_runs = (int32_t)(runs.size() / kRec);
+  p.num_combine = (int32_t)(combine.size() / kRec);
+  p.num_split_items = n_split_items;
+  p.num_slots = n_slots;
+  p.visible_pairs = visible;
+  p.computed_pairs = computed;
+  p.total_tiles = all_tiles;
+  int32_t max_item = 0;
+  for (const ItemRec& it : items) max_item = std::max(max_item, it.tiles);
+  p.max_item_tiles = max_item;
+
+  try {
+    p.meta.assign(kHdr + items.size() * kRec + runs.size() + combine.size(), 0);
+  } catch (...) {
+    return set_error(FFA_ERR_HOST_OOM, "host allocation of the plan failed");
+  }
+  int32_t* h = p.meta.data();
+  h[kHdrMagic] = kMagic;
+  h[kHdrVersion] = FFA_ABI_VERSION;
+  h[kHdrItems] = p.num_items;
+  h[kHdrRuns] = p.num_runs;
+  h[kHdrCombine] = p.num_combine;
+  h[kHdrHeadsPerItem] = G;
+  h[kHdrRowsPerItem] = rows_per_item;
+  h[kHdrBlockN] = kBlockN;
+  h[kHdrHeadDim] = head_dim;
+  h[kHdrHeadsQ] = heads_q;
+  h[kHdrHeadsKv] = heads_kv;
+  h[kHdrTotalQ] = total_q;
+  h[kHdrTotalK] = total_k;
+  h[kHdrSlots] = n_slots;
+  int32_t* w = h + kHdr;
+  for (const ItemRec& it : items) {
+    const int32_t rec[kRec] = {it.q0, it.nrows, it.h0, it.run_off, it.n_runs, it.slot, it.tiles, 0};
+    std::memcpy(w, rec, sizeof(rec));
+    w += kRec;
+  }
+  if (!runs.empty()) std::memcpy(w, runs.data(), runs.size() * 4);
+  w += runs.size();
+  if (!combine.empty()) std::memcpy(w, combine.data(), combine.size() * 4);
+  *plan = std::move(p);
+  return FFA_OK;
+}
+
+}  // namespace ffa

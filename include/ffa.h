@@ -1,0 +1,164 @@
+/*
+ * ffa.h -- C ABI of the MI355X (gfx950) flexible-mask flash-attention forward.
+ *
+ * The operation (MagiAttention quickstart, section "Single-GPU
+ * Flex-Flash-Attention"; FlagAttention user guide, section "FlashAttention"):
+ *
+ *   q [total_q, Hq, D], k and v [total_k, Hkv, D], bfloat16, head_dim D
+ *   contiguous.  A mask is a list of S slices (q_range, k_range, type) with
+ *   half-open ranges.  Query row i of slice s (qs <= i < qe) sees
+ *     FULL   (type 0): keys [ks, ke)
+ *     CAUSAL (type 1): keys [ks, ke - (qe - 1 - i))   -- bottom-right aligned
+ *   (the kv-interval formula of the MagiAttention blog page "Calculate KV
+ *   Interval Boundaries for Mask Types", bits 0 / 1 of the type).
+ *   Query head h uses kv head h / (Hq / Hkv); Hq % Hkv == 0 is required.
+ *   With s_ij = softmax_scale * q_i . k_j over the visible keys V(i):
+ *     lse[i,h] = ln sum_{j in V(i)} exp(s_ij)           (-inf if V(i) is empty)
+ *     out[i,h] = sum_{j in V(i)} exp(s_ij - lse[i,h]) v_j  (0 if V(i) is empty)
+ *   out is bfloat16 (round to nearest even), lse float32; the kernels
+ *   accumulate in float32 (the quickstart states fp32 reduction).
+ *
+ * Calls:
+ *   ffa_plan        validate the slices and build the work plan on the host
+ *   ffa_plan_info   sizes and statistics of a plan
+ *   ffa_plan_upload copy the plan's metadata to a caller-owned device buffer
+ *   ffa_plan_export copy the same metadata to host memory (inspection, tests)
+ *   ffa_fwd         run the forward on a stream (main kernel, then the split
+ *                   combine when the plan has split rows)
+ *   ffa_plan_destroy, ffa_status_string, ffa_last_error, ffa_abi_version
+ *
+ * Ownership.  The library owns only the host plan.  All device memory (meta,
+ * workspace, q/k/v/out/lse) belongs to the caller.  The library never allocates
+ * or frees device memory and never synchronises a stream; ffa_fwd only enqueues
+ * kernels, so a device fault surfaces at the caller's next synchronisation.
+ *
+ * Errors.  Every call returns an ffa_status.  Arguments are validated before
+ * anything is enqueued, so a non-OK return means nothing was written.
+ * ffa_last_error() returns a thread-local message for the last failure in the
+ * calling thread (offending slice, stride, size...).  Nothing throws across the ABI.
+ */
+#ifndef FFA_H
+#define FFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FFA_ABI_VERSION 1
+
+#define FFA_MASK_FULL 0
+#define FFA_MASK_CAUSAL 1
+
+typedef enum {
+  FFA_OK = 0,
+  FFA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+  FFA_ERR_SHAPE = 2,       /* total_q/total_k < 0, heads <= 0, head_dim not in {64, 128}   */
+  FFA_ERR_GQA = 3,         /* heads_q % heads_kv != 0                                      */
+  FFA_ERR_RANGE = 4,       /* a range leaves [0, total] or has start > end                 */
+  FFA_ERR_MASK_TYPE = 5,   /* a type other than 0 (FULL) or 1 (CAUSAL)                     */
+  FFA_ERR_OVERLAP = 6,     /* two slices make some (q, k) pair visible twice               */
+  FFA_ERR_WORKSPACE = 7,   /* meta or workspace buffer missing or too small                */
+  FFA_ERR_HIP = 8,         /* a HIP runtime call failed (message in ffa_last_error)        */
+  FFA_ERR_HOST_OOM = 9,    /* host allocation failed while planning                        */
+  FFA_ERR_ALIGN = 10,      /* a tensor base or stride is not a multiple of 8 elements      */
+  FFA_ERR_ARG = 11         /* any other invalid argument (batch, scale, plan state)        */
+} ffa_status;
+
+/* Opaque host plan; immutable after ffa_plan, safe to share between threads. */
+typedef struct ffa_plan_s* ffa_plan_t;
+
+/* Planner options.  Pass NULL for defaults; zero fields also mean "default". */
+typedef struct {
+  /* Split-K control.  0: automatic (split only when the work cannot fill the
+   * device: long rows and few items).  > 0: split every item whose key-tile
+   * count exceeds this value into chunks of about this many tiles.  < 0: never
+   * split.  Split items write float32 partial (out, lse) to the workspace and a
+   * second kernel merges them with a global logsumexp (FlagAttention user
+   * guide, "Split-KV and paged attention"). */
+  int32_t split_tiles;
+  /* Upper bound on chunks per split item (0: 64). */
+  int32_t max_splits;
+  /* Compute units to plan for (0: query the current HIP device). */
+  int32_t num_cus;
+  /* Bit 0: keep items in natural order (no longest-first ordering). */
+  uint32_t flags;
+} ffa_plan_opts;
+
+/* Plan statistics.  Byte sizes are what ffa_plan_upload / ffa_fwd require. */
+typedef struct {
+  int64_t meta_bytes;        /* device metadata buffer size (ffa_plan_upload)             */
+  int64_t workspace_bytes;   /* split-K workspace per batch element (0: no split rows)     */
+  int64_t visible_pairs;     /* unmasked (q, k) pairs per head: FLOPs = 4 * D * Hq * this  */
+  int64_t computed_pairs;    /* (row, key) pairs the kernels evaluate per head, incl. waste */
+  int32_t num_items;         /* workgroups of the main kernel per batch element            */
+  int32_t num_runs;          /* (item, slice) key runs                                     */
+  int32_t num_combine;       /* combine entries (split row blocks)                         */
+  int32_t num_split_items;   /* main-kernel items that write partials                      */
+  int32_t heads_per_item;    /* query heads one workgroup covers (GQA group share)          */
+  int32_t rows_per_item;     /* query rows one workgroup covers                             */
+  int32_t block_n;           /* keys per tile                                               */
+  int32_t max_item_tiles;    /* longest item, in key tiles                                  */
+  int64_t total_tiles;       /* key tiles over all items                                    */
+} ffa_plan_info;
+
+/*
+ * Build a plan.  q_ranges, k_ranges: HOST int32 [num_slices][2] (start, end);
+ * mask_types: HOST int32 [num_slices].  num_slices may be 0 (every row empty).
+ * The slices must be pairwise disjoint in the (q, k) plane (FFA_ERR_OVERLAP
+ * otherwise); empty ranges (start == end) are valid no-ops.  head_dim must be
+ * 64 or 128.  On success *plan_out receives a plan the caller must destroy.
+ */
+ffa_status ffa_plan(const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* mask_types,
+                    int32_t num_slices, int32_t total_q, int32_t total_k, int32_t heads_q,
+                    int32_t heads_kv, int32_t head_dim, const ffa_plan_opts* opts,
+                    ffa_plan_t* plan_out);
+
+ffa_status ffa_plan_info_get(ffa_plan_t plan, ffa_plan_info* info);
+
+/* Copy the plan metadata (info.meta_bytes) into d_meta, a device buffer of
+ * meta_bytes >= info.meta_bytes, with hipMemcpyAsync on `stream` (a hipStream_t;
+ * NULL = the null stream).  The copy is ordered before later work on the stream. */
+ffa_status ffa_plan_upload(ffa_plan_t plan, void* d_meta, size_t meta_bytes, void* stream);
+
+/* Copy the same metadata to host memory h_meta (>= info.meta_bytes bytes).
+ * Layout: int32 header[16], then items[num_items][8], runs[num_runs][8],
+ * combine[num_combine][8]; see the planner source for the field order. */
+ffa_status ffa_plan_export(ffa_plan_t plan, void* h_meta, size_t meta_bytes);
+
+/*
+ * Forward.  All tensor pointers are DEVICE pointers; strides are in elements.
+ *   batch >= 1 independent problems share the plan; element b of every tensor
+ *   starts at base + b * stride_b.
+ *   q:   bf16, element (b, t, h, d) at q[b*q_sb + t*q_st + h*q_sh + d]
+ *   k,v: bf16, (b, t, hkv, d) likewise with their own strides
+ *   out: bf16, like q (written for every row and head)
+ *   lse: fp32, (b, t, h) at lse[b*l_sb + t*l_st + h*l_sh]
+ * q, k, v, out bases and their strides must be multiples of 8 elements (16 B).
+ * softmax_scale must be finite and > 0 (callers resolve "None" to 1/sqrt(D)).
+ * d_meta: the buffer filled by ffa_plan_upload.  d_workspace: workspace_bytes
+ * >= batch * info.workspace_bytes, may be NULL when that is 0.
+ * Kernels are enqueued on `stream` (a hipStream_t); the call does not block.
+ * Results are bitwise reproducible run to run for a given plan.
+ */
+ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
+                   const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                   const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh,
+                   const void* v, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                   void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                   float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                   float softmax_scale, void* d_workspace, size_t workspace_bytes,
+                   void* stream);
+
+void ffa_plan_destroy(ffa_plan_t plan);
+const char* ffa_status_string(ffa_status status);
+const char* ffa_last_error(void);
+int32_t ffa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFA_H */

@@ -1,0 +1,260 @@
+"""Host-side checks of libffa.so (no GPU, no compute calls).
+
+- the library loads and exports every function include/ffa.h declares;
+- the planner rejects every invalid input with the documented status;
+- the worklist it emits, rasterised with the kernels' visibility rule
+  (key j of a tile is used by row i iff j < min(k_hi, i + edge_base)), covers
+  every visible (row, head, key) of the oracle's explicit mask exactly once and
+  nothing else; tiles before n_full need no mask; split chunks are disjoint and
+  their combine entries cover exactly the split rows;
+- visible_pairs equals the oracle's count.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffa.h")
+
+ffa = pytest.importorskip("flexible_mask_flash_amd")
+
+HDR, REC = 16, 8
+NCU = 256
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ffa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"ffa_plan", "ffa_fwd", "ffa_plan_upload", "ffa_plan_destroy"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ffa.h but not exported"
+    bound = {s[0] for s in ffa._SIGNATURES}
+    assert set(names) == bound, "binding and header disagree"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.ffa_abi_version() == 1
+    for code in range(12):
+        assert lib.ffa_status_string(code).decode() not in ("", "unknown status")
+    assert lib.ffa_status_string(99).decode() == "unknown status"
+
+
+def plan_status(qr, kr, ty, tq, tk, hq, hkv, d, num_cus=NCU):
+    try:
+        ffa.Plan(qr, kr, ty, tq, tk, hq, hkv, d, num_cus=num_cus)
+        return 0
+    except ffa.FFAError as e:
+        return e.status
+
+
+def test_validation_errors():
+    ok = ([[0, 8]], [[0, 8]], [1])
+    assert plan_status(*ok, 8, 8, 2, 2, 128) == 0
+    assert plan_status(*ok, 8, 8, 2, 2, 96) == 2            # head_dim
+    assert plan_status(*ok, 8, 8, 0, 2, 128) == 2           # heads
+    assert plan_status(*ok, -1, 8, 2, 2, 128) == 2          # total_q
+    assert plan_status(*ok, 8, 8, 6, 4, 128) == 3           # GQA
+    assert plan_status([[0, 9]], [[0, 8]], [1], 8, 8, 2, 2, 128) == 4   # q out of range
+    assert plan_status([[5, 3]], [[0, 8]], [1], 8, 8, 2, 2, 128) == 4   # start > end
+    assert plan_status([[0, 8]], [[-1, 8]], [0], 8, 8, 2, 2, 128) == 4
+    assert plan_status([[0, 8]], [[0, 8]], [2], 8, 8, 2, 2, 128) == 5   # mask type
+    assert plan_status([[0, 8], [4, 8]], [[0, 8], [7, 8]], [0, 0], 8, 8, 2, 2, 128) == 6  # overlap
+    # touching but disjoint: causal [0,8)x[0,8) and full rows [0,8) keys [8,12)
+    assert plan_status([[0, 8], [0, 8]], [[0, 8], [8, 12]], [1, 0], 8, 12, 2, 2, 128) == 0
+    # causal slices whose rectangles overlap but whose visible pairs do not
+    # (row i of a 4x8 causal sees keys < 5 + i, so key 7 only from row 3 on)
+    assert plan_status([[0, 4], [0, 3]], [[0, 8], [7, 8]], [1, 0], 4, 8, 1, 1, 64) == 0
+    assert plan_status([[0, 4], [0, 4]], [[0, 8], [7, 8]], [1, 0], 4, 8, 1, 1, 64) == 6
+    assert plan_status(*ok, 8, 8, 2, 2, 128, num_cus=-3) == 11
+    # zero slices is a valid (all-empty) problem
+    assert plan_status(np.zeros((0, 2)), np.zeros((0, 2)), np.zeros(0), 8, 8, 2, 2, 64) == 0
+    # empty slices are no-ops, even when their rectangle would overlap another slice
+    assert plan_status([[0, 8], [2, 2]], [[0, 8], [0, 8]], [0, 0], 8, 8, 2, 2, 64) == 0
+
+
+def test_last_error_names_the_slice(lib):
+    with pytest.raises(ffa.FFAError) as ei:
+        ffa.Plan([[0, 4], [0, 4], [1, 3]], [[0, 4], [4, 6], [5, 6]], [0, 0, 0], 4, 6, 1, 1, 64, num_cus=NCU)
+    assert ei.value.status == 6
+    assert "slices 1 and 2" in lib.ffa_last_error().decode()
+
+
+def parse(meta):
+    h = meta[:HDR]
+    assert h[0] == 0x46464131
+    n_items, n_runs, n_comb, G, rows, bn = h[2], h[3], h[4], h[5], h[6], h[7]
+    items = meta[HDR:HDR + n_items * REC].reshape(n_items, REC)
+    runs = meta[HDR + n_items * REC:HDR + (n_items + n_runs) * REC].reshape(n_runs, REC)
+    comb = meta[HDR + (n_items + n_runs) * REC:HDR + (n_items + n_runs + n_comb) * REC].reshape(n_comb, REC)
+    return dict(G=G, rows=rows, bn=bn, items=items, runs=runs, comb=comb, hdr=h)
+
+
+def rasterise(p, plan):
+    """Per head, count how often each (row, key) is used by the kernels."""
+    m = parse(plan.meta_host())
+    G, bn = m["G"], m["bn"]
+    hq = p.heads_q
+    cover = np.zeros((hq, p.total_q, p.total_k), dtype=np.int32)
+    rows_written = np.zeros((hq, p.total_q), dtype=np.int32)      # final writes (main kernel)
+    partial_slots = {}
+    for it in m["items"]:
+        q0, nrows, h0, roff, nruns, slot, tiles = it[:7]
+        assert 1 <= nrows <= m["rows"] and h0 % G == 0
+        rows = np.arange(q0, q0 + nrows)
+        assert sum(m["runs"][roff + r][1] for r in range(nruns)) == tiles
+        for r in range(nruns):
+            k0, nt, nf, khi, eb = m["runs"][roff + r][:5]
+            assert nt >= 1 and 0 <= nf <= nt
+            for t in range(nt):
+                keys = np.arange(k0 + t * bn, k0 + (t + 1) * bn)
+                lim = np.minimum(khi, rows + eb)
+                vis = keys[None, :] < lim[:, None]
+                if t < nf:
+                    assert vis.all(), "a tile before n_full needs a mask"
+                assert vis.any(), "an emitted tile is fully masked"
+                kk = keys[keys < p.total_k]
+                for g in range(G):
+                    cover[h0 + g][np.ix_(rows, kk)] += vis[:, : kk.size]
+        for g in range(G):
+            if slot < 0:
+                rows_written[h0 + g, rows] += 1
+            else:
+                for lr in range(nrows):
+                    s = slot + lr * G + g
+                    assert s not in partial_slots, "two items write one partial slot"
+                    partial_slots[s] = (q0 + lr, h0 + g)
+    combined = np.zeros((hq, p.total_q), dtype=np.int32)
+    for c in m["comb"]:
+        q0, nrows, h0, nch, slot0 = c[:5]
+        for lr in range(nrows):
+            for g in range(G):
+                combined[h0 + g, q0 + lr] += 1
+                for ch in range(nch):
+                    assert partial_slots.pop(slot0 + ch * 128 + lr * G + g) == (q0 + lr, h0 + g)
+    assert not partial_slots, "partial slots nobody combines"
+    # every (row, head) is finalised exactly once, by the main kernel or by the combine
+    assert ((rows_written + combined) == 1).all()
+    return cover, m
+
+
+def check_plan(p, **kw):
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, num_cus=kw.pop("num_cus", NCU), **kw)
+    cover, m = rasterise(p, plan)
+    mask = oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k)
+    for h in range(p.heads_q):
+        assert (cover[h] == mask).all(), f"head {h}: coverage differs from the mask"
+    assert plan.info["visible_pairs"] == int(mask.sum())
+    return plan, m
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_worklist_covers_mask_exactly_once(seed):
+    rng = np.random.default_rng(seed)
+    tq, tk = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    p = W.random_problem(seed, tq, tk, hq, hkv, 64)
+    check_plan(p)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_forced_split_covers_mask_exactly_once(seed):
+    rng = np.random.default_rng(50 + seed)
+    p = W.random_problem(50 + seed, int(rng.integers(40, 260)), int(rng.integers(200, 700)), 4, 1, 128)
+    plan, m = check_plan(p, split_tiles=int(rng.integers(1, 4)), max_splits=int(rng.integers(2, 6)))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_scaled_configs_cover_mask(cfg):
+    p = W.scaled(cfg, {1: 1, 2: 16, 3: 16, 4: 32}[cfg])
+    p.heads_q, p.heads_kv = min(p.heads_q, 8), min(p.heads_kv, 2)
+    check_plan(p)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_visible_pairs_match_oracle_at_full_size(cfg):
+    p = W.config(cfg)
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, num_cus=NCU)
+    if cfg == 5:
+        expect = 131072 * 131073 // 2
+    else:
+        expect = oracle.count_visible_pairs(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k)
+    assert plan.info["visible_pairs"] == expect
+    assert plan.info["computed_pairs"] >= expect
+
+
+def test_plan_meta_layout_and_order():
+    p = W.config(3)
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, num_cus=NCU)
+    i = plan.info
+    assert i["meta_bytes"] == 4 * (HDR + REC * (i["num_items"] + i["num_runs"] + i["num_combine"]))
+    m = parse(plan.meta_host())
+    assert m["G"] == 4 and m["rows"] == 32 and m["bn"] == 64
+    cost = m["items"][:, 6] + 2 * (m["items"][:, 4] > 0)
+    assert (np.diff(cost) <= 0).all(), "items are not longest-first"
+    # per-document causal: one run per item, every row of the problem in some item
+    assert (m["items"][:, 4] == 1).all()
+
+
+def test_auto_split_only_when_items_cannot_fill_the_device():
+    # one long causal sequence with few heads: items far longer than a fair share -> split
+    p = W.make_problem("long_few", 256, 65536, 4, 1, 128, [((0, 256), (0, 65536), W.CAUSAL)])
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, num_cus=NCU)
+    assert plan.info["num_split_items"] > 0 and plan.info["num_combine"] > 0
+    assert plan.info["workspace_bytes"] > 0
+    # the packed-document workload fills the device without splitting
+    p3 = W.config(3)
+    plan3 = ffa.Plan(p3.q_ranges, p3.k_ranges, p3.mask_types, p3.total_q, p3.total_k, p3.heads_q, p3.heads_kv,
+                     p3.head_dim, num_cus=NCU)
+    assert plan3.info["num_split_items"] == 0 and plan3.info["workspace_bytes"] == 0
+    # never split below the minimum chunk
+    plan_n = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                      p.head_dim, num_cus=NCU, split_tiles=-1)
+    assert plan_n.info["num_split_items"] == 0
+
+
+def test_fwd_rejects_bad_arguments_without_launching(lib):
+    p = ffa.Plan([[0, 64]], [[0, 64]], [1], 64, 64, 2, 2, 128, num_cus=NCU)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    def call(**kw):
+        a = dict(meta=fake, batch=1, q=fake, k=fake, v=fake, out=fake, lse=fake, st=2 * 128, sh=128,
+                 scale=0.1, ws=None, wsb=0)
+        a.update(kw)
+        return lib.ffa_fwd(p.handle, a["meta"], a["batch"], a["q"], 0, a["st"], a["sh"], a["k"], 0, a["st"],
+                           a["sh"], a["v"], 0, a["st"], a["sh"], a["out"], 0, a["st"], a["sh"], a["lse"], 0, 2, 1,
+                           a["scale"], a["ws"], a["wsb"], None)
+    assert call(batch=0) == 11
+    assert call(scale=float("nan")) == 11
+    assert call(scale=0.0) == 11
+    assert call(meta=None) == 1
+    assert call(q=None) == 1
+    assert call(k=None) == 1
+    assert call(q=fake + 2) == 10
+    assert call(st=2 * 128 + 4) == 10
+    assert lib.ffa_fwd(None, fake, 1, fake, 0, 1, 1, fake, 0, 1, 1, fake, 0, 1, 1, fake, 0, 1, 1, fake, 0, 1, 1,
+                       0.1, None, 0, None) == 1
+    # a split plan without workspace
+    ps = ffa.Plan([[0, 32]], [[0, 8192]], [0], 32, 8192, 4, 1, 128, num_cus=NCU, split_tiles=16)
+    assert ps.info["workspace_bytes"] > 0
+    assert lib.ffa_fwd(ps.handle, fake, 1, fake, 0, 512, 128, fake, 0, 128, 128, fake, 0, 128, 128, fake, 0, 512,
+                       128, fake, 0, 4, 1, 0.1, None, 0, None) == 7
