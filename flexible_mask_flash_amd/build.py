@@ -20,7 +20,7 @@ ARCH = "gfx950"
 SOURCES = ["ffa_plan.cpp", "ffa_fwd.hip"]
 
 # Packed fp32 VALU ops are disabled: the compiler must not form v_pk_{add,mul,fma}_f32.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans"]
 
 
 def hipcc() -> str:

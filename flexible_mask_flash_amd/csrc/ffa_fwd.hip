@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -90,13 +91,18 @@ struct CombineArgs {
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
+// buffer resource word 3 for raw (untyped) dword loads on gfx9-class parts
+constexpr int kBufferFlags = 0x00020000;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: the running max may lag by up to 2^8
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 
-// LDS row swizzles (16-byte chunk index XOR), see the header comment.
+// LDS row swizzles (16-byte chunk index XOR by key row).
+//  K rows are read as MFMA A operands: lanes 0-15 read one chunk of rows
+//  r..r+15, so the XOR spreads those 16 rows over all 16-byte bank groups.
+//  V rows are read transposed: a 16-lane group reads two chunks of four
+//  consecutive rows, so four consecutive rows are spread by 4 chunks.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
@@ -106,18 +112,52 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
+// LDS reads are issued through inline asm with an explicit address register and
+// a compile-time offset; the results are waited for with lds_wait<N>() (at most N
+// LDS reads of this wave still outstanding) and pinned behind that wait with
+// fence().  Going around the compiler here keeps it from draining the in-flight
+// K/V prefetch (it cannot prove the reads and the DMA writes are disjoint) and
+// lets several reads be in flight while MFMAs run.
+template <int OFF>
+__device__ __forceinline__ f32x4_t lds_read_b128(uint32_t addr) {
+  f32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4 of
 // the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12 of the group.
 // Pointing lane j at row (key0 + j/4), columns (c0 + 4*(j%4) .. +3) therefore
 // hands lane i the column c0 + i of rows key0 .. key0+3.
-__device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
+template <int OFF>
+__device__ __forceinline__ s16x4_t lds_read_tr16(uint32_t addr) {
   s16x4_t r;
-  const uint32_t addr = (uint32_t)(uintptr_t)(const FFA_LDS char*)p;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return r;
 }
+// compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
 
-// Workgroup barrier without a memory fence (the LDS waits are explicit), but a
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void fence(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Workgroup barrier without a memory fence (the waits are explicit), but a
 // compiler barrier for memory operations on both sides.
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
@@ -134,22 +174,22 @@ __device__ __forceinline__ float partner_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+__device__ __forceinline__ bf16x8_t as_bf16x8(f32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
   constexpr int BN = kBlockN;          // 64 keys per tile
-  constexpr int CH = D / 8;            // 16-byte chunks per K/V row
-  constexpr int KSTEPS = D / 16;       // MFMA k-steps of Q K^T
+  constexpr int ROWB = D * 2;          // bytes of one K/V row
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int KSTEPS = D / 16;       // MFMA k-steps of K Q^T
   constexpr int DBLK = D / 32;         // 32-wide head-dim blocks of O
-  constexpr int TILE = BN * D * 2;     // bytes of one K or V tile
-  constexpr int NLD = TILE / 4096;     // 16-byte DMA loads per thread per tile (K or V)
-  static_assert(BN == 64, "tile shape");
-  // Four distinct LDS objects (not one array): with the buffer chosen at compile
-  // time the compiler can tell a DMA into one buffer from reads of the other and
-  // does not drain the prefetch before every LDS read.
-  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+  constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
+  constexpr int NLD = TILE / 4096;     // DMA instructions per thread per K (or V) tile
+  constexpr int RPL = 4096 / ROWB;     // key rows between consecutive DMA instructions
+  static_assert(BN == 64 && (D == 64 || D == 128), "tile shape");
+  // one LDS array: K0 | V0 | K1 | V1; every read offset is a compile-time immediate
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  constexpr int kOffK0 = 0, kOffV0 = TILE, kOffK1 = 2 * TILE, kOffV1 = 3 * TILE;
 
   const int bid = blockIdx.x;
   const int item_idx = bid / a.batch;
@@ -159,7 +199,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int slot = itp[5], total_tiles = itp[6];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int hh = lane >> 5;            // which half of the 64 lanes
   const int G = a.heads_per_item;
   const int g = wave % G, rsub = wave / G;
@@ -169,10 +210,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int row = q0 + lrow;
   const bool row_ok = lrow < nrows;
 
-  const __bf16* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
-  const __bf16* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
+  const char* kbase = (const char*)(a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh);
+  const char* vbase = (const char*)(a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
 
-  // ---- Q^T operand: lane holds query `row`, head-dim half hh (contiguous D/2 values)
+  // ---- Q^T operand: lane holds query `row`, head-dim half hh (D/2 contiguous values)
   bf16x8_t qf[KSTEPS];
   if (row_ok && n_runs > 0) {
     const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh +
@@ -194,21 +235,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY;  // running max, log2 units (already scaled)
   float l_run = 0.0f;       // this lane's part of the row sum
 
-  // ---- tile loader: K and V tile at key `kstart` into buffer BUF
+  // ---- per-lane LDS read addresses (the low 10 bits of the LDS base are zero)
+  const uint32_t lds = (uint32_t)(uintptr_t)(FFA_LDS char*)smem;
+  // K fragment of k-step s: row (lane & 31) (+32 per key block), chunk (D/16)*hh + s
+  uint32_t k_addr[KSTEPS];
+  {
+    const int r = lane & 31;
+    const uint32_t a0 = lds + r * ROWB + ((((D / 16) * hh) ^ swz_k<D>(r)) << 4);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) k_addr[s] = a0 ^ (s << 4);
+  }
+  // V^T fragment of head-dim block d: rows 4hh + j/4 (+16 t, +8), column 32d + 16(grp&1) + 4(j&3)
+  uint32_t v_addr[DBLK];
+  {
+    const int grp = lane >> 4, jl = lane & 15;
+    const int vr = 4 * hh + (jl >> 2);
+    const int cl = 2 * (grp & 1) + ((jl & 3) >> 1);
+    const uint32_t a0 = lds + vr * ROWB + ((cl ^ swz_v<D>(vr)) << 4) + (jl & 1) * 8;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d) v_addr[d] = a0 ^ (d << 6);
+  }
+
+  // ---- DMA of a K/V tile: instruction i of wave w fills LDS block (4i + w) of the
+  // tile; lane l's 16 bytes are chunk (lin % CH) of key row (lin / CH), lin = 64 (4i + w) + l,
+  // loaded from the swizzled global chunk.  The lane's byte offset inside the tile
+  // is the same for every i up to a whole number of rows, so the address is a
+  // scalar base plus one constant 32-bit offset per lane.
+  const int lin0 = wave * 64 + lane;
+  const int dr0 = lin0 / CH, dp = lin0 % CH;
+  const int64_t kst_b = a.k_st * 2, vst_b = a.v_st * 2;
+  const uint32_t k_goff = (uint32_t)(dr0 * kst_b) + ((dp ^ swz_k<D>(dr0)) << 4);
+  const uint32_t v_goff = (uint32_t)(dr0 * vst_b) + ((dp ^ swz_v<D>(dr0)) << 4);
   auto load_tile = [&](auto buf_tag, int kstart) {
     constexpr int BUF = decltype(buf_tag)::value;
-    char* kdst = BUF == 0 ? k_lds0 : k_lds1;
-    char* vdst = BUF == 0 ? v_lds0 : v_lds1;
+    char* kdst = smem + (BUF == 0 ? kOffK0 : kOffK1);
+    char* vdst = smem + (BUF == 0 ? kOffV0 : kOffV1);
+    if (kstart + BN <= a.total_k) {
+      // buffer resources based at the tile's first key row: scalar row offsets,
+      // one constant per-lane offset, no per-load vector arithmetic
+      const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kbase + (int64_t)kstart * kst_b), (short)0, 0x7fffffff, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vbase + (int64_t)kstart * vst_b), (short)0, 0x7fffffff, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int blk = i * 4 + wave;     // this wave's 1 KB block of the tile
-      const int lin = blk * 64 + lane;  // 16-byte chunk index in the tile
-      const int r = lin / CH, p = lin % CH;
-      const int key = min(kstart + r, a.total_k - 1);  // rows past the data are masked later
-      const __bf16* ks = kbase + (int64_t)key * a.k_st + ((p ^ swz_k<D>(r)) * 8);
-      const __bf16* vs = vbase + (int64_t)key * a.v_st + ((p ^ swz_v<D>(r)) * 8);
-      __builtin_amdgcn_global_load_lds((const void*)ks, (FFA_LDS void*)(kdst + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)vs, (FFA_LDS void*)(vdst + blk * 1024), 16, 0, 0);
+      for (int i = 0; i < NLD; ++i) {
+        const int blk = i * 4 + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FFA_LDS void*)(kdst + blk * 1024), 16, k_goff,
+                                                 (int)(i * RPL * kst_b), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FFA_LDS void*)(vdst + blk * 1024), 16, v_goff,
+                                                 (int)(i * RPL * vst_b), 0, 0);
+      }
+    } else {
+      // last tile of the key axis: rows past total_k re-read the last row (they are masked)
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int blk = i * 4 + wave;
+        const int key = min(kstart + dr0 + i * RPL, a.total_k - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + (int64_t)key * kst_b + ((dp ^ swz_k<D>(dr0)) << 4)),
+                                         (FFA_LDS void*)(kdst + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + (int64_t)key * vst_b + ((dp ^ swz_v<D>(dr0)) << 4)),
+                                         (FFA_LDS void*)(vdst + blk * 1024), 16, 0, 0);
+      }
     }
   };
 
@@ -222,64 +309,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   const float c2 = a.scale_log2;
-  const int grp = lane >> 4, jl = lane & 15;
 
-  // One pipeline step: prefetch tile it+1 into the other buffer, then compute
-  // tile `it` from buffer BUF.
+  // One pipeline step on tile `it`, held in buffer BUF: wait for its DMA, one
+  // barrier (its data is visible to all waves, and every wave is done with the
+  // other buffer), start the DMA of tile it+1 into the other buffer, compute.
   auto step = [&](auto buf_tag, int it) {
     constexpr int BUF = decltype(buf_tag)::value;
-    const char* ks = BUF == 0 ? k_lds0 : k_lds1;
-    const char* vs = BUF == 0 ? v_lds0 : v_lds1;
+    constexpr int OK = BUF == 0 ? kOffK0 : kOffK1;
+    constexpr int OV = BUF == 0 ? kOffV0 : kOffV1;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    wg_barrier();
+
     // next tile position
-    int n_ri = ri, n_ti = ti + 1, n_k0 = r_k0;
+    int n_ri = ri, n_ti = ti + 1;
     if (n_ti >= r_nt && it + 1 < total_tiles) {
       n_ri = ri + 1;
       n_ti = 0;
-      n_k0 = rp[n_ri * kRec + 0];
     }
     if (it + 1 < total_tiles) {
+      const int n_k0 = n_ri == ri ? r_k0 : rp[n_ri * kRec + 0];
       load_tile(std::integral_constant<int, 1 - BUF>{}, n_k0 + n_ti * BN);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NLD));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    wg_barrier();
 
     const int kstart = r_k0 + ti * BN;
 
-    // ---- S^T = K Q^T  (two 32-key blocks)
-    f32x16_t sacc[2];
+    // ---- S^T = K Q^T: key block 0 fragments first, then block 1's reads ride
+    // behind block 0's MFMAs (each reuses the register its MFMA just consumed)
+    f32x16_t s0, s1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int i = 0; i < 16; ++i) { s0[i] = 0.0f; s1[i] = 0.0f; }
+    f32x4_t kf[KSTEPS];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.0f;
-      const int r = kb * 32 + (lane & 31);
+    for (int s = 0; s < KSTEPS; ++s) kf[s] = lds_read_b128<OK>(k_addr[s]);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int c = (D / 16) * hh + s;
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + r * (D * 2) + ((c ^ swz_k<D>(r)) * 16));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
-      }
+    for (int s = 0; s < KSTEPS; ++s) {
+      lds_wait<KSTEPS - 1>();
+      fence(kf[s]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), qf[s], s0, 0, 0, 0);
+      kf[s] = lds_read_b128<OK + 32 * ROWB>(k_addr[s]);
     }
+    static_for<KSTEPS>([&](auto s_tag) {
+      constexpr int s = decltype(s_tag)::value;
+      lds_wait<KSTEPS - 1 - s>();
+      fence(kf[s]);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), qf[s], s1, 0, 0, 0);
+    });
 
     // ---- edge mask: key j (absolute) visible iff j < min(k_hi, row + edge_base)
     if (ti >= r_nf) {
-      const int lim = min(r_khi, row + r_eb) - kstart;
+      const int lim = min(r_khi, row + r_eb) - kstart - 4 * hh;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rel = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (rel >= lim) sacc[kb][i] = -INFINITY;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int rel = 8 * (i >> 2) + (i & 3);
+        if (rel >= lim) s0[i] = -INFINITY;
+        if (rel + 32 >= lim) s1[i] = -INFINITY;
+      }
     }
 
     // ---- online softmax (base 2)
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);  // v_max3
     mx = partner_max(mx) * c2;
     const float m_new = fmaxf(m_run, mx);
     const bool need = m_new > m_run + kRescaleThreshold;
@@ -293,49 +383,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
     }
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+    // P in fp32 for the row sum (the lse needs the unrounded sum), bf16 for P V
     bf16x8_t pf[4];
+    float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c2, -msub));
-        l_run += p;
-        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
-      }
-
-    // ---- O^T += V^T P^T
-    // The transposed reads go through inline asm: the compiler has no alias
-    // information for them and would otherwise drain the in-flight prefetch of
-    // the other buffer before the first one.  Their results are waited for
-    // explicitly (lgkmcnt) before the MFMAs use them.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {  // 16 keys per MFMA
-      const int key_lo = 16 * t + 4 * hh + (jl >> 2);
-      s16x4_t vlo[DBLK], vhi[DBLK];
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d) {
-        const int dcol = 32 * d + 16 * (grp & 1) + 4 * (jl & 3);
-        const int c = dcol >> 3, half = (dcol >> 2) & 1;
-        const int r0 = key_lo, r1 = key_lo + 8;
-        vlo[d] = lds_read_tr16(vs + r0 * (D * 2) + ((c ^ swz_v<D>(r0)) * 16) + half * 8);
-        vhi[d] = lds_read_tr16(vs + r1 * (D * 2) + ((c ^ swz_v<D>(r1)) * 16) + half * 8);
-      }
-      // wait for the transposed reads, and make every result depend on that
-      // wait so that no MFMA can be scheduled above it
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d) asm volatile("" : "+v"(vlo[d]), "+v"(vhi[d]));
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d) {
-        const s16x8_t vv = {vlo[d][0], vlo[d][1], vlo[d][2], vlo[d][3], vhi[d][0], vhi[d][1], vhi[d][2], vhi[d][3]};
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[t], o[d], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c2, -msub));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c2, -msub));
+      ps0 += p0;
+      ps1 += p1;
+      pf[i >> 3][i & 7] = (__bf16)p0;
+      pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
     }
+    l_run += ps0 + ps1;
 
-    // every LDS read of this buffer has returned before the barrier that lets
-    // the next prefetch overwrite it
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    wg_barrier();
+    // ---- O^T += V^T P^T, 16 keys per MFMA; the reads of step t+1 are in flight
+    // while the MFMAs of step t run
+    s16x4_t vlo[2][DBLK], vhi[2][DBLK];
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d) {
+      vlo[0][d] = lds_read_tr16<OV>(v_addr[d]);
+      vhi[0][d] = lds_read_tr16<OV + 8 * ROWB>(v_addr[d]);
+    }
+    static_for<4>([&](auto t_tag) {
+      constexpr int t = decltype(t_tag)::value;
+      constexpr int cur = t & 1, nxt = cur ^ 1;
+      if constexpr (t + 1 < 4) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) {
+          vlo[nxt][d] = lds_read_tr16<OV + 16 * (t + 1) * ROWB>(v_addr[d]);
+          vhi[nxt][d] = lds_read_tr16<OV + (16 * (t + 1) + 8) * ROWB>(v_addr[d]);
+        }
+      }
+      constexpr int ahead = (t + 1 < 4) ? 2 * DBLK : 0;
+      static_for<DBLK>([&](auto d_tag) {
+        constexpr int d = decltype(d_tag)::value;
+        lds_wait<2 * (DBLK - 1 - d) + ahead>();
+        fence(vlo[cur][d]);
+        fence(vhi[cur][d]);
+        const s16x8_t vv = {vlo[cur][d][0], vlo[cur][d][1], vlo[cur][d][2], vlo[cur][d][3],
+                            vhi[cur][d][0], vhi[cur][d][1], vhi[cur][d][2], vhi[cur][d][3]};
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[t], o[d], 0, 0, 0);
+      });
+    });
 
     // advance the iterator
     if (n_ri != ri) {
@@ -563,6 +653,10 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   if (!st8(q_sb) || !st8(q_st) || !st8(q_sh) || !st8(k_sb) || !st8(k_st) || !st8(k_sh) || !st8(v_sb) ||
       !st8(v_st) || !st8(v_sh) || !st8(o_sb) || !st8(o_st) || !st8(o_sh))
     return ffa::set_error(FFA_ERR_ALIGN, "q, k, v and out strides must be multiples of 8 elements");
+  // the kernels address one 64-key tile with 32-bit offsets
+  const int64_t kv_lim = ((int64_t)1 << 31) / (2 * ffa::kBlockN);
+  if (need_kv && (std::llabs(k_st) >= kv_lim || std::llabs(v_st) >= kv_lim))
+    return ffa::set_error(FFA_ERR_ARG, "k / v token strides must be below 2^24 elements");
   if (p.num_items == 0) return FFA_OK;
   if ((int64_t)p.num_items * batch > INT32_MAX || (int64_t)p.num_combine * batch > INT32_MAX)
     return ffa::set_error(FFA_ERR_ARG, "grid too large");
