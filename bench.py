@@ -39,7 +39,50 @@ def parse():
     ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "flexible_mask_flash_amd", "csrc", f)
+                  for f in ("ffa_fwd.hip", "ffa_internal.h", "ffa_plan.cpp")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the main kernel from profiles/traffic.json (FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy's reading), or None when missing or taken on another kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else w.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+
+    n = 1 << 30  # bytes
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
 def cpu_baseline(p, q, k, v, budget_s: float):
@@ -84,6 +127,9 @@ def cpu_baseline(p, q, k, v, budget_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -176,7 +222,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(p.name),
             "kernel": "ffa_fwd_main",
             "algorithmic_flops_per_launch": flops,
         },
