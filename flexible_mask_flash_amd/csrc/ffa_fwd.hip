@@ -176,20 +176,45 @@ __device__ __forceinline__ float partner_sum(float x) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(f32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
+// Tile iterator over an item's runs (wave-uniform): the tile's first key and the
+// mask parameters of its run.
+struct TileIt {
+  int ri, ti, k0, nt, nf, khi, eb;
+  __device__ __forceinline__ int kstart() const { return k0 + ti * kBlockN; }
+  __device__ __forceinline__ bool edge() const { return ti >= nf; }
+};
+__device__ __forceinline__ void tile_first(TileIt& t, const FFA_CONST int32_t* rp) {
+  t.ri = 0; t.ti = 0;
+  t.k0 = rp[0]; t.nt = rp[1]; t.nf = rp[2]; t.khi = rp[3]; t.eb = rp[4];
+}
+__device__ __forceinline__ void tile_next(TileIt& t, const FFA_CONST int32_t* rp, int n_runs) {
+  if (++t.ti >= t.nt && t.ri + 1 < n_runs) {
+    ++t.ri;
+    t.ti = 0;
+    const FFA_CONST int32_t* r = rp + t.ri * kRec;
+    t.k0 = r[0]; t.nt = r[1]; t.nf = r[2]; t.khi = r[3]; t.eb = r[4];
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
   constexpr int BN = kBlockN;          // 64 keys per tile
   constexpr int ROWB = D * 2;          // bytes of one K/V row
   constexpr int CH = D / 8;            // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;       // MFMA k-steps of K Q^T
+  constexpr int KSTEPS = D / 16;       // MFMA k-steps of K Q^T per 32-key block
   constexpr int DBLK = D / 32;         // 32-wide head-dim blocks of O
   constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
   constexpr int NLD = TILE / 4096;     // DMA instructions per thread per K (or V) tile
   constexpr int RPL = 4096 / ROWB;     // key rows between consecutive DMA instructions
+  constexpr int QSLOTS = 2 * KSTEPS;   // MFMAs of one K Q^T tile
+  constexpr int PSLOTS = 4 * DBLK;     // MFMAs of one V^T P^T tile
+  constexpr int EPQ = 32 / QSLOTS;     // score elements exponentiated per K Q^T MFMA
+  constexpr int EPP = 32 / PSLOTS;     // score elements max-reduced per P V MFMA
   static_assert(BN == 64 && (D == 64 || D == 128), "tile shape");
   // one LDS array: K0 | V0 | K1 | V1; every read offset is a compile-time immediate
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
-  constexpr int kOffK0 = 0, kOffV0 = TILE, kOffK1 = 2 * TILE, kOffV1 = 3 * TILE;
+  constexpr int kOffK[2] = {0, 2 * TILE};
+  constexpr int kOffV[2] = {TILE, 3 * TILE};
 
   const int bid = blockIdx.x;
   const int item_idx = bid / a.batch;
@@ -256,149 +281,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int d = 0; d < DBLK; ++d) v_addr[d] = a0 ^ (d << 6);
   }
 
-  // ---- DMA of a K/V tile: instruction i of wave w fills LDS block (4i + w) of the
-  // tile; lane l's 16 bytes are chunk (lin % CH) of key row (lin / CH), lin = 64 (4i + w) + l,
-  // loaded from the swizzled global chunk.  The lane's byte offset inside the tile
-  // is the same for every i up to a whole number of rows, so the address is a
-  // scalar base plus one constant 32-bit offset per lane.
+  // ---- DMA of a K or V tile: instruction i of wave w fills LDS block (4i + w) of
+  // the tile; lane l's 16 bytes are chunk (lin % CH) of key row (lin / CH),
+  // lin = 64 (4i + w) + l, loaded from the swizzled global chunk.  The lane's
+  // offset is the same for every i up to whole rows, so each load is a scalar
+  // base plus one constant 32-bit per-lane offset.
   const int lin0 = wave * 64 + lane;
   const int dr0 = lin0 / CH, dp = lin0 % CH;
   const int64_t kst_b = a.k_st * 2, vst_b = a.v_st * 2;
   const uint32_t k_goff = (uint32_t)(dr0 * kst_b) + ((dp ^ swz_k<D>(dr0)) << 4);
   const uint32_t v_goff = (uint32_t)(dr0 * vst_b) + ((dp ^ swz_v<D>(dr0)) << 4);
-  auto load_tile = [&](auto buf_tag, int kstart) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    char* kdst = smem + (BUF == 0 ? kOffK0 : kOffK1);
-    char* vdst = smem + (BUF == 0 ? kOffV0 : kOffV1);
+  auto dma = [&](const char* base, int64_t st_b, uint32_t goff, int swzc, char* dst, int kstart) {
     if (kstart + BN <= a.total_k) {
-      // buffer resources based at the tile's first key row: scalar row offsets,
-      // one constant per-lane offset, no per-load vector arithmetic
-      const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kbase + (int64_t)kstart * kst_b), (short)0, 0x7fffffff, kBufferFlags);
-      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vbase + (int64_t)kstart * vst_b), (short)0, 0x7fffffff, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kstart * st_b), (short)0, 0x7fffffff, kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int blk = i * 4 + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FFA_LDS void*)(kdst + blk * 1024), 16, k_goff,
-                                                 (int)(i * RPL * kst_b), 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FFA_LDS void*)(vdst + blk * 1024), 16, v_goff,
-                                                 (int)(i * RPL * vst_b), 0, 0);
-      }
+      for (int i = 0; i < NLD; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(dst + (i * 4 + wave) * 1024), 16, goff,
+                                                 (int)(i * RPL * st_b), 0, 0);
     } else {
       // last tile of the key axis: rows past total_k re-read the last row (they are masked)
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int blk = i * 4 + wave;
         const int key = min(kstart + dr0 + i * RPL, a.total_k - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + (int64_t)key * kst_b + ((dp ^ swz_k<D>(dr0)) << 4)),
-                                         (FFA_LDS void*)(kdst + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase + (int64_t)key * vst_b + ((dp ^ swz_v<D>(dr0)) << 4)),
-                                         (FFA_LDS void*)(vdst + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)key * st_b + ((dp ^ swzc) << 4)),
+                                         (FFA_LDS void*)(dst + (i * 4 + wave) * 1024), 16, 0, 0);
       }
     }
   };
-
-  // ---- run iterator (wave-uniform)
-  const FFA_CONST int32_t* rp = (const FFA_CONST int32_t*)(a.runs + (int64_t)run_off * kRec);
-  int ri = 0, ti = 0;
-  int r_k0 = 0, r_nt = 0, r_nf = 0, r_khi = 0, r_eb = 0;
-  if (total_tiles > 0) {
-    r_k0 = rp[0]; r_nt = rp[1]; r_nf = rp[2]; r_khi = rp[3]; r_eb = rp[4];
-    load_tile(std::integral_constant<int, 0>{}, r_k0);
-  }
-
-  const float c2 = a.scale_log2;
-
-  // One pipeline step on tile `it`, held in buffer BUF: wait for its DMA, one
-  // barrier (its data is visible to all waves, and every wave is done with the
-  // other buffer), start the DMA of tile it+1 into the other buffer, compute.
-  auto step = [&](auto buf_tag, int it) {
+  auto dma_k = [&](auto buf_tag, int kstart) {
     constexpr int BUF = decltype(buf_tag)::value;
-    constexpr int OK = BUF == 0 ? kOffK0 : kOffK1;
-    constexpr int OV = BUF == 0 ? kOffV0 : kOffV1;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    wg_barrier();
+    dma(kbase, kst_b, k_goff, swz_k<D>(dr0), smem + kOffK[BUF], kstart);
+  };
+  auto dma_v = [&](auto buf_tag, int kstart) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    dma(vbase, vst_b, v_goff, swz_v<D>(dr0), smem + kOffV[BUF], kstart);
+  };
 
-    // next tile position
-    int n_ri = ri, n_ti = ti + 1;
-    if (n_ti >= r_nt && it + 1 < total_tiles) {
-      n_ri = ri + 1;
-      n_ti = 0;
-    }
-    if (it + 1 < total_tiles) {
-      const int n_k0 = n_ri == ri ? r_k0 : rp[n_ri * kRec + 0];
-      load_tile(std::integral_constant<int, 1 - BUF>{}, n_k0 + n_ti * BN);
-    }
-
-    const int kstart = r_k0 + ti * BN;
-
-    // ---- S^T = K Q^T: key block 0 fragments first, then block 1's reads ride
-    // behind block 0's MFMAs (each reuses the register its MFMA just consumed)
-    f32x16_t s0, s1;
+  // ---- K Q^T of one tile from K buffer BUF into (sa, sb); hook(slot) runs after
+  // the slot-th MFMA is issued, so independent VALU work overlaps the MFMAs
+  auto qk = [&](auto buf_tag, f32x16_t& sa, f32x16_t& sb, auto&& hook) {
+    constexpr int OK = kOffK[decltype(buf_tag)::value];
+    constexpr int NQ = 2 * KSTEPS;   // fragments of the tile, in MFMA order
+    constexpr int KIF = 4;           // fragment reads in flight (a ring of KIF registers)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { s0[i] = 0.0f; s1[i] = 0.0f; }
-    f32x4_t kf[KSTEPS];
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) kf[s] = lds_read_b128<OK>(k_addr[s]);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      lds_wait<KSTEPS - 1>();
-      fence(kf[s]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), qf[s], s0, 0, 0, 0);
-      kf[s] = lds_read_b128<OK + 32 * ROWB>(k_addr[s]);
-    }
-    static_for<KSTEPS>([&](auto s_tag) {
-      constexpr int s = decltype(s_tag)::value;
-      lds_wait<KSTEPS - 1 - s>();
-      fence(kf[s]);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), qf[s], s1, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) { sa[i] = 0.0f; sb[i] = 0.0f; }
+    f32x4_t kf[KIF];
+    static_for<KIF>([&](auto m_tag) {
+      constexpr int m = decltype(m_tag)::value;
+      kf[m] = lds_read_b128<OK + (m / KSTEPS) * 32 * ROWB>(k_addr[m % KSTEPS]);
     });
-
-    // ---- edge mask: key j (absolute) visible iff j < min(k_hi, row + edge_base)
-    if (ti >= r_nf) {
-      const int lim = min(r_khi, row + r_eb) - kstart - 4 * hh;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rel = 8 * (i >> 2) + (i & 3);
-        if (rel >= lim) s0[i] = -INFINITY;
-        if (rel + 32 >= lim) s1[i] = -INFINITY;
+    static_for<NQ>([&](auto m_tag) {
+      constexpr int m = decltype(m_tag)::value;
+      constexpr int later = (m + KIF - 1 < NQ - 1) ? KIF - 1 : NQ - 1 - m;  // reads issued after read m
+      lds_wait<later>();
+      fence(kf[m % KIF]);
+      if constexpr (m < KSTEPS)
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m], sa, 0, 0, 0);
+      else
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m - KSTEPS], sb, 0, 0, 0);
+      if constexpr (m + KIF < NQ) {
+        constexpr int r = m + KIF;
+        kf[m % KIF] = lds_read_b128<OK + (r / KSTEPS) * 32 * ROWB>(k_addr[r % KSTEPS]);
       }
-    }
+      hook(std::integral_constant<int, m>{});
+    });
+  };
 
-    // ---- online softmax (base 2)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);  // v_max3
-    mx = partner_max(mx) * c2;
-    const float m_new = fmaxf(m_run, mx);
-    const bool need = m_new > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      if (need) m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-    }
-    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    // P in fp32 for the row sum (the lse needs the unrounded sum), bf16 for P V
-    bf16x8_t pf[4];
-    float ps0 = 0.0f, ps1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c2, -msub));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c2, -msub));
-      ps0 += p0;
-      ps1 += p1;
-      pf[i >> 3][i & 7] = (__bf16)p0;
-      pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
-    }
-    l_run += ps0 + ps1;
-
-    // ---- O^T += V^T P^T, 16 keys per MFMA; the reads of step t+1 are in flight
-    // while the MFMAs of step t run
+  // ---- O^T += V^T P^T of one tile from V buffer BUF (16 keys per MFMA; the reads
+  // of step t+1 are in flight during the MFMAs of step t); hook(slot) as above
+  auto pv = [&](auto buf_tag, const bf16x8_t (&pf)[4], auto&& hook) {
+    constexpr int OV = kOffV[decltype(buf_tag)::value];
     s16x4_t vlo[2][DBLK], vhi[2][DBLK];
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
@@ -424,21 +377,147 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const s16x8_t vv = {vlo[cur][d][0], vlo[cur][d][1], vlo[cur][d][2], vlo[cur][d][3],
                             vhi[cur][d][0], vhi[cur][d][1], vhi[cur][d][2], vhi[cur][d][3]};
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[t], o[d], 0, 0, 0);
+        hook(std::integral_constant<int, t * DBLK + d>{});
       });
     });
-
-    // advance the iterator
-    if (n_ri != ri) {
-      ri = n_ri;
-      r_k0 = rp[ri * kRec + 0]; r_nt = rp[ri * kRec + 1]; r_nf = rp[ri * kRec + 2];
-      r_khi = rp[ri * kRec + 3]; r_eb = rp[ri * kRec + 4];
-    }
-    ti = n_ti;
   };
 
-  for (int it = 0; it < total_tiles; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < total_tiles) step(std::integral_constant<int, 1>{}, it + 1);
+  // edge mask of a tile's scores: key j (absolute) visible iff j < min(k_hi, row + edge_base)
+  auto mask = [&](const TileIt& t, f32x16_t& sa, f32x16_t& sb) {
+    const int lim = min(t.khi, row + t.eb) - t.kstart() - 4 * hh;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rel = 8 * (i >> 2) + (i & 3);
+      if (rel >= lim) sa[i] = -INFINITY;
+      if (rel + 32 >= lim) sb[i] = -INFINITY;
+    }
+  };
+
+  const float c2 = a.scale_log2;
+  const FFA_CONST int32_t* rp = (const FFA_CONST int32_t*)(a.runs + (int64_t)run_off * kRec);
+
+  if (total_tiles > 0) {
+    // Software pipeline: iteration j exponentiates the scores of tile j while the
+    // MFMAs of K Q^T for tile j+1 run, then multiplies P_j V_j while the scores of
+    // tile j+1 are masked and max-reduced.  K is one tile ahead of V:
+    // LDS holds K_{j+1}, V_j, and receives K_{j+2}, V_{j+1} during iteration j.
+    TileIt t0;
+    tile_first(t0, rp);
+    dma_k(std::integral_constant<int, 0>{}, t0.kstart());
+    dma_v(std::integral_constant<int, 0>{}, t0.kstart());
+    TileIt tA = t0, tB;   // tA: tile j+1, tB: tile j+2
+    tile_next(tA, rp, n_runs);
+    tB = tA;
+    tile_next(tB, rp, n_runs);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    wg_barrier();
+    if (total_tiles > 1) dma_k(std::integral_constant<int, 1>{}, tA.kstart());
+
+    // two score sets alternate between even and odd tiles (no copies)
+    f32x16_t sa0, sb0, sa1, sb1;
+    qk(std::integral_constant<int, 0>{}, sa0, sb0, [](auto) {});
+    if (t0.edge()) mask(t0, sa0, sb0);
+    float mxc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mxc = fmaxf(fmaxf(mxc, sa0[i]), sb0[i]);
+    mxc = partner_max(mxc);
+
+    auto iter = [&](auto buf_tag, auto next_tag, int j, f32x16_t& ca, f32x16_t& cb, f32x16_t& na,
+                    f32x16_t& nb) {
+      constexpr int P = decltype(buf_tag)::value;  // V_j in V buffer P, K_{j+1} in K buffer 1-P
+      constexpr bool NEXT = decltype(next_tag)::value;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      wg_barrier();
+      if constexpr (NEXT) {
+        if (j + 2 < total_tiles) dma_k(std::integral_constant<int, P>{}, tB.kstart());
+        dma_v(std::integral_constant<int, 1 - P>{}, tA.kstart());
+      }
+
+      // running max: move it only when it grows by more than 2^8
+      const float m_new = fmaxf(m_run, mxc * c2);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        if (need) m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      }
+      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+
+      // P_j = exp2(S_j * c2 - m), interleaved with K Q^T of tile j+1.  Each hook
+      // packs its probabilities into bf16 pairs and pins them (and the running
+      // sum) with fence(), so the work stays between the MFMAs it is meant to
+      // overlap instead of sinking to its use in P V.
+      uint32_t pu[16];  // bf16 pairs of P_j, pair q = elements 2q, 2q+1
+      float ps = 0.0f;
+      auto exp_hook = [&](auto slot_tag) {
+        constexpr int sl = decltype(slot_tag)::value;
+#pragma unroll
+        for (int e = sl * EPQ; e < (sl + 1) * EPQ; e += 2) {
+          const float s0v = e < 16 ? ca[e] : cb[e - 16];
+          const float s1v = e + 1 < 16 ? ca[e + 1] : cb[e + 1 - 16];
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0v, c2, -msub));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1v, c2, -msub));
+          ps += p0 + p1;
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
+          pu[e >> 1] = __builtin_bit_cast(uint32_t, pr);
+          fence(pu[e >> 1]);
+        }
+        fence(ps);
+      };
+      if constexpr (NEXT) {
+        qk(std::integral_constant<int, 1 - P>{}, na, nb, exp_hook);
+      } else {
+        static_for<QSLOTS>(exp_hook);
+      }
+      l_run += ps;
+      bf16x8_t pf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t w = {pu[4 * t], pu[4 * t + 1], pu[4 * t + 2], pu[4 * t + 3]};
+        pf[t] = __builtin_bit_cast(bf16x8_t, w);
+      }
+
+      // O += P_j V_j, interleaved with the mask and max of tile j+1
+      float mxn = -INFINITY;
+      if constexpr (NEXT) {
+        if (tA.edge()) mask(tA, na, nb);
+        pv(std::integral_constant<int, P>{}, pf, [&](auto slot_tag) {
+          constexpr int sl = decltype(slot_tag)::value;
+#pragma unroll
+          for (int e = sl * EPP; e < (sl + 1) * EPP; e += 2) {
+            const float x0 = e < 16 ? na[e] : nb[e - 16];
+            const float x1 = e + 1 < 16 ? na[e + 1] : nb[e + 1 - 16];
+            mxn = fmaxf(fmaxf(mxn, x0), x1);
+          }
+          fence(mxn);
+        });
+        mxc = partner_max(mxn);
+        tA = tB;
+        tile_next(tB, rp, n_runs);
+      } else {
+        pv(std::integral_constant<int, P>{}, pf, [](auto) {});
+      }
+    };
+
+    // steady state: pairs of iterations that both have a next tile
+    int j = 0;
+    for (; j + 2 < total_tiles; j += 2) {
+      iter(std::integral_constant<int, 0>{}, std::true_type{}, j, sa0, sb0, sa1, sb1);
+      iter(std::integral_constant<int, 1>{}, std::true_type{}, j + 1, sa1, sb1, sa0, sb0);
+    }
+    // tail: one or two tiles left, the last one without a successor
+    if (j + 1 < total_tiles) {
+      iter(std::integral_constant<int, 0>{}, std::true_type{}, j, sa0, sb0, sa1, sb1);
+      iter(std::integral_constant<int, 1>{}, std::false_type{}, j + 1, sa1, sb1, sa0, sb0);
+    } else {
+      iter(std::integral_constant<int, 0>{}, std::false_type{}, j, sa0, sb0, sa1, sb1);
+    }
   }
 
   // ---- epilogue
