@@ -33,8 +33,11 @@ WORKLOADS = {name: i for i, name in __import__("workloads").CONFIG_NAMES.items()
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-warmup-seconds", type=float, default=0.3,
+                    help="keep warming up (untimed) until this much GPU time has passed: the clocks ramp "
+                         "over the first tens of milliseconds of sustained load")
     ap.add_argument("--workload", default="packed_docs", choices=sorted(WORKLOADS))
     ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,8 +169,13 @@ def main():
     def step():
         ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale)
 
-    for _ in range(args.warmup):
+    warm = 0
+    t_w = time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_seconds:
         step()
+        warm += 1
+        if warm % 5 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)  # the stream ffa_fwd launches on
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -193,7 +201,7 @@ def main():
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -1,6 +1,6 @@
 // gfx950 (MI355X) kernels and the C ABI of the flexible-mask attention forward.
 //
-// Main kernel (one workgroup = 4 wavefronts per plan item):
+// Main kernel (one workgroup = 4 wavefronts per plan item, two workgroups per CU):
 //   * wavefront w covers 32 query rows of one query head; the workgroup covers
 //     rows_per_item rows x heads_per_item heads that share one kv head, so a
 //     K/V tile staged in LDS serves 128 (row, head) pairs.
@@ -197,15 +197,17 @@ __device__ __forceinline__ void tile_next(TileIt& t, const FFA_CONST int32_t* rp
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
+__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
   constexpr int BN = kBlockN;          // 64 keys per tile
   constexpr int ROWB = D * 2;          // bytes of one K/V row
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;       // MFMA k-steps of K Q^T per 32-key block
   constexpr int DBLK = D / 32;         // 32-wide head-dim blocks of O
   constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
-  constexpr int NLD = TILE / 4096;     // DMA instructions per thread per K (or V) tile
-  constexpr int RPL = 4096 / ROWB;     // key rows between consecutive DMA instructions
+  constexpr int W = ffa::kWaves;       // wavefronts sharing the DMA of a tile
+  constexpr int NLD = TILE / (1024 * W);  // DMA instructions per thread per K (or V) tile
+  constexpr int RPL = 1024 * W / ROWB;    // key rows between consecutive DMA instructions
+  static_assert(NLD * 1024 * W == TILE, "DMA split");
   constexpr int QSLOTS = 2 * KSTEPS;   // MFMAs of one K Q^T tile
   constexpr int PSLOTS = 4 * DBLK;     // MFMAs of one V^T P^T tile
   constexpr int EPQ = 32 / QSLOTS;     // score elements exponentiated per K Q^T MFMA
@@ -281,9 +283,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int d = 0; d < DBLK; ++d) v_addr[d] = a0 ^ (d << 6);
   }
 
-  // ---- DMA of a K or V tile: instruction i of wave w fills LDS block (4i + w) of
+  // ---- DMA of a K or V tile: instruction i of wave w fills LDS block (W i + w) of
   // the tile; lane l's 16 bytes are chunk (lin % CH) of key row (lin / CH),
-  // lin = 64 (4i + w) + l, loaded from the swizzled global chunk.  The lane's
+  // lin = 64 (W i + w) + l, loaded from the swizzled global chunk.  The lane's
   // offset is the same for every i up to whole rows, so each load is a scalar
   // base plus one constant 32-bit per-lane offset.
   const int lin0 = wave * 64 + lane;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kstart * st_b), (short)0, 0x7fffffff, kBufferFlags);
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(dst + (i * 4 + wave) * 1024), 16, goff,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(dst + (i * W + wave) * 1024), 16, goff,
                                                  (int)(i * RPL * st_b), 0, 0);
     } else {
       // last tile of the key axis: rows past total_k re-read the last row (they are masked)
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < NLD; ++i) {
         const int key = min(kstart + dr0 + i * RPL, a.total_k - 1);
         __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)key * st_b + ((dp ^ swzc) << 4)),
-                                         (FFA_LDS void*)(dst + (i * 4 + wave) * 1024), 16, 0, 0);
+                                         (FFA_LDS void*)(dst + (i * W + wave) * 1024), 16, 0, 0);
       }
     }
   };
@@ -324,34 +326,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int OK = kOffK[decltype(buf_tag)::value];
     constexpr int NQ = 2 * KSTEPS;   // fragments of the tile, in MFMA order
     constexpr int KIF = 4;           // fragment reads in flight (a ring of KIF registers)
+    // MFMA m uses k-step m/2 of key block m%2: the two accumulator chains
+    // alternate, so consecutive MFMAs never depend on each other
 #pragma unroll
     for (int i = 0; i < 16; ++i) { sa[i] = 0.0f; sb[i] = 0.0f; }
+    __builtin_amdgcn_s_setprio(1);
     f32x4_t kf[KIF];
     static_for<KIF>([&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
-      kf[m] = lds_read_b128<OK + (m / KSTEPS) * 32 * ROWB>(k_addr[m % KSTEPS]);
+      kf[m] = lds_read_b128<OK + (m % 2) * 32 * ROWB>(k_addr[m / 2]);
     });
     static_for<NQ>([&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
       constexpr int later = (m + KIF - 1 < NQ - 1) ? KIF - 1 : NQ - 1 - m;  // reads issued after read m
       lds_wait<later>();
       fence(kf[m % KIF]);
-      if constexpr (m < KSTEPS)
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m], sa, 0, 0, 0);
+      if constexpr (m % 2 == 0)
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m / 2], sa, 0, 0, 0);
       else
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m - KSTEPS], sb, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m / 2], sb, 0, 0, 0);
       if constexpr (m + KIF < NQ) {
         constexpr int r = m + KIF;
-        kf[m % KIF] = lds_read_b128<OK + (r / KSTEPS) * 32 * ROWB>(k_addr[r % KSTEPS]);
+        kf[m % KIF] = lds_read_b128<OK + (r % 2) * 32 * ROWB>(k_addr[r / 2]);
       }
       hook(std::integral_constant<int, m>{});
     });
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- O^T += V^T P^T of one tile from V buffer BUF (16 keys per MFMA; the reads
   // of step t+1 are in flight during the MFMAs of step t); hook(slot) as above
   auto pv = [&](auto buf_tag, const bf16x8_t (&pf)[4], auto&& hook) {
     constexpr int OV = kOffV[decltype(buf_tag)::value];
+    __builtin_amdgcn_s_setprio(1);
     s16x4_t vlo[2][DBLK], vhi[2][DBLK];
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
@@ -380,6 +387,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         hook(std::integral_constant<int, t * DBLK + d>{});
       });
     });
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // edge mask of a tile's scores: key j (absolute) visible iff j < min(k_hi, row + edge_base)
@@ -766,9 +774,9 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)((int64_t)p.num_items * batch));
   if (p.head_dim == 128)
-    hipLaunchKernelGGL(ffa_fwd_main<128>, grid, dim3(256), 0, s, fa);
+    hipLaunchKernelGGL(ffa_fwd_main<128>, grid, dim3(64 * ffa::kWaves), 0, s, fa);
   else
-    hipLaunchKernelGGL(ffa_fwd_main<64>, grid, dim3(256), 0, s, fa);
+    hipLaunchKernelGGL(ffa_fwd_main<64>, grid, dim3(64 * ffa::kWaves), 0, s, fa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch ffa_fwd_main");
 

@@ -20,6 +20,8 @@
 // Combine: q0, nrows, h0, n_chunks, slot0, 0, 0, 0
 //          chunk c of row (q0 + r), head (h0 + g) is partial slot
 //          slot0 + c * kSlotsPerItem + r * heads_per_item + g.
+// A workgroup (kWaves wavefronts) covers kSlotsPerItem = 128 (row, head) pairs
+// that share one kv head: 32 rows x 4 heads, 64 x 2 or 128 x 1.
 #pragma once
 
 #include <cstdint>
@@ -33,7 +35,7 @@ namespace ffa {
 constexpr int32_t kMagic = 0x46464131;  // "FFA1"
 constexpr int32_t kBlockN = 64;         // keys per tile
 constexpr int32_t kWaveRows = 32;       // query rows per wavefront (one 32x32 MFMA block)
-constexpr int32_t kWaves = 4;           // wavefronts per workgroup
+constexpr int32_t kWaves = 4;           // wavefronts per workgroup (two workgroups per CU)
 constexpr int32_t kSlotsPerItem = kWaveRows * kWaves;  // (row, head) pairs one workgroup covers
 constexpr int32_t kNoEdge = 0x3fffffff; // edge_base of a full slice: never limits
 constexpr int kRec = 8;                 // int32 per record

@@ -146,7 +146,7 @@ def rasterise(p, plan):
             for g in range(G):
                 combined[h0 + g, q0 + lr] += 1
                 for ch in range(nch):
-                    assert partial_slots.pop(slot0 + ch * 128 + lr * G + g) == (q0 + lr, h0 + g)
+                    assert partial_slots.pop(slot0 + ch * m["rows"] * G + lr * G + g) == (q0 + lr, h0 + g)
     assert not partial_slots, "partial slots nobody combines"
     # every (row, head) is finalised exactly once, by the main kernel or by the combine
     assert ((rows_written + combined) == 1).all()
