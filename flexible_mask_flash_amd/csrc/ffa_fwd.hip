@@ -532,20 +532,38 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const float lsum = partner_sum(l_run);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   const float lse_v = lsum > 0.0f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
-  if (!row_ok) return;
   if (slot < 0) {
-    __bf16* op = a.out + (int64_t)b * a.o_sb + (int64_t)row * a.o_st + (int64_t)h * a.o_sh;
+    // Stage the bf16 tile of this wave (32 rows x D) in LDS, then write whole
+    // rows with 16-byte stores: in the MFMA layout a lane holds 4 consecutive
+    // values of each of 16 head-dim groups, which would otherwise become 8-byte
+    // stores spread over 32 rows.  Every wave is past its last LDS read first.
+    wg_barrier();
+    char* st = smem + wave * (32 * ROWB);
+    {
+      const int q = lane & 31;
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+      for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        bf16x4_t w;
+        for (int gq = 0; gq < 4; ++gq) {
+          bf16x4_t w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[d][4 * gq + e] * inv);
-        *reinterpret_cast<bf16x4_t*>(op + 32 * d + 8 * gq + 4 * hh) = w;
-      }
-    if (hh == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)h * a.l_sh] = lse_v;
-  } else {
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[d][4 * gq + e] * inv);
+          const int c = 4 * d + gq;  // 16-byte chunk of the row
+          *reinterpret_cast<bf16x4_t*>(st + q * ROWB + ((c ^ swz_k<D>(q)) << 4) + hh * 8) = w;
+        }
+    }
+    __bf16* ob = a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+    const int r0 = q0 + rsub * 32;
+    const int nvalid = min(32, nrows - rsub * 32);
+#pragma unroll
+    for (int i = 0; i < 32 * CH / 64; ++i) {
+      const int lin = i * 64 + lane;
+      const int r = lin / CH, c = lin % CH;
+      const f32x4_t val = *reinterpret_cast<const f32x4_t*>(st + r * ROWB + ((c ^ swz_k<D>(r)) << 4));
+      if (r < nvalid) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * a.o_st + c * 8) = val;
+    }
+    if (row_ok && hh == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)h * a.l_sh] = lse_v;
+  } else if (row_ok) {
     const int64_t sidx = (int64_t)b * a.ws_slots + slot + lrow * G + g;
     float* op = a.ws_o + sidx * D;
 #pragma unroll
