@@ -12,10 +12,12 @@
 //   * O^T += V^T P^T with the same MFMA: P^T comes straight from the S^T
 //     registers (bf16), V^T from LDS with ds_read_b64_tr_b16 (4 keys of one
 //     head-dim column per lane, two reads per MFMA operand).
-//   * online softmax in fp32, base 2 (scale * log2 e folded into one FMA);
-//     the running max is only moved when it grows by more than 2^8, so the
-//     rescale of the accumulator is rare (the result is the same: every term
-//     uses one reference point per row).
+//   * online softmax in fp32, base 2 (scale * log2 e folded into one FMA).  A
+//     row's reference point is the max of the first tile where it sees a key;
+//     later tiles are exponentiated against it without a per-tile max, and
+//     only when a probability would exceed 2^64 does the wave take the max,
+//     rescale the accumulator and redo the tile (the result is the same: every
+//     term of a row uses one reference point).
 //   * K and V tiles are double-buffered in LDS and filled by
 //     global_load_lds_dwordx4 (HBM -> LDS without registers), XOR-swizzled by
 //     key row so that both the K row reads and the V transposed reads are
@@ -93,7 +95,11 @@ struct CombineArgs {
 constexpr float kLn2 = 0.69314718055994530942f;
 // buffer resource word 3 for raw (untyped) dword loads on gfx9-class parts
 constexpr int kBufferFlags = 0x00020000;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: the running max may lag by up to 2^8
+// A row keeps its reference point (log2 units) until one of its probabilities
+// would exceed 2^64: a lane's per-tile partial sum above kOverflow sends the
+// whole wave through the exact rescale path.  Values up to 2^64 are exact
+// enough in bf16 / fp32 (relative rounding) and cannot overflow the fp32 sums.
+constexpr float kOverflow = 18446744073709551616.0f;  // 2^64
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -209,9 +215,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   constexpr int RPL = 1024 * W / ROWB;    // key rows between consecutive DMA instructions
   static_assert(NLD * 1024 * W == TILE, "DMA split");
   constexpr int QSLOTS = 2 * KSTEPS;   // MFMAs of one K Q^T tile
-  constexpr int PSLOTS = 4 * DBLK;     // MFMAs of one V^T P^T tile
   constexpr int EPQ = 32 / QSLOTS;     // score elements exponentiated per K Q^T MFMA
-  constexpr int EPP = 32 / PSLOTS;     // score elements max-reduced per P V MFMA
   static_assert(BN == 64 && (D == 64 || D == 128), "tile shape");
   // one LDS array: K0 | V0 | K1 | V1; every read offset is a compile-time immediate
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
@@ -425,10 +429,6 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     f32x16_t sa0, sb0, sa1, sb1;
     qk(std::integral_constant<int, 0>{}, sa0, sb0, [](auto) {});
     if (t0.edge()) mask(t0, sa0, sb0);
-    float mxc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mxc = fmaxf(fmaxf(mxc, sa0[i]), sb0[i]);
-    mxc = partner_max(mxc);
 
     auto iter = [&](auto buf_tag, auto next_tag, int j, f32x16_t& ca, f32x16_t& cb, f32x16_t& na,
                     f32x16_t& nb) {
@@ -441,17 +441,16 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         dma_v(std::integral_constant<int, 1 - P>{}, tA.kstart());
       }
 
-      // running max: move it only when it grows by more than 2^8
-      const float m_new = fmaxf(m_run, mxc * c2);
-      const bool need = m_new > m_run + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        if (need) m_run = m_new;
-        l_run *= alpha;
+      // Reference point of the exponentials.  A row that has not met a visible key
+      // yet (m_run = -inf) takes the max of this tile; every other row keeps its
+      // reference, and the overflow check after the exponentials restores the
+      // exact max when a tile's scores outgrow it by more than 2^64.
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, ca[i]), cb[i]);
+        mx = partner_max(mx);
+        if (m_run == -INFINITY) m_run = mx * c2;
       }
       const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
 
@@ -482,6 +481,33 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       } else {
         static_for<QSLOTS>(exp_hook);
       }
+      if (__builtin_amdgcn_ballot_w64(!(ps <= kOverflow))) {
+        // rare: some probability above 2^64 -- move the reference to the row max
+        // of this tile, rescale what is accumulated, and redo the tile
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, ca[i]), cb[i]);
+        mx = partner_max(mx);
+        const float m_new = fmaxf(m_run, mx * c2);
+        const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+        const float ms2 = (m_run == -INFINITY) ? 0.0f : m_run;
+        ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(e < 16 ? ca[e] : cb[e - 16], c2, -ms2));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(e + 1 < 16 ? ca[e + 1] : cb[e + 1 - 16], c2, -ms2));
+          ps += p0 + p1;
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
+          pu[e >> 1] = __builtin_bit_cast(uint32_t, pr);
+        }
+      }
       l_run += ps;
       bf16x8_t pf[4];
 #pragma unroll
@@ -491,21 +517,10 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         pf[t] = __builtin_bit_cast(bf16x8_t, w);
       }
 
-      // O += P_j V_j, interleaved with the mask and max of tile j+1
-      float mxn = -INFINITY;
+      // O += P_j V_j (the edge mask of tile j+1 goes first)
       if constexpr (NEXT) {
         if (tA.edge()) mask(tA, na, nb);
-        pv(std::integral_constant<int, P>{}, pf, [&](auto slot_tag) {
-          constexpr int sl = decltype(slot_tag)::value;
-#pragma unroll
-          for (int e = sl * EPP; e < (sl + 1) * EPP; e += 2) {
-            const float x0 = e < 16 ? na[e] : nb[e - 16];
-            const float x1 = e + 1 < 16 ? na[e + 1] : nb[e + 1 - 16];
-            mxn = fmaxf(fmaxf(mxn, x0), x1);
-          }
-          fence(mxn);
-        });
-        mxc = partner_max(mxn);
+        pv(std::integral_constant<int, P>{}, pf, [](auto) {});
         tA = tB;
         tile_next(tB, rp, n_runs);
       } else {

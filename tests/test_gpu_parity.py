@@ -149,6 +149,54 @@ def test_q_zero_closed_form_hetero(gpu_lib):
     assert np.abs(l[fin] - ref[fin, None]).max() < 2e-5
 
 
+# ---------------------------------------------------------------- reference point of the exponentials
+
+@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (64, True)])
+def test_scores_growing_across_tiles(gpu_lib, d, causal):
+    # Scores rise by ~8 (log2 units) per 64-key tile, so later tiles outgrow the
+    # reference point taken from the first tile by far more than 2^64: the exact
+    # rescale path must run several times per row and still match the oracle.
+    T = 1536
+    p = W.make_problem(f"growing{d}", T, T, 4, 1, d, [((0, T), (0, T), W.CAUSAL if causal else W.FULL)], seed=11)
+    g = torch.Generator().manual_seed(11)
+    q = (1.0 + 0.1 * torch.randn(T, 4, d, generator=g)).to(torch.bfloat16)
+    tile = (torch.arange(T) // 64).float()
+    c = 0.5 * tile * math.sqrt(128 / d)
+    k = (c[:, None, None] + 0.2 * torch.randn(T, 1, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(T, 1, d, generator=g).to(torch.bfloat16)
+    out, lse = run(gpu_lib, p, q, k, v)
+    rows = np.unique(np.concatenate([np.arange(0, T, 37), [T - 1]]))
+    ro, rl = oracle_ref(p, q, k, v, rows=rows)
+    assert np.isfinite(rl).all() and rl.max() > 100.0  # the scores really span > 2^64 relative
+    compare(out, lse, ro, rl, rows=rows, what=f"growing scores D={d} causal={causal}")
+
+
+def test_scores_falling_across_tiles(gpu_lib):
+    # the first tile holds the largest scores: later probabilities underflow to 0
+    T = 1024
+    p = W.make_problem("falling", T, T, 4, 2, 128, [((0, T), (0, T), W.FULL)], seed=12)
+    g = torch.Generator().manual_seed(12)
+    q = (1.0 + 0.1 * torch.randn(T, 4, 128, generator=g)).to(torch.bfloat16)
+    c = 6.0 - 0.5 * (torch.arange(T) // 64).float()
+    k = (c[:, None, None] + 0.2 * torch.randn(T, 2, 128, generator=g)).to(torch.bfloat16)
+    v = torch.randn(T, 2, 128, generator=g).to(torch.bfloat16)
+    out, lse = run(gpu_lib, p, q, k, v)
+    rows = np.arange(0, T, 29)
+    compare(out, lse, *oracle_ref(p, q, k, v, rows=rows), rows=rows, what="falling scores")
+
+
+def test_rows_without_keys_in_first_run(gpu_lib):
+    # Rows 32..47 of the second row block see nothing of the causal slice (its
+    # k_range is shorter than its q_range) and meet their first key only in the
+    # FULL slice that follows, so their reference point is set mid-item while the
+    # other rows of the same wavefront already have one.
+    p = W.make_problem("late_first_key", 128, 400, 4, 1, 128,
+                       [((0, 128), (0, 80), W.CAUSAL), ((0, 128), (80, 400), W.FULL)], seed=13)
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v)
+    compare(out, lse, *oracle_ref(p, q, k, v), what="late first key")
+
+
 # ---------------------------------------------------------------- properties
 
 def test_bitwise_deterministic(gpu_lib):
