@@ -362,7 +362,6 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   // of step t+1 are in flight during the MFMAs of step t); hook(slot) as above
   auto pv = [&](auto buf_tag, const bf16x8_t (&pf)[4], auto&& hook) {
     constexpr int OV = kOffV[decltype(buf_tag)::value];
-    __builtin_amdgcn_s_setprio(1);
     s16x4_t vlo[2][DBLK], vhi[2][DBLK];
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
@@ -391,7 +390,6 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         hook(std::integral_constant<int, t * DBLK + d>{});
       });
     });
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // edge mask of a tile's scores: key j (absolute) visible iff j < min(k_hi, row + edge_base)
