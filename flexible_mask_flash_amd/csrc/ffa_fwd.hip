@@ -53,6 +53,7 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 namespace {
 
 using ffa::kBlockN;
+using ffa::kItemRec;
 using ffa::kRec;
 using ffa::kSlotsPerItem;
 
@@ -222,12 +223,21 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   constexpr int kOffK[2] = {0, 2 * TILE};
   constexpr int kOffV[2] = {TILE, 3 * TILE};
 
+  // The first tile waits on a chain of dependent loads: arguments -> item record
+  // -> Q and the first K/V tile.  Each fence below makes its whole group of
+  // scalar loads issue together (the compiler would otherwise sink every load
+  // next to its first use, one more round trip each).
+  asm volatile("" ::"s"(a.items), "s"(a.runs), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.q_sb), "s"(a.q_st),
+               "s"(a.q_sh), "s"(a.k_sb), "s"(a.k_st), "s"(a.k_sh), "s"(a.v_sb), "s"(a.v_st), "s"(a.v_sh),
+               "s"(a.total_k), "s"(a.batch), "s"(a.heads_per_item), "s"(a.kv_ratio), "s"(a.ws_slots));
   const int bid = blockIdx.x;
   const int item_idx = bid / a.batch;
   const int b = bid - item_idx * a.batch;
-  const FFA_CONST int32_t* itp = (const FFA_CONST int32_t*)(a.items + (int64_t)item_idx * kRec);
+  const FFA_CONST int32_t* itp = (const FFA_CONST int32_t*)(a.items + (int64_t)item_idx * kItemRec);
   const int q0 = itp[0], nrows = itp[1], h0 = itp[2], run_off = itp[3], n_runs = itp[4];
   const int slot = itp[5], total_tiles = itp[6];
+  asm volatile("" ::"s"(q0), "s"(nrows), "s"(h0), "s"(run_off), "s"(n_runs), "s"(slot), "s"(total_tiles),
+               "s"(itp[8]), "s"(itp[9]), "s"(itp[10]), "s"(itp[11]), "s"(itp[12]));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     // tile j+1 are masked and max-reduced.  K is one tile ahead of V:
     // LDS holds K_{j+1}, V_j, and receives K_{j+2}, V_{j+1} during iteration j.
     TileIt t0;
-    tile_first(t0, rp);
+    tile_first(t0, itp + 8);  // the inline copy of runs[run_off]
     dma_k(std::integral_constant<int, 0>{}, t0.kstart());
     dma_v(std::integral_constant<int, 0>{}, t0.kstart());
     TileIt tA = t0, tB;   // tA: tile j+1, tB: tile j+2
@@ -782,7 +792,7 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   const int32_t* meta = static_cast<const int32_t*>(d_meta);
   FwdArgs fa;
   fa.items = meta + ffa::kHdr;
-  fa.runs = fa.items + (size_t)p.num_items * kRec;
+  fa.runs = fa.items + (size_t)p.num_items * kItemRec;
   fa.q = static_cast<const __bf16*>(q);
   fa.k = static_cast<const __bf16*>(k);
   fa.v = static_cast<const __bf16*>(v);

@@ -4,14 +4,17 @@
 // once per mask and read by the kernels:
 //
 //   header  [16]             magic, version, counts, tile shape (see kHdr*)
-//   items   [num_items][8]   one main-kernel workgroup each (per batch element)
+//   items   [num_items][16]  one main-kernel workgroup each (per batch element)
 //   runs    [num_runs][8]    a contiguous range of key tiles of one slice
 //   combine [num_combine][8] one split row block to merge
 //
-// Item:    q0, nrows, h0, run_off, n_runs, slot (-1: final output), tiles, 0
+// Item:    q0, nrows, h0, run_off, n_runs, slot (-1: final output), tiles, 0,
+//          then a copy of its first run record (zeros when n_runs == 0)
 //          rows [q0, q0 + nrows) and query heads [h0, h0 + heads_per_item)
 //          share one kv head; the item walks runs[run_off .. run_off + n_runs)
-//          in order; `tiles` is the total key-tile count of those runs.
+//          in order; `tiles` is the total key-tile count of those runs.  The
+//          inline first run lets a workgroup issue its first K/V loads as soon
+//          as its one item record has arrived (no second dependent load).
 // Run:     k0, n_tiles, n_full, k_hi, edge_base, 0, 0, 0
 //          key tile t covers [k0 + t*BN, k0 + (t+1)*BN); row i sees key j iff
 //          j < min(k_hi, i + edge_base) (edge_base = ke - qe + 1 for a causal
@@ -38,7 +41,8 @@ constexpr int32_t kWaveRows = 32;       // query rows per wavefront (one 32x32 M
 constexpr int32_t kWaves = 4;           // wavefronts per workgroup (two workgroups per CU)
 constexpr int32_t kSlotsPerItem = kWaveRows * kWaves;  // (row, head) pairs one workgroup covers
 constexpr int32_t kNoEdge = 0x3fffffff; // edge_base of a full slice: never limits
-constexpr int kRec = 8;                 // int32 per record
+constexpr int kRec = 8;                 // int32 per run / combine record
+constexpr int kItemRec = 16;            // int32 per item record (item fields + first run)
 constexpr int kHdr = 16;                // int32 in the header
 
 enum HeaderField {
@@ -56,7 +60,7 @@ struct Plan {
   int64_t meta_bytes() const { return (int64_t)meta.size() * 4; }
   int64_t workspace_bytes() const { return (int64_t)num_slots * (head_dim + 1) * 4; }
   const int32_t* items() const { return meta.data() + kHdr; }
-  const int32_t* runs() const { return items() + (size_t)num_items * kRec; }
+  const int32_t* runs() const { return items() + (size_t)num_items * kItemRec; }
   const int32_t* combine() const { return runs() + (size_t)num_runs * kRec; }
 };
 

@@ -284,7 +284,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
     });
   }
 
-  if (items.size() > (size_t)INT32_MAX / kRec || runs.size() > (size_t)INT32_MAX)
+  if (items.size() > (size_t)INT32_MAX / kItemRec || runs.size() > (size_t)INT32_MAX)
     return set_error(FFA_ERR_ARG, "plan too large");
 
   Plan p;
@@ -308,7 +308,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   p.max_item_tiles = max_item;
 
   try {
-    p.meta.assign(kHdr + items.size() * kRec + runs.size() + combine.size(), 0);
+    p.meta.assign(kHdr + items.size() * kItemRec + runs.size() + combine.size(), 0);
   } catch (...) {
     return set_error(FFA_ERR_HOST_OOM, "host allocation of the plan failed");
   }
@@ -329,9 +329,10 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   h[kHdrSlots] = n_slots;
   int32_t* w = h + kHdr;
   for (const ItemRec& it : items) {
-    const int32_t rec[kRec] = {it.q0, it.nrows, it.h0, it.run_off, it.n_runs, it.slot, it.tiles, 0};
+    int32_t rec[kItemRec] = {it.q0, it.nrows, it.h0, it.run_off, it.n_runs, it.slot, it.tiles, 0};
+    if (it.n_runs > 0) std::memcpy(rec + 8, runs.data() + (size_t)it.run_off * kRec, kRec * 4);
     std::memcpy(w, rec, sizeof(rec));
-    w += kRec;
+    w += kItemRec;
   }
   if (!runs.empty()) std::memcpy(w, runs.data(), runs.size() * 4);
   w += runs.size();

@@ -124,7 +124,8 @@ ffa_status ffa_plan_info_get(ffa_plan_t plan, ffa_plan_info* info);
 ffa_status ffa_plan_upload(ffa_plan_t plan, void* d_meta, size_t meta_bytes, void* stream);
 
 /* Copy the same metadata to host memory h_meta (>= info.meta_bytes bytes).
- * Layout: int32 header[16], then items[num_items][8], runs[num_runs][8],
+ * Layout: int32 header[16], then items[num_items][16] (8 item fields followed
+ * by a copy of the item's first run), runs[num_runs][8],
  * combine[num_combine][8]; see the planner source for the field order. */
 ffa_status ffa_plan_export(ffa_plan_t plan, void* h_meta, size_t meta_bytes);
 

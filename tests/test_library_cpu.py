@@ -24,7 +24,7 @@ HEADER = os.path.join(ROOT, "include", "ffa.h")
 
 ffa = pytest.importorskip("flexible_mask_flash_amd")
 
-HDR, REC = 16, 8
+HDR, REC, IREC = 16, 8, 16
 NCU = 256
 
 
@@ -99,10 +99,16 @@ def parse(meta):
     h = meta[:HDR]
     assert h[0] == 0x46464131
     n_items, n_runs, n_comb, G, rows, bn = h[2], h[3], h[4], h[5], h[6], h[7]
-    items = meta[HDR:HDR + n_items * REC].reshape(n_items, REC)
-    runs = meta[HDR + n_items * REC:HDR + (n_items + n_runs) * REC].reshape(n_runs, REC)
-    comb = meta[HDR + (n_items + n_runs) * REC:HDR + (n_items + n_runs + n_comb) * REC].reshape(n_comb, REC)
-    return dict(G=G, rows=rows, bn=bn, items=items, runs=runs, comb=comb, hdr=h)
+    items = meta[HDR:HDR + n_items * IREC].reshape(n_items, IREC)
+    r0 = HDR + n_items * IREC
+    runs = meta[r0:r0 + n_runs * REC].reshape(n_runs, REC)
+    comb = meta[r0 + n_runs * REC:r0 + (n_runs + n_comb) * REC].reshape(n_comb, REC)
+    # every item carries a copy of its first run record (zeros when it has none)
+    has = items[:, 4] > 0
+    assert (items[~has, 8:] == 0).all()
+    if has.any():
+        assert (items[has, 8:] == runs[items[has, 3]]).all(), "inline first run differs from runs[run_off]"
+    return dict(G=G, rows=rows, bn=bn, items=items[:, :8], runs=runs, comb=comb, hdr=h)
 
 
 def rasterise(p, plan):
@@ -206,7 +212,7 @@ def test_plan_meta_layout_and_order():
     plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
                     p.head_dim, num_cus=NCU)
     i = plan.info
-    assert i["meta_bytes"] == 4 * (HDR + REC * (i["num_items"] + i["num_runs"] + i["num_combine"]))
+    assert i["meta_bytes"] == 4 * (HDR + IREC * i["num_items"] + REC * (i["num_runs"] + i["num_combine"]))
     m = parse(plan.meta_host())
     assert m["G"] == 4 and m["rows"] == 32 and m["bn"] == 64
     cost = m["items"][:, 6] + 2 * (m["items"][:, 4] > 0)
