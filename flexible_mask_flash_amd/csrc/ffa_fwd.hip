@@ -619,15 +619,40 @@ __global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
   const int dq = (t % TPP) * 4;
   for (int p = t / TPP; p < npairs; p += PPP) {
     const int64_t base = (int64_t)b * a.ws_slots + slot0 + p;
+    const float* lsep = a.ws_lse + base;
+    const float* op = a.ws_o + base * D + dq;
+    // chunks in groups of four: the loads of a group are independent, so four
+    // are in flight at a time instead of one dependent load per chunk
     float mx = -INFINITY;
-    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.ws_lse[base + (int64_t)c * kSlotsPerItem]);
+    int c = 0;
+    for (; c + 4 <= nch; c += 4) {
+      const float l0 = lsep[(int64_t)c * kSlotsPerItem], l1 = lsep[(int64_t)(c + 1) * kSlotsPerItem];
+      const float l2 = lsep[(int64_t)(c + 2) * kSlotsPerItem], l3 = lsep[(int64_t)(c + 3) * kSlotsPerItem];
+      mx = fmaxf(fmaxf(mx, fmaxf(l0, l1)), fmaxf(l2, l3));
+    }
+    for (; c < nch; ++c) mx = fmaxf(mx, lsep[(int64_t)c * kSlotsPerItem]);
     const float msafe = mx == -INFINITY ? 0.0f : mx;
     float den = 0.0f;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < nch; ++c) {
-      const int64_t s = base + (int64_t)c * kSlotsPerItem;
-      const float w = __expf(a.ws_lse[s] - msafe);
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.ws_o + s * D + dq);
+    c = 0;
+    for (; c + 4 <= nch; c += 4) {
+      f32x4_t x[4];
+      float l[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        l[u] = lsep[(int64_t)(c + u) * kSlotsPerItem];
+        x[u] = *reinterpret_cast<const f32x4_t*>(op + (int64_t)(c + u) * kSlotsPerItem * D);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __expf(l[u] - msafe);
+        den += w;
+        acc += w * x[u];
+      }
+    }
+    for (; c < nch; ++c) {
+      const float w = __expf(lsep[(int64_t)c * kSlotsPerItem] - msafe);
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(op + (int64_t)c * kSlotsPerItem * D);
       den += w;
       acc += w * x;
     }

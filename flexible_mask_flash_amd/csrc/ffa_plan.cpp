@@ -18,14 +18,19 @@
 //  4. split-K: long items are cut into chunks of key tiles that write float32
 //     partial (out, lse); the combine kernel merges them with a global
 //     logsumexp (FlagAttention user guide, "Split-KV and paged attention").
-//     The automatic rule splits only when an item is longer than a fair share
-//     of the device (few items or very long rows), as FlagAttention picks its
-//     split-KV path by occupancy.
+//     The automatic rule picks the split by occupancy, as FlagAttention picks
+//     its split-KV path: it estimates the time of the plan without a split and
+//     with chunks of 1/2, 1 and 2 fair shares (dispatch makespan of the items
+//     in longest-first order on the resident workgroup slots, plus the combine
+//     pass for a split) and keeps the cheapest.  The constants are measured on
+//     MI355X (per-tile and per-item time of the main kernel, combine launch and
+//     HBM rate).
 //  5. order: longest items first, so the hardware dispatcher fills the device
 //     with long work and ends on short work.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <numeric>
 #include <string>
 #include <vector>
@@ -68,8 +73,28 @@ struct QTile {
 };
 
 constexpr int32_t kMinChunkTiles = 16;   // never split below 1024 keys per chunk
-constexpr int32_t kItemOverhead = 2;     // prologue / epilogue cost of an item, in tiles
+constexpr int32_t kItemOverhead = 3;     // prologue / epilogue cost of an item, in tiles (measured)
 constexpr int32_t kResidentPerCu = 2;    // main-kernel workgroups resident per CU
+// Split cost model (measured on MI355X, D = 128; D = 64 tiles take about 0.6x):
+constexpr double kTileUs128 = 1.8;         // one key tile of one item, per resident slot
+constexpr double kCombineFixedUs = 6.0;    // combine launch and its own tail
+constexpr double kCombineBytesPerUs = 4.0e6;  // effective HBM rate of partial writes + combine (4 TB/s)
+constexpr double kSplitImbalance = 1.1;    // only consider a split when the makespan exceeds the mean by 10%
+
+// Longest-first greedy makespan of item costs on `slots` identical slots (what
+// the hardware dispatcher does with an item list in longest-first order).
+double lpt_makespan(std::vector<int64_t>& costs, int64_t slots) {
+  if (costs.empty()) return 0.0;
+  std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
+  if ((int64_t)costs.size() <= slots) return (double)costs.front();
+  std::vector<int64_t> heap(slots, 0);  // min-heap of slot loads
+  for (int64_t c : costs) {
+    std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+    heap.back() += c;
+    std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+  }
+  return (double)*std::max_element(heap.begin(), heap.end());
+}
 constexpr int64_t kMaxTokens = (int64_t)1 << 30;
 
 }  // namespace
@@ -201,19 +226,49 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   }
 
   // ---------------------------------------------------------------- split-K decision
-  int64_t total_cost = 0, max_tiles = 0;
-  for (const QTile& t : tiles) {
-    total_cost += (t.tiles + (t.runs.empty() ? 0 : kItemOverhead)) * n_groups;
-    max_tiles = std::max(max_tiles, t.tiles);
-  }
+  // number of chunks of a q tile for a chunk target (0: no split)
+  auto n_chunks_of = [&](int64_t tiles, int64_t target) -> int64_t {
+    if (target <= 0 || tiles <= target) return 1;
+    return std::min<int64_t>({(int64_t)max_splits, (tiles + target - 1) / target, tiles});
+  };
   int64_t chunk_target = 0;  // 0: no split
   if (split_tiles > 0) {
     chunk_target = split_tiles;
   } else if (split_tiles == 0) {
     const int64_t slots = (int64_t)num_cus * kResidentPerCu;
-    const int64_t fair = (total_cost + slots - 1) / slots;
-    const int64_t target = std::max<int64_t>(kMinChunkTiles, fair);
-    if (max_tiles > target) chunk_target = target;
+    const double tile_us = head_dim == 128 ? kTileUs128 : 0.6 * kTileUs128;
+    // estimated time (us) of the plan for a chunk target
+    auto estimate = [&](int64_t target) -> double {
+      std::vector<int64_t> costs;
+      double comb_bytes = 0.0;
+      for (const QTile& t : tiles) {
+        const int64_t n = n_chunks_of(t.tiles, target);
+        for (int64_t c = 0; c < n; ++c) {
+          const int64_t ct = (c + 1) * t.tiles / n - c * t.tiles / n;
+          const int64_t cost = ct + (t.runs.empty() ? 1 : kItemOverhead);
+          for (int32_t g = 0; g < n_groups; ++g) costs.push_back(cost);
+        }
+        if (n > 1)  // partials written and read back, out written by the combine
+          comb_bytes += (double)n_groups * t.nrows * G * ((2.0 * n) * (4.0 * head_dim + 4.0) + 2.0 * head_dim + 4.0);
+      }
+      const double t_main = lpt_makespan(costs, slots) * tile_us;
+      return comb_bytes > 0.0 ? t_main + kCombineFixedUs + comb_bytes / kCombineBytesPerUs : t_main;
+    };
+    int64_t total_cost = 0;
+    for (const QTile& t : tiles) total_cost += (t.tiles + (t.runs.empty() ? 1 : kItemOverhead)) * n_groups;
+    const double mean = (double)total_cost / (double)slots;
+    double best = estimate(0);
+    if (best > kSplitImbalance * mean * (head_dim == 128 ? kTileUs128 : 0.6 * kTileUs128)) {
+      const int64_t fair = std::max<int64_t>(1, (int64_t)std::ceil(mean));
+      for (int64_t target : {fair / 2, fair, 2 * fair}) {
+        const int64_t tgt = std::max<int64_t>(kMinChunkTiles, target);
+        const double e = estimate(tgt);
+        if (e < best) {
+          best = e;
+          chunk_target = tgt;
+        }
+      }
+    }
   }
 
   // ---------------------------------------------------------------- emit
@@ -233,10 +288,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   for (const QTile& t : tiles) {
     computed += (int64_t)rows_per_item * t.tiles * kBlockN;
     all_tiles += t.tiles * n_groups;
-    int64_t n_chunks = 1;
-    if (chunk_target > 0 && t.tiles > chunk_target) {
-      n_chunks = std::min<int64_t>({(int64_t)max_splits, (t.tiles + chunk_target - 1) / chunk_target, t.tiles});
-    }
+    const int64_t n_chunks = n_chunks_of(t.tiles, chunk_target);
     if (n_chunks <= 1) {
       const int32_t off = (int32_t)(runs.size() / kRec);
       for (const TileRun& r : t.runs) push_run(r.k0, r.n_tiles, r.n_full, r.k_hi, r.edge_base);
@@ -279,7 +331,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
 
   if (!(flags & 1u)) {
     std::stable_sort(items.begin(), items.end(), [](const ItemRec& x, const ItemRec& y) {
-      const int32_t cx = x.tiles + (x.n_runs ? kItemOverhead : 0), cy = y.tiles + (y.n_runs ? kItemOverhead : 0);
+      const int32_t cx = x.tiles + (x.n_runs ? kItemOverhead : 1), cy = y.tiles + (y.n_runs ? kItemOverhead : 1);
       return cx > cy;
     });
   }
