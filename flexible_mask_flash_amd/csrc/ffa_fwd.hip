@@ -12,7 +12,8 @@
 //   * O^T += V^T P^T with the same MFMA: P^T comes straight from the S^T
 //     registers (bf16), V^T from LDS with ds_read_b64_tr_b16 (4 keys of one
 //     head-dim column per lane, two reads per MFMA operand).
-//   * online softmax in fp32, base 2 (scale * log2 e folded into one FMA).  A
+//   * online softmax in fp32, base 2 (scale * log2 e folded into one FMA, done
+//     for tile j+1 between the P V MFMAs of tile j).  A
 //     row's reference point is the max of the first tile where it sees a key;
 //     later tiles are exponentiated against it without a per-tile max, and
 //     only when a probability would exceed 2^64 does the wave take the max,
@@ -438,6 +439,33 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     qk(std::integral_constant<int, 0>{}, sa0, sb0, [](auto) {});
     if (t0.edge()) mask(t0, sa0, sb0);
 
+    // Reference point and exponent arguments of a tile, computed in place
+    // (x = s * c2 - m) one tile ahead of its exponentials.  A row that has not
+    // met a visible key yet (m_run = -inf) takes the max of this tile; every
+    // other row keeps its reference, and the overflow check after the
+    // exponentials restores the exact max when a tile's scores outgrow it by
+    // more than 2^64.  msub_next is the reference the arguments were taken with.
+    float msub_next = 0.0f;
+    auto reference = [&](f32x16_t& xa, f32x16_t& xb) {
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, xa[i]), xb[i]);
+        mx = partner_max(mx);
+        if (m_run == -INFINITY) m_run = mx * c2;
+      }
+      msub_next = (m_run == -INFINITY) ? 0.0f : m_run;
+    };
+    auto prep = [&](f32x16_t& xa, f32x16_t& xb, int e0, int e1) {
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        if (e < 16) xa[e] = __builtin_fmaf(xa[e], c2, -msub_next);
+        else xb[e - 16] = __builtin_fmaf(xb[e - 16], c2, -msub_next);
+      }
+    };
+    reference(sa0, sb0);
+    prep(sa0, sb0, 0, 32);
+
     auto iter = [&](auto buf_tag, auto next_tag, int j, f32x16_t& ca, f32x16_t& cb, f32x16_t& na,
                     f32x16_t& nb) {
       constexpr int P = decltype(buf_tag)::value;  // V_j in V buffer P, K_{j+1} in K buffer 1-P
@@ -449,23 +477,13 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         dma_v(std::integral_constant<int, 1 - P>{}, tA.kstart());
       }
 
-      // Reference point of the exponentials.  A row that has not met a visible key
-      // yet (m_run = -inf) takes the max of this tile; every other row keeps its
-      // reference, and the overflow check after the exponentials restores the
-      // exact max when a tile's scores outgrow it by more than 2^64.
-      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, ca[i]), cb[i]);
-        mx = partner_max(mx);
-        if (m_run == -INFINITY) m_run = mx * c2;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+      const float msub = msub_next;  // reference of tile j's arguments
 
-      // P_j = exp2(S_j * c2 - m), interleaved with K Q^T of tile j+1.  Each hook
-      // packs its probabilities into bf16 pairs and pins them (and the running
-      // sum) with fence(), so the work stays between the MFMAs it is meant to
-      // overlap instead of sinking to its use in P V.
+      // P_j = exp2(x_j), interleaved with K Q^T of tile j+1 (the arguments x_j were
+      // prepared during the previous P V).  Each hook packs its probabilities into
+      // bf16 pairs and pins them (and the running sum) with fence(), so the work
+      // stays between the MFMAs it is meant to overlap instead of sinking to its
+      // use in P V.
       uint32_t pu[16];  // bf16 pairs of P_j, pair q = elements 2q, 2q+1
       float ps = 0.0f;
       auto exp_hook = [&](auto slot_tag) {
@@ -474,8 +492,8 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         for (int e = sl * EPQ; e < (sl + 1) * EPQ; e += 2) {
           const float s0v = e < 16 ? ca[e] : cb[e - 16];
           const float s1v = e + 1 < 16 ? ca[e + 1] : cb[e + 1 - 16];
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0v, c2, -msub));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1v, c2, -msub));
+          const float p0 = __builtin_amdgcn_exp2f(s0v);
+          const float p1 = __builtin_amdgcn_exp2f(s1v);
           ps += p0 + p1;
           typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
           const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
@@ -491,12 +509,13 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       }
       if (__builtin_amdgcn_ballot_w64(!(ps <= kOverflow))) {
         // rare: some probability above 2^64 -- move the reference to the row max
-        // of this tile, rescale what is accumulated, and redo the tile
+        // of this tile, rescale what is accumulated, and redo the tile (the
+        // arguments hold s * c2 - msub)
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, ca[i]), cb[i]);
         mx = partner_max(mx);
-        const float m_new = fmaxf(m_run, mx * c2);
+        const float m_new = fmaxf(m_run, mx + msub);
         const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         m_run = m_new;
         l_run *= alpha;
@@ -504,12 +523,12 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         for (int d = 0; d < DBLK; ++d)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-        const float ms2 = (m_run == -INFINITY) ? 0.0f : m_run;
+        const float shift = (m_run == -INFINITY) ? 0.0f : m_run - msub;
         ps = 0.0f;
 #pragma unroll
         for (int e = 0; e < 32; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(e < 16 ? ca[e] : cb[e - 16], c2, -ms2));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(e + 1 < 16 ? ca[e + 1] : cb[e + 1 - 16], c2, -ms2));
+          const float p0 = __builtin_amdgcn_exp2f((e < 16 ? ca[e] : cb[e - 16]) - shift);
+          const float p1 = __builtin_amdgcn_exp2f((e + 1 < 16 ? ca[e + 1] : cb[e + 1 - 16]) - shift);
           ps += p0 + p1;
           typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
           const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
@@ -525,10 +544,19 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         pf[t] = __builtin_bit_cast(bf16x8_t, w);
       }
 
-      // O += P_j V_j (the edge mask of tile j+1 goes first)
+      // O += P_j V_j; the edge mask and reference point of tile j+1 go first, its
+      // exponent arguments are prepared between the MFMAs (this keeps the FMAs
+      // out of the K Q^T section, where the exponentials already take the VALU)
       if constexpr (NEXT) {
         if (tA.edge()) mask(tA, na, nb);
-        pv(std::integral_constant<int, P>{}, pf, [](auto) {});
+        reference(na, nb);
+        pv(std::integral_constant<int, P>{}, pf, [&](auto slot_tag) {
+          constexpr int sl = decltype(slot_tag)::value;
+          constexpr int EPP = 32 / (4 * DBLK);
+          prep(na, nb, sl * EPP, (sl + 1) * EPP);
+          fence(na);
+          fence(nb);
+        });
         tA = tB;
         tile_next(tB, rp, n_runs);
       } else {
