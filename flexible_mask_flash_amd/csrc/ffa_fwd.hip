@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   // next to its first use, one more round trip each).
   asm volatile("" ::"s"(a.items), "s"(a.runs), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.q_sb), "s"(a.q_st),
                "s"(a.q_sh), "s"(a.k_sb), "s"(a.k_st), "s"(a.k_sh), "s"(a.v_sb), "s"(a.v_st), "s"(a.v_sh),
-               "s"(a.total_k), "s"(a.batch), "s"(a.heads_per_item), "s"(a.kv_ratio), "s"(a.ws_slots));
+               "s"(a.total_k), "s"(a.batch), "s"(a.heads_per_item), "s"(a.kv_ratio));
   const int bid = blockIdx.x;
   const int item_idx = bid / a.batch;
   const int b = bid - item_idx * a.batch;
@@ -312,10 +312,16 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     if (kstart + BN <= a.total_k) {
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kstart * st_b), (short)0, 0x7fffffff, kBufferFlags);
+      // LDS destinations and row offsets are recomputed here with scalar adds;
+      // hoisted out of the tile loop they would be 2 x NLD long-lived scalars
+      // per tensor and buffer, spilled to VGPR lanes and read back by the VALU.
+      uint32_t ldst = (uint32_t)(uintptr_t)(FFA_LDS char*)dst + wave * 1024;
+      int32_t rstep = (int32_t)(RPL * st_b);
+      asm volatile("" : "+s"(ldst), "+s"(rstep));
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(dst + (i * W + wave) * 1024), 16, goff,
-                                                 (int)(i * RPL * st_b), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(uintptr_t)(ldst + i * W * 1024), 16, goff,
+                                                 i * rstep, 0, 0);
     } else {
       // last tile of the key axis: rows past total_k re-read the last row (they are masked)
 #pragma unroll
@@ -580,6 +586,11 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   }
 
   // ---- epilogue
+  // The output pointers and strides are read again from the argument segment
+  // through a pointer the compiler cannot see through, so that they are not
+  // held in scalar registers (or spilled) across the tile loop.
+  const FFA_CONST FwdArgs* ea = (const FFA_CONST FwdArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ea));
   const float lsum = partner_sum(l_run);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   const float lse_v = lsum > 0.0f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
@@ -603,7 +614,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           *reinterpret_cast<bf16x4_t*>(st + q * ROWB + ((c ^ swz_k<D>(q)) << 4) + hh * 8) = w;
         }
     }
-    __bf16* ob = a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+    __bf16* ob = ea->out + (int64_t)b * ea->o_sb + (int64_t)h * ea->o_sh;
     const int r0 = q0 + rsub * 32;
     const int nvalid = min(32, nrows - rsub * 32);
 #pragma unroll
@@ -611,12 +622,12 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       const int lin = i * 64 + lane;
       const int r = lin / CH, c = lin % CH;
       const f32x4_t val = *reinterpret_cast<const f32x4_t*>(st + r * ROWB + ((c ^ swz_k<D>(r)) << 4));
-      if (r < nvalid) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * a.o_st + c * 8) = val;
+      if (r < nvalid) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * ea->o_st + c * 8) = val;
     }
-    if (row_ok && hh == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)h * a.l_sh] = lse_v;
+    if (row_ok && hh == 0) ea->lse[(int64_t)b * ea->l_sb + (int64_t)row * ea->l_st + (int64_t)h * ea->l_sh] = lse_v;
   } else if (row_ok) {
-    const int64_t sidx = (int64_t)b * a.ws_slots + slot + lrow * G + g;
-    float* op = a.ws_o + sidx * D;
+    const int64_t sidx = (int64_t)b * ea->ws_slots + slot + lrow * G + g;
+    float* op = ea->ws_o + sidx * D;
 #pragma unroll
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
@@ -626,7 +637,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         for (int e = 0; e < 4; ++e) w[e] = o[d][4 * gq + e] * inv;
         *reinterpret_cast<f32x4_t*>(op + 32 * d + 8 * gq + 4 * hh) = w;
       }
-    if (hh == 0) a.ws_lse[sidx] = lse_v;
+    if (hh == 0) ea->ws_lse[sidx] = lse_v;
   }
 }
 
