@@ -595,6 +595,13 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   const float lse_v = lsum > 0.0f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
   if (slot < 0) {
+    // all the output arguments in one round trip (each use would otherwise
+    // reload its own field right before its store)
+    __bf16* const out_p = ea->out;
+    float* const lse_p = ea->lse;
+    const int64_t o_sb = ea->o_sb, o_st = ea->o_st, o_sh = ea->o_sh;
+    const int64_t l_sb = ea->l_sb, l_st = ea->l_st, l_sh = ea->l_sh;
+    asm volatile("" ::"s"(out_p), "s"(lse_p), "s"(o_sb), "s"(o_st), "s"(o_sh), "s"(l_sb), "s"(l_st), "s"(l_sh));
     // Stage the bf16 tile of this wave (32 rows x D) in LDS, then write whole
     // rows with 16-byte stores: in the MFMA layout a lane holds 4 consecutive
     // values of each of 16 head-dim groups, which would otherwise become 8-byte
@@ -614,17 +621,24 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           *reinterpret_cast<bf16x4_t*>(st + q * ROWB + ((c ^ swz_k<D>(q)) << 4) + hh * 8) = w;
         }
     }
-    __bf16* ob = ea->out + (int64_t)b * ea->o_sb + (int64_t)h * ea->o_sh;
+    __bf16* ob = out_p + (int64_t)b * o_sb + (int64_t)h * o_sh;
     const int r0 = q0 + rsub * 32;
     const int nvalid = min(32, nrows - rsub * 32);
+    constexpr int NST = 32 * CH / 64;  // 16-byte chunks per lane
+    f32x4_t val[NST];
 #pragma unroll
-    for (int i = 0; i < 32 * CH / 64; ++i) {
+    for (int i = 0; i < NST; ++i) {  // every read issued before the first store
       const int lin = i * 64 + lane;
       const int r = lin / CH, c = lin % CH;
-      const f32x4_t val = *reinterpret_cast<const f32x4_t*>(st + r * ROWB + ((c ^ swz_k<D>(r)) << 4));
-      if (r < nvalid) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * ea->o_st + c * 8) = val;
+      val[i] = *reinterpret_cast<const f32x4_t*>(st + r * ROWB + ((c ^ swz_k<D>(r)) << 4));
     }
-    if (row_ok && hh == 0) ea->lse[(int64_t)b * ea->l_sb + (int64_t)row * ea->l_st + (int64_t)h * ea->l_sh] = lse_v;
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int lin = i * 64 + lane;
+      const int r = lin / CH, c = lin % CH;
+      if (r < nvalid) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * o_st + c * 8) = val[i];
+    }
+    if (row_ok && hh == 0) lse_p[(int64_t)b * l_sb + (int64_t)row * l_st + (int64_t)h * l_sh] = lse_v;
   } else if (row_ok) {
     const int64_t sidx = (int64_t)b * ea->ws_slots + slot + lrow * G + g;
     float* op = ea->ws_o + sidx * D;
