@@ -239,6 +239,27 @@ def test_auto_split_only_when_items_cannot_fill_the_device():
     assert plan_n.info["num_split_items"] == 0
 
 
+def test_auto_split_cost_model_cases():
+    # Cases whose answer is fixed by the cost model's measured constants (about 1.8 us
+    # per tile per slot, 3 tiles per item, 6 us + partial traffic for the combine):
+    # (a) as many items as resident slots, each at most 64 tiles: splitting cannot pay
+    #     for the combine pass -- the rectangular causal GQA workload stays unsplit;
+    p2 = W.config(2)
+    plan2 = ffa.Plan(p2.q_ranges, p2.k_ranges, p2.mask_types, p2.total_q, p2.total_k, p2.heads_q,
+                     p2.heads_kv, p2.head_dim, num_cus=NCU)
+    assert plan2.info["num_items"] == 512 and plan2.info["num_split_items"] == 0
+    # (b) a quarter of the slots busy with items of up to 256 tiles: split;
+    p = W.make_problem("one_head", 16384, 16384, 1, 1, 128, [((0, 16384), (0, 16384), W.CAUSAL)])
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, num_cus=NCU)
+    assert plan.info["num_split_items"] > 0 and plan.info["num_items"] > 2 * NCU
+    # (c) the same sequence on a device with 8 CUs already has 8x more work per slot
+    #     than there are items to balance: no split.
+    plan_s = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                      p.head_dim, num_cus=8)
+    assert plan_s.info["num_split_items"] == 0
+
+
 def test_fwd_rejects_bad_arguments_without_launching(lib):
     p = ffa.Plan([[0, 64]], [[0, 64]], [1], 64, 64, 2, 2, 128, num_cus=NCU)
     fake = 1 << 20  # never dereferenced: validation fails first
