@@ -149,6 +149,44 @@ def test_q_zero_closed_form_hetero(gpu_lib):
     assert np.abs(l[fin] - ref[fin, None]).max() < 2e-5
 
 
+# ---------------------------------------------------------------- error relative to same-precision torch
+
+def _torch_bf16_out(p, q, k, v):
+    """Same-precision PyTorch result: bf16 scaled_dot_product_attention on the CPU, one call
+    per slice (the masks of configs 1-3 are per-slice causal squares or bottom-right
+    rectangles; GQA by repeating the kv heads)."""
+    import torch.nn.functional as F
+    out = torch.zeros(p.total_q, p.heads_q, p.head_dim, dtype=torch.float64)
+    rep = p.heads_q // p.heads_kv
+    for (qs, qe), (ks, ke), t in zip(p.q_ranges.tolist(), p.k_ranges.tolist(), p.mask_types.tolist()):
+        M, N = qe - qs, ke - ks
+        qq = q[qs:qe].permute(1, 0, 2).unsqueeze(0)
+        kk = k[ks:ke].repeat_interleave(rep, dim=1).permute(1, 0, 2).unsqueeze(0).contiguous()
+        vv = v[ks:ke].repeat_interleave(rep, dim=1).permute(1, 0, 2).unsqueeze(0).contiguous()
+        mask = None
+        if t == W.CAUSAL:  # bottom-right: local row m sees local key n <= N - M + m
+            mask = torch.arange(N)[None, :] <= (N - M + torch.arange(M))[:, None]
+        o = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask)
+        out[qs:qe] = o[0].permute(1, 0, 2).double()
+    return out.numpy()
+
+
+@pytest.mark.parametrize("cfg,div", [(1, 1), (2, 4), (3, 8)])
+def test_error_within_twice_same_precision_torch(gpu_lib, cfg, div):
+    # The FlagAttention user guide's accuracy rule ("Installation" / testing section):
+    # the kernel's error against a full-precision reference may be at most about twice
+    # the error of the same computation done by PyTorch at the kernel's precision, plus a
+    # small absolute allowance.  Reference: the fp64 oracle; same precision: bf16 SDPA.
+    p = W.config(cfg) if div == 1 else W.scaled(cfg, div)
+    q, k, v = W.make_qkv(p)
+    out, _ = run(gpu_lib, p, q, k, v)
+    ref, _ = oracle_ref(p, q, k, v)
+    e_gpu = np.abs(out.double().cpu().numpy() - ref).max()
+    e_torch = np.abs(_torch_bf16_out(p, q, k, v) - ref).max()
+    log(f"  config {cfg}/{div}: max error GPU {e_gpu:.3e}, torch bf16 {e_torch:.3e}, ratio {e_gpu / e_torch:.2f}")
+    assert e_gpu <= 2.0 * e_torch + 1e-3
+
+
 # ---------------------------------------------------------------- reference point of the exponentials
 
 @pytest.mark.parametrize("d,causal", [(128, False), (128, True), (64, True)])
