@@ -13,6 +13,8 @@ attention special cases, closed forms and the split/merge identity.
 from .fwd import (  # noqa: F401
     FULL,
     CAUSAL,
+    INVCAUSAL,
+    BICAUSAL,
     slice_row_interval,
     row_intervals,
     mask_rows,

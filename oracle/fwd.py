@@ -9,10 +9,16 @@ FlagAttention user guide, "FlashAttention"):
   (contiguous GQA groups; the pages only require Hq % Hkv == 0):
 
     V(i)      = union over slices s with qs <= i < qe of the keys
-                  j in [ks, ke)                         if s is FULL  (type 0)
-                  j in [ks, ke - (qe - 1 - i))          if s is CAUSAL (type 1)
-                (causal is bottom-right aligned: local row m of an M x N slice
-                 sees local keys n <= N - M + m)
+                  j in [ks, ke)                                   FULL      (type 0)
+                  j in [ks, ke - (qe - 1 - i))                    CAUSAL    (type 1)
+                  j in [ks + (i - qs), ke)                        INVCAUSAL (type 2)
+                  j in [ks + (i - qs), ke - (qe - 1 - i))         BICAUSAL  (type 3)
+                (the kv-interval formula of the MagiAttention blog page
+                 "Calculate KV Interval Boundaries for Mask Types": bit 1 of the
+                 type moves the start by the row's offset from qs, bit 0 moves the
+                 end back by its distance to qe - 1; so causal is bottom-right
+                 aligned -- local row m of an M x N slice sees local keys
+                 n <= N - M + m -- and inverse causal is top-left aligned)
     s_ij      = scale * sum_d q[i,h,d] * k[j,g,d]          scale defaults to 1/sqrt(D)
     lse[i,h]  = ln sum_{j in V(i)} exp(s_ij)                -inf when V(i) is empty
     out[i,h]  = sum_{j in V(i)} exp(s_ij - lse[i,h]) v[j,g]  0 when V(i) is empty
@@ -35,6 +41,8 @@ import numpy as np
 
 FULL = 0
 CAUSAL = 1
+INVCAUSAL = 2
+BICAUSAL = 3
 
 
 def slice_row_interval(i: int, qs: int, qe: int, ks: int, ke: int, mask_type: int) -> Tuple[int, int]:
@@ -42,14 +50,16 @@ def slice_row_interval(i: int, qs: int, qe: int, ks: int, ke: int, mask_type: in
 
     FULL: every key of the slice.  CAUSAL: bottom-right aligned, so the last
     query row of the slice sees every key and each earlier row one key fewer.
+    INVCAUSAL: top-left aligned, so the first row sees every key and each later
+    row starts one key later.  BICAUSAL: both bounds move, a band.
     """
     if not (qs <= i < qe):
         return (0, 0)
-    if mask_type == FULL:
-        return (ks, ke)
-    if mask_type == CAUSAL:
-        return (ks, ke - (qe - 1 - i))
-    raise ValueError(f"unknown mask type {mask_type}")
+    if mask_type not in (FULL, CAUSAL, INVCAUSAL, BICAUSAL):
+        raise ValueError(f"unknown mask type {mask_type}")
+    a = ks + (i - qs) if mask_type in (INVCAUSAL, BICAUSAL) else ks
+    b = ke - (qe - 1 - i) if mask_type in (CAUSAL, BICAUSAL) else ke
+    return (a, b)
 
 
 def row_intervals(i: int, q_ranges, k_ranges, mask_types) -> List[Tuple[int, int]]:
@@ -73,13 +83,11 @@ def mask_rows(rows: Sequence[int], q_ranges, k_ranges, mask_types, total_k: int)
         inside = (rows >= qs) & (rows < qe)
         if not inside.any():
             continue
-        if t == FULL:
-            end = np.full(rows.shape, ke, dtype=np.int64)
-        elif t == CAUSAL:
-            end = ke - (qe - 1 - rows)
-        else:
+        if t not in (FULL, CAUSAL, INVCAUSAL, BICAUSAL):
             raise ValueError(f"unknown mask type {t}")
-        vis = (cols >= ks) & (cols < end[:, None]) & inside[:, None]
+        start = ks + (rows - qs) if t in (INVCAUSAL, BICAUSAL) else np.full(rows.shape, ks, dtype=np.int64)
+        end = ke - (qe - 1 - rows) if t in (CAUSAL, BICAUSAL) else np.full(rows.shape, ke, dtype=np.int64)
+        vis = (cols >= start[:, None]) & (cols < end[:, None]) & inside[:, None]
         m |= vis
     return m
 

@@ -25,6 +25,9 @@ MUTATIONS = {
     "lse_drops_max": ("l = np.where(nonempty, safe + np.log(", "l = np.where(nonempty, 0.0 + np.log("),
     "union_lost": ("m |= vis", "m = vis"),
     "merge_weights_unshifted": ("w = np.exp(L - safe)", "w = np.exp(L - 2 * safe)"),
+    "invcausal_from_the_end": ("start = ks + (rows - qs) if", "start = ks + (qe - 1 - rows) if"),
+    "bicausal_loses_start": ("start = ks + (rows - qs) if t in (INVCAUSAL, BICAUSAL)",
+                             "start = ks + (rows - qs) if t in (INVCAUSAL,)"),
 }
 
 PINS = [
@@ -39,6 +42,10 @@ PINS = [
     lambda: pins.test_split_and_merge_reproduces_single_slice("causal"),
     pins.test_merge_with_empty_partial,
     pins.test_visible_pair_count_matches_mask_sum,
+    lambda: pins.test_mask_equals_interval_formula(9),
+    pins.test_square_inverse_causal_is_causal_on_reversed_sequences,
+    pins.test_square_bicausal_sees_only_its_diagonal_key,
+    pins.test_bicausal_band_splits_into_inverse_causal_and_causal,
 ]
 
 

@@ -89,11 +89,11 @@ def any_visible_cells(mask, cells):
 
 # ---------------------------------------------------------------- mask geometry
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_mask_equals_interval_formula(seed):
     rng = np.random.default_rng(seed)
     tq, tk = int(rng.integers(1, 40)), int(rng.integers(1, 40))
-    p = W.random_problem(seed, tq, tk, 1, 1, 8)
+    p = W.random_problem(seed, tq, tk, 1, 1, 8, n_types=2 if seed < 8 else 4)
     m = oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, tq, tk)
     sl = slices_of(p)
     ref = np.array([[any(formula_visible(i, j, *s) for s in sl) for j in range(tk)] for i in range(tq)])
@@ -133,14 +133,14 @@ def test_golden_block_causal_picture():
 
 # ---------------------------------------------------------------- values vs brute force
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_oracle_matches_brute_force(seed):
     rng = np.random.default_rng(100 + seed)
     tq, tk = int(rng.integers(1, 24)), int(rng.integers(1, 24))
     hkv = int(rng.choice([1, 2]))
     hq = hkv * int(rng.choice([1, 2]))
     d = int(rng.choice([4, 8]))
-    p = W.random_problem(seed, tq, tk, hq, hkv, d)
+    p = W.random_problem(seed, tq, tk, hq, hkv, d, n_types=2 if seed < 8 else 4)
     q, k, v = W.make_qkv(p, seed=seed)
     scale = float(rng.uniform(0.1, 1.0))
     out, lse = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, scale, block_rows=5)
@@ -305,6 +305,58 @@ def test_split_and_merge_reproduces_single_slice(kind):
     p2 = W.make_problem("two", M, N, 2, 1, 16, [left, right])
     o3, l3 = oracle.attend(q, k, v, p2.q_ranges, p2.k_ranges, p2.mask_types)
     assert np.allclose(o3, o, atol=1e-12) and np.allclose(l3, l, atol=1e-12)
+
+
+def test_square_inverse_causal_is_causal_on_reversed_sequences():
+    # Row i of a square INVCAUSAL slice sees keys j >= i.  Reversing the order of
+    # queries and keys turns that into j' <= i': torch's fp64 causal SDPA on the
+    # flipped tensors, flipped back, must give the same out and lse.
+    import torch.nn.functional as F
+    T = 40
+    p = W.make_problem("inv", T, T, 2, 1, 16, [((0, T), (0, T), W.INVCAUSAL)])
+    q, k, v = W.make_qkv(p, seed=21)
+    out, lse = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types)
+    qf, kf, vf = (x.double().flip(0) for x in (q, k, v))
+    for h in range(2):
+        ref = F.scaled_dot_product_attention(qf[:, h][None], kf[:, 0][None], vf[:, 0][None], is_causal=True)[0].flip(0)
+        assert np.allclose(out[:, h], ref.numpy(), atol=1e-12)
+        s = (qf[:, h] @ kf[:, 0].T) / math.sqrt(16)
+        s = s.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), -math.inf)
+        assert np.allclose(lse[:, h], torch.logsumexp(s, dim=1).flip(0).numpy(), atol=1e-12)
+
+
+def test_square_bicausal_sees_only_its_diagonal_key():
+    # A square BICAUSAL slice leaves each row exactly one key, its own:
+    # out = v[i], lse = scale * q[i] . k[i].
+    T, D = 24, 8
+    p = W.make_problem("bi", T, T, 2, 2, D, [((0, T), (0, T), W.BICAUSAL)])
+    q, k, v = W.make_qkv(p, seed=22)
+    out, lse = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types)
+    qd, kd, vd = q.double(), k.double(), v.double()
+    assert np.allclose(out, vd.numpy(), atol=1e-12)
+    assert np.allclose(lse, ((qd * kd).sum(-1) / math.sqrt(D)).numpy(), atol=1e-12)
+
+
+def test_bicausal_band_splits_into_inverse_causal_and_causal():
+    # A BICAUSAL slice of M queries over N >= 2M - 1 keys is a band of width
+    # w = N - M + 1 >= M.  Cut its keys at kmid in [M - 1, w]: row i sees
+    # [i, kmid) through the left part (INVCAUSAL over [0, kmid)) and
+    # [kmid, N - (M - 1 - i)) through the right part (CAUSAL over [kmid, N)).
+    # Merging the two by logsumexp must give the band.
+    M, N = 12, 30
+    p = W.make_problem("band", M, N, 2, 1, 16, [((0, M), (0, N), W.BICAUSAL)])
+    q, k, v = W.make_qkv(p, seed=23)
+    o, l = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types)
+    for kmid in (M - 1, 15, N - M + 1):
+        pl = W.make_problem("l", M, N, 2, 1, 16, [((0, M), (0, kmid), W.INVCAUSAL)])
+        pr = W.make_problem("r", M, N, 2, 1, 16, [((0, M), (kmid, N), W.CAUSAL)])
+        o1, l1 = oracle.attend(q, k, v, pl.q_ranges, pl.k_ranges, pl.mask_types)
+        o2, l2 = oracle.attend(q, k, v, pr.q_ranges, pr.k_ranges, pr.mask_types)
+        om, lm = oracle.merge_partials([o1, o2], [l1, l2])
+        assert np.allclose(om, o, atol=1e-12) and np.allclose(lm, l, atol=1e-12)
+    # the band has exactly w keys on every row
+    m = oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, M, N)
+    assert (m.sum(axis=1) == N - M + 1).all()
 
 
 def test_merge_with_empty_partial():

@@ -39,6 +39,8 @@ import numpy as np
 
 FULL = 0
 CAUSAL = 1
+INVCAUSAL = 2
+BICAUSAL = 3
 
 CONFIG_NAMES = {
     1: "tiny_causal",
@@ -161,12 +163,13 @@ def scaled(i: int, factor: int) -> Problem:
 
 
 def random_problem(seed: int, total_q: int, total_k: int, hq: int, hkv: int, d: int,
-                   max_slices: int = 6) -> Problem:
+                   max_slices: int = 6, n_types: int = 2) -> Problem:
     """Random disjoint slices for small property tests.
 
     Slices are built on a grid of q bands; each q band receives up to two slices
     whose k ranges do not overlap, so no (q, k) pair is covered twice.  Types are
-    random full / causal; empty ranges and rows with no slice occur by design.
+    drawn from the first n_types codes (2: full / causal; 4: also inverse causal
+    and bi-causal); empty ranges and rows with no slice occur by design.
     """
     rng = np.random.default_rng(seed)
     cuts = sorted(set([0, total_q] + list(rng.integers(0, total_q + 1, size=rng.integers(1, 4)))))
@@ -182,7 +185,7 @@ def random_problem(seed: int, total_q: int, total_k: int, hq: int, hkv: int, d: 
             if rng.random() < 0.3 and b - a > 2:
                 qa = int(rng.integers(a, b))
                 qb = int(rng.integers(qa, b + 1))
-            slices.append(((int(qa), int(qb)), (int(ka), int(kb)), int(rng.integers(0, 2))))
+            slices.append(((int(qa), int(qb)), (int(ka), int(kb)), int(rng.integers(0, n_types))))
             if len(slices) >= max_slices:
                 break
         if len(slices) >= max_slices:
