@@ -36,11 +36,15 @@ __all__ = [
     "load_library",
     "library_path",
     "FULL",
+    "INVCAUSAL",
+    "BICAUSAL",
     "CAUSAL",
 ]
 
 FULL = 0
 CAUSAL = 1
+INVCAUSAL = 2  # row i of a slice starts at ks + (i - qs): top-left aligned
+BICAUSAL = 3   # both bounds move with the row: a band (sliding window)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libffa.so")

@@ -187,20 +187,21 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(f32x4_t x) { return __builtin_bit_
 // Tile iterator over an item's runs (wave-uniform): the tile's first key and the
 // mask parameters of its run.
 struct TileIt {
-  int ri, ti, k0, nt, nf, khi, eb;
+  int ri, ti, k0, nt, nf, khi, eb, nl, lb;
   __device__ __forceinline__ int kstart() const { return k0 + ti * kBlockN; }
-  __device__ __forceinline__ bool edge() const { return ti >= nf; }
+  // tiles [nl, nl + nf) of a run are visible to every row; the others need the mask
+  __device__ __forceinline__ bool edge() const { return (unsigned)(ti - nl) >= (unsigned)nf; }
 };
 __device__ __forceinline__ void tile_first(TileIt& t, const FFA_CONST int32_t* rp) {
   t.ri = 0; t.ti = 0;
-  t.k0 = rp[0]; t.nt = rp[1]; t.nf = rp[2]; t.khi = rp[3]; t.eb = rp[4];
+  t.k0 = rp[0]; t.nt = rp[1]; t.nf = rp[2]; t.khi = rp[3]; t.eb = rp[4]; t.nl = rp[5]; t.lb = rp[6];
 }
 __device__ __forceinline__ void tile_next(TileIt& t, const FFA_CONST int32_t* rp, int n_runs) {
   if (++t.ti >= t.nt && t.ri + 1 < n_runs) {
     ++t.ri;
     t.ti = 0;
     const FFA_CONST int32_t* r = rp + t.ri * kRec;
-    t.k0 = r[0]; t.nt = r[1]; t.nf = r[2]; t.khi = r[3]; t.eb = r[4];
+    t.k0 = r[0]; t.nt = r[1]; t.nf = r[2]; t.khi = r[3]; t.eb = r[4]; t.nl = r[5]; t.lb = r[6];
   }
 }
 
@@ -409,14 +410,26 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     });
   };
 
-  // edge mask of a tile's scores: key j (absolute) visible iff j < min(k_hi, row + edge_base)
+  // edge mask of a tile's scores: key j (absolute) visible iff
+  // row + lo_base <= j < min(k_hi, row + edge_base); the lower bound only exists
+  // for slices whose start moves with the row (inverse causal, bi-causal)
   auto mask = [&](const TileIt& t, f32x16_t& sa, f32x16_t& sb) {
-    const int lim = min(t.khi, row + t.eb) - t.kstart() - 4 * hh;
+    const int base = t.kstart() + 4 * hh;
+    const int lim = min(t.khi, row + t.eb) - base;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int rel = 8 * (i >> 2) + (i & 3);
       if (rel >= lim) sa[i] = -INFINITY;
       if (rel + 32 >= lim) sb[i] = -INFINITY;
+    }
+    if (t.lb != -ffa::kNoEdge) {
+      const int low = row + t.lb - base;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rel = 8 * (i >> 2) + (i & 3);
+        if (rel < low) sa[i] = -INFINITY;
+        if (rel + 32 < low) sb[i] = -INFINITY;
+      }
     }
   };
 

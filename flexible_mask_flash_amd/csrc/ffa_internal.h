@@ -15,11 +15,13 @@
 //          in order; `tiles` is the total key-tile count of those runs.  The
 //          inline first run lets a workgroup issue its first K/V loads as soon
 //          as its one item record has arrived (no second dependent load).
-// Run:     k0, n_tiles, n_full, k_hi, edge_base, 0, 0, 0
+// Run:     k0, n_tiles, n_full, k_hi, edge_base, n_lead, lo_base, 0
 //          key tile t covers [k0 + t*BN, k0 + (t+1)*BN); row i sees key j iff
-//          j < min(k_hi, i + edge_base) (edge_base = ke - qe + 1 for a causal
-//          slice, kNoEdge for a full one); the first n_full tiles are visible
-//          to every row of the item, so they need no mask.
+//          i + lo_base <= j < min(k_hi, i + edge_base)  (edge_base = ke - qe + 1
+//          when bit 0 of the slice type is set, else kNoEdge; lo_base = ks - qs
+//          when bit 1 is set, else -kNoEdge); tiles [n_lead, n_lead + n_full)
+//          are visible to every row of the item and need no mask, the first
+//          n_lead and the last n_tiles - n_lead - n_full tiles do.
 // Combine: q0, nrows, h0, n_chunks, slot0, 0, 0, 0
 //          chunk c of row (q0 + r), head (h0 + g) is partial slot
 //          slot0 + c * kSlotsPerItem + r * heads_per_item + g.

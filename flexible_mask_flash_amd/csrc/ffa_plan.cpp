@@ -46,24 +46,64 @@ struct Slice {
   int32_t qs, qe, ks, ke, type, id;
 };
 
-// Visible key end of row i through slice s (may be <= ks: nothing visible).
+// Keys row i sees through slice s: [row_start, row_end) (the kv-interval
+// formula: bit 1 of the type moves the start by the row's offset from qs, bit 0
+// moves the end back by its distance to qe - 1).  Both are nondecreasing in i;
+// the interval may be empty.
+inline int64_t row_start(const Slice& s, int64_t i) {
+  return (s.type & 2) ? (int64_t)s.ks + (i - s.qs) : (int64_t)s.ks;
+}
 inline int64_t row_end(const Slice& s, int64_t i) {
-  return s.type == FFA_MASK_CAUSAL ? (int64_t)s.ke - ((int64_t)s.qe - 1 - i) : (int64_t)s.ke;
+  return (s.type & 1) ? (int64_t)s.ke - ((int64_t)s.qe - 1 - i) : (int64_t)s.ke;
 }
 
 int64_t slice_visible_pairs(const Slice& s) {
   const int64_t M = s.qe - s.qs, N = s.ke - s.ks;
   if (M <= 0 || N <= 0) return 0;
   if (s.type == FFA_MASK_FULL) return M * N;
-  // causal: local row m sees clamp(N - M + 1 + m, 0, N) keys
+  if (s.type == FFA_MASK_BICAUSAL) return M * std::max<int64_t>(0, N - M + 1);  // a band of N - M + 1 keys
+  // causal: local row m sees clamp(N - M + 1 + m, 0, N) keys; inverse causal is
+  // the same count with the rows in reverse order
   const int64_t c = N - M + 1;
   const int64_t m0 = std::max<int64_t>(0, 1 - c);
   if (m0 >= M) return 0;
   return (c + m0 + N) * (M - m0) / 2;
 }
 
+// Largest number of keys two slices share on one row over the rows both cover
+// (0: disjoint).  The shared count min(ends) - max(starts) is concave and
+// piecewise linear in the row (slopes 0 / 1), so its maximum lies at an end of
+// the shared rows or where two of the bounding lines cross.
+int64_t max_shared_keys(const Slice& a, const Slice& b) {
+  const int64_t r0 = std::max(a.qs, b.qs), r1 = std::min(a.qe, b.qe) - 1;
+  if (r1 < r0) return 0;
+  auto shared = [&](int64_t i) {
+    const int64_t lo = std::max({row_start(a, i), row_start(b, i), (int64_t)a.ks, (int64_t)b.ks});
+    const int64_t hi = std::min({row_end(a, i), row_end(b, i), (int64_t)a.ke, (int64_t)b.ke});
+    return hi - lo;
+  };
+  // each bound is c + slope * i; crossings of two lines with different slopes
+  std::vector<int64_t> cand = {r0, r1};
+  const int64_t ca[4] = {row_start(a, 0), row_start(b, 0), row_end(a, 0), row_end(b, 0)};
+  const int64_t sl[4] = {(a.type & 2) ? 1 : 0, (b.type & 2) ? 1 : 0, (a.type & 1) ? 1 : 0, (b.type & 1) ? 1 : 0};
+  const int64_t cst[4] = {a.ks, b.ks, a.ke, b.ke};
+  for (int x = 0; x < 4; ++x) {
+    for (int y = 0; y < 4; ++y) {
+      if (sl[x] == 1 && sl[y] == 0) cand.push_back(ca[y] - ca[x]);       // line x meets line y
+      if (sl[x] == 1) cand.push_back(cst[x] - ca[x]);                    // line x meets its clamp
+    }
+  }
+  int64_t best = 0;
+  for (int64_t c : cand)
+    for (int64_t d = -1; d <= 1; ++d) {
+      const int64_t i = std::min(r1, std::max(r0, c + d));
+      best = std::max(best, shared(i));
+    }
+  return best;
+}
+
 struct TileRun {
-  int32_t k0, n_tiles, n_full, k_hi, edge_base;
+  int32_t k0, n_tiles, n_full, k_hi, edge_base, n_lead, lo_base;
 };
 
 struct QTile {
@@ -137,17 +177,17 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
     if (x.ks < 0 || x.ke > total_k || x.ks > x.ke)
       return set_error(FFA_ERR_RANGE, "slice " + std::to_string(s) + ": k_range [" + std::to_string(x.ks) + ", " +
                                           std::to_string(x.ke) + ") outside [0, " + std::to_string(total_k) + "]");
-    if (x.type != FFA_MASK_FULL && x.type != FFA_MASK_CAUSAL)
+    if (x.type < FFA_MASK_FULL || x.type > FFA_MASK_BICAUSAL)
       return set_error(FFA_ERR_MASK_TYPE, "slice " + std::to_string(s) + ": mask type " + std::to_string(x.type) +
-                                              " (supported: 0 full, 1 causal)");
+                                              " (supported: 0 full, 1 causal, 2 inverse causal, 3 bi-causal)");
     const int64_t vp = slice_visible_pairs(x);
     if (vp == 0) continue;  // a slice that makes nothing visible is a no-op
     visible += vp;
     slices.push_back(x);
   }
 
-  // overlap: two slices share a visible pair iff they do on the last row both cover,
-  // because visible ends are nondecreasing in the row and starts are constant.
+  // overlap: two slices share a visible pair iff some row both cover sees a
+  // common key (max_shared_keys evaluates the shared count where it can peak).
   {
     std::vector<int> ord(slices.size());
     std::iota(ord.begin(), ord.end(), 0);
@@ -157,12 +197,9 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
       for (size_t ib = ia + 1; ib < ord.size(); ++ib) {
         const Slice& b = slices[ord[ib]];
         if (b.qs >= a.qe) break;
-        const int64_t last = std::min(a.qe, b.qe) - 1;
-        const int64_t ea = std::min<int64_t>(row_end(a, last), a.ke);
-        const int64_t eb = std::min<int64_t>(row_end(b, last), b.ke);
-        if (std::max(a.ks, b.ks) < std::min(ea, eb))
+        if (max_shared_keys(a, b) > 0)
           return set_error(FFA_ERR_OVERLAP, "slices " + std::to_string(a.id) + " and " + std::to_string(b.id) +
-                                                " overlap (row " + std::to_string(last) + ")");
+                                                " overlap");
       }
     }
   }
@@ -208,15 +245,24 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
       const int64_t r_last = (int64_t)r0 + t.nrows - 1;
       for (int si : active) {
         const Slice& s = slices[si];
+        // starts and ends are nondecreasing in the row, and so is neither width
+        // bound's direction: the tile sees [lo_first, e_last) in total, every
+        // row of it sees [lo_last, e_first), and a row sees something iff the
+        // wider of its first and last rows does
+        const int64_t lo_first = row_start(s, r0), lo_last = row_start(s, r_last);
+        const int64_t e_first = std::min<int64_t>(row_end(s, r0), s.ke);
         const int64_t e_last = std::min<int64_t>(row_end(s, r_last), s.ke);
-        if (e_last <= s.ks) continue;  // no row of the tile sees this slice
-        const int64_t e_first = std::max<int64_t>(std::min<int64_t>(row_end(s, r0), s.ke), s.ks);
+        if (std::max(e_first - lo_first, e_last - lo_last) <= 0) continue;  // no row sees this slice
+        const int64_t t_first = (lo_first - s.ks) / kBlockN;                 // tiles aligned to ks
+        const int64_t k0 = s.ks + t_first * kBlockN;
         TileRun run;
-        run.k0 = s.ks;
-        run.n_tiles = (int32_t)((e_last - s.ks + kBlockN - 1) / kBlockN);
-        run.n_full = (int32_t)((e_first - s.ks) / kBlockN);
+        run.k0 = (int32_t)k0;
+        run.n_tiles = (int32_t)((e_last - k0 + kBlockN - 1) / kBlockN);
+        run.n_lead = (int32_t)std::min<int64_t>(run.n_tiles, (std::max<int64_t>(lo_last - k0, 0) + kBlockN - 1) / kBlockN);
+        run.n_full = (int32_t)std::max<int64_t>(0, std::min<int64_t>(run.n_tiles, (e_first - k0) / kBlockN) - run.n_lead);
         run.k_hi = s.ke;
-        run.edge_base = s.type == FFA_MASK_CAUSAL ? s.ke - s.qe + 1 : kNoEdge;
+        run.edge_base = (s.type & 1) ? s.ke - s.qe + 1 : kNoEdge;
+        run.lo_base = (s.type & 2) ? s.ks - s.qs : -kNoEdge;
         t.runs.push_back(run);
         t.tiles += run.n_tiles;
       }
@@ -280,8 +326,8 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   std::vector<int32_t> combine;   // flattened combine records
   int32_t n_slots = 0, n_split_items = 0;
   int64_t computed = 0, all_tiles = 0;
-  auto push_run = [&](int32_t k0, int32_t nt, int32_t nf, int32_t khi, int32_t eb) {
-    const int32_t rec[kRec] = {k0, nt, nf, khi, eb, 0, 0, 0};
+  auto push_run = [&](int32_t k0, int32_t nt, int32_t nl, int32_t nf, const TileRun& r) {
+    const int32_t rec[kRec] = {k0, nt, nf, r.k_hi, r.edge_base, nl, r.lo_base, 0};
     runs.insert(runs.end(), rec, rec + kRec);
   };
 
@@ -291,7 +337,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
     const int64_t n_chunks = n_chunks_of(t.tiles, chunk_target);
     if (n_chunks <= 1) {
       const int32_t off = (int32_t)(runs.size() / kRec);
-      for (const TileRun& r : t.runs) push_run(r.k0, r.n_tiles, r.n_full, r.k_hi, r.edge_base);
+      for (const TileRun& r : t.runs) push_run(r.k0, r.n_tiles, r.n_lead, r.n_full, r);
       for (int32_t g = 0; g < n_groups; ++g)
         items.push_back({t.q0, t.nrows, g * G, off, (int32_t)t.runs.size(), -1, (int32_t)t.tiles});
       continue;
@@ -309,7 +355,11 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
         if (b > a) {
           const int32_t skip = (int32_t)(a - cs);
           const int32_t nt = (int32_t)(b - a);
-          push_run(r.k0 + skip * kBlockN, nt, std::max(0, std::min(nt, r.n_full - skip)), r.k_hi, r.edge_base);
+          // the chunk's tiles [skip, skip + nt) of the run: lead edge tiles, then
+          // the full ones, then trailing edge tiles, as in the run itself
+          const int32_t nl = std::max(0, std::min(nt, r.n_lead - skip));
+          const int32_t fa = std::max(skip, r.n_lead), fb = std::min(skip + nt, r.n_lead + r.n_full);
+          push_run(r.k0 + skip * kBlockN, nt, nl, std::max(0, fb - fa), r);
           ++nr;
         }
         cs += r.n_tiles;

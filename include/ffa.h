@@ -7,8 +7,10 @@
  *   q [total_q, Hq, D], k and v [total_k, Hkv, D], bfloat16, head_dim D
  *   contiguous.  A mask is a list of S slices (q_range, k_range, type) with
  *   half-open ranges.  Query row i of slice s (qs <= i < qe) sees
- *     FULL   (type 0): keys [ks, ke)
- *     CAUSAL (type 1): keys [ks, ke - (qe - 1 - i))   -- bottom-right aligned
+ *     FULL      (type 0): keys [ks, ke)
+ *     CAUSAL    (type 1): keys [ks, ke - (qe - 1 - i))             -- bottom-right aligned
+ *     INVCAUSAL (type 2): keys [ks + (i - qs), ke)                 -- top-left aligned
+ *     BICAUSAL  (type 3): keys [ks + (i - qs), ke - (qe - 1 - i))  -- a band (sliding window)
  *   (the kv-interval formula of the MagiAttention blog page "Calculate KV
  *   Interval Boundaries for Mask Types", bits 0 / 1 of the type).
  *   Query head h uses kv head h / (Hq / Hkv); Hq % Hkv == 0 is required.
@@ -51,6 +53,8 @@ extern "C" {
 
 #define FFA_MASK_FULL 0
 #define FFA_MASK_CAUSAL 1
+#define FFA_MASK_INVCAUSAL 2
+#define FFA_MASK_BICAUSAL 3
 
 typedef enum {
   FFA_OK = 0,
@@ -58,7 +62,7 @@ typedef enum {
   FFA_ERR_SHAPE = 2,       /* total_q/total_k < 0, heads <= 0, head_dim not in {64, 128}   */
   FFA_ERR_GQA = 3,         /* heads_q % heads_kv != 0                                      */
   FFA_ERR_RANGE = 4,       /* a range leaves [0, total] or has start > end                 */
-  FFA_ERR_MASK_TYPE = 5,   /* a type other than 0 (FULL) or 1 (CAUSAL)                     */
+  FFA_ERR_MASK_TYPE = 5,   /* a type outside 0..3 (FULL, CAUSAL, INVCAUSAL, BICAUSAL)      */
   FFA_ERR_OVERLAP = 6,     /* two slices make some (q, k) pair visible twice               */
   FFA_ERR_WORKSPACE = 7,   /* meta or workspace buffer missing or too small                */
   FFA_ERR_HIP = 8,         /* a HIP runtime call failed (message in ffa_last_error)        */

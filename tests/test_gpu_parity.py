@@ -267,6 +267,64 @@ def test_random_slices(gpu_lib, seed):
             what=f"random {seed} T=({tq},{tk}) H=({hq},{hkv}) D={d} split={split}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_slices_all_mask_types(gpu_lib, seed):
+    # inverse-causal and bi-causal slices mixed with full and causal ones
+    rng = np.random.default_rng(1700 + seed)
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    tq, tk = int(rng.integers(1, 700)), int(rng.integers(1, 900))
+    p = W.random_problem(1700 + seed, tq, tk, hq, hkv, d, n_types=4)
+    q, k, v = W.make_qkv(p)
+    split = int(rng.choice([0, -1, 2]))
+    out, lse = run(gpu_lib, p, q, k, v, split_tiles=split)
+    compare(out, lse, *oracle_ref(p, q, k, v),
+            what=f"random all types {seed} T=({tq},{tk}) H=({hq},{hkv}) D={d} types={p.mask_types.tolist()}")
+
+
+def sliding_window_problem(T, w, docs, hq, hkv, d, seed):
+    """Per-document sliding window of w keys: row i sees keys [max(s, i - w + 1), i + 1).
+    The first w - 1 rows of a document are a causal slice; the rest a bi-causal band."""
+    sl = []
+    for s0, e0 in zip(docs[:-1], docs[1:]):
+        h = min(e0, s0 + w - 1)
+        if h > s0:
+            sl.append(((s0, h), (s0, h), W.CAUSAL))
+        if e0 > h:
+            sl.append(((h, e0), (h - w + 1, e0), W.BICAUSAL))
+    return W.make_problem(f"window{w}", T, T, hq, hkv, d, sl, seed=seed)
+
+
+@pytest.mark.parametrize("w,split", [(1, 0), (200, 0), (513, 0), (513, 3)])
+def test_sliding_window(gpu_lib, w, split):
+    T = 3000
+    docs = [0, 1100, 1130, 3000]
+    p = sliding_window_problem(T, w, docs, 8, 2, 128, seed=31)
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v, split_tiles=split)
+    compare(out, lse, *oracle_ref(p, q, k, v), what=f"sliding window w={w} split={split}")
+    # q = 0: lse = ln(window size) row by row
+    q0 = torch.zeros_like(q)
+    _, lse0 = run(gpu_lib, p, q0, k, v, split_tiles=split)
+    cnt = np.zeros(T)
+    for s0, e0 in zip(docs[:-1], docs[1:]):
+        i = np.arange(s0, e0)
+        cnt[s0:e0] = np.minimum(i - s0 + 1, w)
+    err = np.abs(lse0.double().cpu().numpy() - np.log(cnt)[:, None]).max()
+    assert err < 2e-5, err
+
+
+def test_inverse_causal_full_size_sampled(gpu_lib):
+    # top-left aligned inverse causal over a 4096 x 6000 slice (the first row sees every
+    # key, row i starts at key i), GQA 4, D = 128
+    p = W.make_problem("inv", 4096, 6000, 16, 4, 128, [((0, 4096), (0, 6000), W.INVCAUSAL)], seed=41)
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v)
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 97), [0, 1, 63, 64, 4095]]))
+    compare(out, lse, *oracle_ref(p, q, k, v, rows=rows), rows=rows, what="inverse causal 4096x6000")
+
+
 def test_no_slices_and_empty_rows(gpu_lib):
     p = W.make_problem("none", 100, 50, 4, 2, 64, [])
     q, k, v = W.make_qkv(p)

@@ -73,7 +73,10 @@ def test_validation_errors():
     assert plan_status([[0, 9]], [[0, 8]], [1], 8, 8, 2, 2, 128) == 4   # q out of range
     assert plan_status([[5, 3]], [[0, 8]], [1], 8, 8, 2, 2, 128) == 4   # start > end
     assert plan_status([[0, 8]], [[-1, 8]], [0], 8, 8, 2, 2, 128) == 4
-    assert plan_status([[0, 8]], [[0, 8]], [2], 8, 8, 2, 2, 128) == 5   # mask type
+    assert plan_status([[0, 8]], [[0, 8]], [4], 8, 8, 2, 2, 128) == 5   # mask type
+    assert plan_status([[0, 8]], [[0, 8]], [-1], 8, 8, 2, 2, 128) == 5
+    assert plan_status([[0, 8]], [[0, 8]], [2], 8, 8, 2, 2, 128) == 0   # inverse causal
+    assert plan_status([[0, 8]], [[0, 8]], [3], 8, 8, 2, 2, 128) == 0   # bi-causal (the diagonal)
     assert plan_status([[0, 8], [4, 8]], [[0, 8], [7, 8]], [0, 0], 8, 8, 2, 2, 128) == 6  # overlap
     # touching but disjoint: causal [0,8)x[0,8) and full rows [0,8) keys [8,12)
     assert plan_status([[0, 8], [0, 8]], [[0, 8], [8, 12]], [1, 0], 8, 12, 2, 2, 128) == 0
@@ -82,10 +85,38 @@ def test_validation_errors():
     assert plan_status([[0, 4], [0, 3]], [[0, 8], [7, 8]], [1, 0], 4, 8, 1, 1, 64) == 0
     assert plan_status([[0, 4], [0, 4]], [[0, 8], [7, 8]], [1, 0], 4, 8, 1, 1, 64) == 6
     assert plan_status(*ok, 8, 8, 2, 2, 128, num_cus=-3) == 11
+    # a band (row i sees keys [i, i + 3)) meets the FULL slice on key 5 only on
+    # rows 3..5: neither the first nor the last shared row shows the overlap
+    assert plan_status([[0, 10], [0, 10]], [[0, 12], [5, 6]], [3, 0], 10, 12, 1, 1, 64) == 6
+    assert plan_status([[0, 10], [0, 3]], [[0, 12], [5, 6]], [3, 0], 10, 12, 1, 1, 64) == 0
+    assert plan_status([[0, 10], [6, 10]], [[0, 12], [5, 6]], [3, 0], 10, 12, 1, 1, 64) == 0
+    # inverse causal over keys [i, 10) next to causal over [0, i - 4): disjoint on every row
+    assert plan_status([[0, 10], [0, 10]], [[0, 10], [0, 5]], [2, 1], 10, 10, 1, 1, 64) == 0
+    # ... but a FULL slice on key 0 meets it on the first row only
+    assert plan_status([[0, 10], [0, 10]], [[0, 10], [0, 1]], [2, 0], 10, 10, 1, 1, 64) == 6
     # zero slices is a valid (all-empty) problem
     assert plan_status(np.zeros((0, 2)), np.zeros((0, 2)), np.zeros(0), 8, 8, 2, 2, 64) == 0
     # empty slices are no-ops, even when their rectangle would overlap another slice
     assert plan_status([[0, 8], [2, 2]], [[0, 8], [0, 8]], [0, 0], 8, 8, 2, 2, 64) == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_overlap_verdict_matches_mask_intersection(seed):
+    # random pairs of slices of all four types: the planner rejects a pair iff the
+    # oracle's masks of the two slices share a (row, key) pair
+    rng = np.random.default_rng(900 + seed)
+    for _ in range(150):
+        T = int(rng.integers(1, 24))
+        qr, kr = [], []
+        for _s in range(2):
+            a, b = sorted(rng.integers(0, T + 1, size=2).tolist())
+            c, d = sorted(rng.integers(0, T + 1, size=2).tolist())
+            qr.append([a, b]), kr.append([c, d])
+        ty = rng.integers(0, 4, size=2).tolist()
+        m0 = oracle.dense_mask([qr[0]], [kr[0]], [ty[0]], T, T)
+        m1 = oracle.dense_mask([qr[1]], [kr[1]], [ty[1]], T, T)
+        want = 6 if (m0 & m1).any() else 0
+        assert plan_status(qr, kr, ty, T, T, 1, 1, 64) == want, (qr, kr, ty)
 
 
 def test_last_error_names_the_slice(lib):
@@ -125,14 +156,14 @@ def rasterise(p, plan):
         rows = np.arange(q0, q0 + nrows)
         assert sum(m["runs"][roff + r][1] for r in range(nruns)) == tiles
         for r in range(nruns):
-            k0, nt, nf, khi, eb = m["runs"][roff + r][:5]
-            assert nt >= 1 and 0 <= nf <= nt
+            k0, nt, nf, khi, eb, nl, lb = m["runs"][roff + r][:7]
+            assert nt >= 1 and nl >= 0 and nf >= 0 and nl + nf <= nt
             for t in range(nt):
                 keys = np.arange(k0 + t * bn, k0 + (t + 1) * bn)
                 lim = np.minimum(khi, rows + eb)
-                vis = keys[None, :] < lim[:, None]
-                if t < nf:
-                    assert vis.all(), "a tile before n_full needs a mask"
+                vis = (keys[None, :] < lim[:, None]) & (keys[None, :] >= (rows + lb)[:, None])
+                if nl <= t < nl + nf:
+                    assert vis.all(), "a tile marked full needs a mask"
                 assert vis.any(), "an emitted tile is fully masked"
                 kk = keys[keys < p.total_k]
                 for g in range(G):
@@ -170,14 +201,35 @@ def check_plan(p, **kw):
     return plan, m
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(16))
 def test_worklist_covers_mask_exactly_once(seed):
     rng = np.random.default_rng(seed)
     tq, tk = int(rng.integers(1, 300)), int(rng.integers(1, 300))
     hkv = int(rng.choice([1, 2]))
     hq = hkv * int(rng.choice([1, 2, 4, 8]))
-    p = W.random_problem(seed, tq, tk, hq, hkv, 64)
+    p = W.random_problem(seed, tq, tk, hq, hkv, 64, n_types=2 if seed < 10 else 4)
     check_plan(p)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sliding_window_bands_cover_mask_exactly_once(seed):
+    # sliding windows written as bi-causal slices: rows [s, e) of a document see
+    # the w keys ending at their own position (keys [i - w + 1, i + 1) clipped to
+    # the document), i.e. a band slice q [s, e) x k [s - w + 1, e) cut at s
+    rng = np.random.default_rng(300 + seed)
+    T, w = int(rng.integers(200, 700)), int(rng.integers(1, 200))
+    docs = [0] + sorted(rng.choice(np.arange(1, T), size=2, replace=False).tolist()) + [T]
+    sl = []
+    for s0, e0 in zip(docs[:-1], docs[1:]):
+        # rows [s0, min(e0, s0 + w - 1)) see the document start: causal part
+        h = min(e0, s0 + w - 1)
+        if h > s0:
+            sl.append(((s0, h), (s0, h), W.CAUSAL))
+        if e0 > h:
+            sl.append(((h, e0), (h - w + 1, e0), W.BICAUSAL))
+    p = W.make_problem("window", T, T, 4, 1, 64, sl)
+    check_plan(p)
+    check_plan(p, split_tiles=2)
 
 
 @pytest.mark.parametrize("seed", range(6))
