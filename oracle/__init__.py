@@ -24,3 +24,4 @@ from .fwd import (  # noqa: F401
     attend_dense,
     merge_partials,
 )
+from .bwd import attend_backward  # noqa: F401,E402
