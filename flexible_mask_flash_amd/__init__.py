@@ -8,9 +8,12 @@ or cannot be loaded, every entry point raises.
 
 API (names follow the pages):
   flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, softmax_scale=None)
-      MagiAttention's single-GPU FFA interface, forward only; packed THD
+      MagiAttention's single-GPU FFA interface, forward; packed THD
       tensors q [Tq,Hq,D], k/v [Tk,Hkv,D] (bf16) -> (out [Tq,Hq,D] bf16,
       lse [Tq,Hq] fp32).
+  flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map)
+      its gradients (dq, dk, dv).
+  flex_flash_attn_func(...)  the same forward as a torch.autograd.Function.
   flash_attention(q, k, v, causal=False, sm_scale=None, ...)
       FlagAttention's dense contract on [B,H,M,D] tensors (GQA, bottom-right
       causal); returns out, or the 5-tuple (out, lse [B,Hq,M], None, None,
@@ -32,6 +35,8 @@ __all__ = [
     "FFAError",
     "Plan",
     "flex_flash_attn_fwd",
+    "flex_flash_attn_bwd",
+    "flex_flash_attn_func",
     "flash_attention",
     "load_library",
     "library_path",
@@ -83,6 +88,11 @@ class PlanInfo(ctypes.Structure):
         ("block_n", _i32),
         ("max_item_tiles", _i32),
         ("total_tiles", _i64),
+        ("bwd_workspace_bytes", _i64),
+        ("dq_tiles", _i64),
+        ("kv_tiles", _i64),
+        ("num_dq_items", _i32),
+        ("num_kv_items", _i32),
     ]
 
 
@@ -103,10 +113,23 @@ _SIGNATURES = [
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
                        _f32, _vp, _sz, _vp]),
+    ("ffa_bwd", _i32, [_vp, _vp, _i32,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _vp, _i64, _i64, _i64,
+                       _f32, _vp, _sz, _vp]),
     ("ffa_plan_destroy", None, [_vp]),
 ]
 
-ABI_VERSION = 1
+ABI_VERSION = 2
+PLAN_NATURAL_ORDER = 1
+PLAN_BACKWARD = 2
 
 
 def library_path() -> str:
@@ -164,7 +187,7 @@ class Plan:
 
     def __init__(self, q_ranges, k_ranges, mask_types, total_q: int, total_k: int, heads_q: int,
                  heads_kv: int, head_dim: int, split_tiles: int = 0, max_splits: int = 0,
-                 num_cus: int = 0, natural_order: bool = False):
+                 num_cus: int = 0, natural_order: bool = False, backward: bool = False):
         lib = load_library()
         qr = _host_i32(q_ranges, (2,))
         kr = _host_i32(k_ranges, (2,))
@@ -174,7 +197,9 @@ class Plan:
         self.q_ranges, self.k_ranges, self.mask_types = qr, kr, ty
         self.total_q, self.total_k = int(total_q), int(total_k)
         self.heads_q, self.heads_kv, self.head_dim = int(heads_q), int(heads_kv), int(head_dim)
-        opts = PlanOpts(int(split_tiles), int(max_splits), int(num_cus), 1 if natural_order else 0)
+        self.backward = bool(backward)
+        flags = (PLAN_NATURAL_ORDER if natural_order else 0) | (PLAN_BACKWARD if backward else 0)
+        opts = PlanOpts(int(split_tiles), int(max_splits), int(num_cus), flags)
         h = _vp()
         st = lib.ffa_plan(qr.ctypes.data if qr.size else None, kr.ctypes.data if kr.size else None,
                           ty.ctypes.data if ty.size else None, int(qr.shape[0]), self.total_q, self.total_k,
@@ -186,6 +211,7 @@ class Plan:
         self.info = {name: getattr(inf, name) for name, _ in PlanInfo._fields_}
         self._meta = {}  # device index -> torch int32 tensor
         self._ws = {}    # device index -> torch uint8 tensor
+        self._bws = {}   # device index -> torch uint8 tensor (backward)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -235,15 +261,30 @@ class Plan:
         return t, need
 
 
+    def bwd_workspace(self, device, batch: int = 1):
+        import torch
+
+        need = int(self.info["bwd_workspace_bytes"]) * int(batch)
+        if need == 0:
+            return None, 0
+        dev = torch.device(device)
+        key = dev.index if dev.index is not None else torch.cuda.current_device()
+        t = self._bws.get(key)
+        if t is None or t.numel() < need:
+            t = torch.empty(need, dtype=torch.uint8, device=torch.device("cuda", key))
+            self._bws[key] = t
+        return t, need
+
+
 _plan_cache: "OrderedDict[tuple, Plan]" = OrderedDict()
 _PLAN_CACHE_MAX = 16
 
 
-def _cached_plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles) -> Plan:
-    key = (qr.tobytes(), kr.tobytes(), ty.tobytes(), tq, tk, hq, hkv, d, split_tiles)
+def _cached_plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles, backward: bool = False) -> Plan:
+    key = (qr.tobytes(), kr.tobytes(), ty.tobytes(), tq, tk, hq, hkv, d, split_tiles, bool(backward))
     p = _plan_cache.get(key)
     if p is None:
-        p = Plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles=split_tiles)
+        p = Plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles=split_tiles, backward=backward)
         _plan_cache[key] = p
         if len(_plan_cache) > _PLAN_CACHE_MAX:
             _plan_cache.popitem(last=False)
@@ -330,6 +371,120 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
     }
     run_fwd(plan, q, k, v, out, lse, strides, 1, scale)
     return out, lse
+
+
+def run_bwd(plan: Plan, t: dict, strides: dict, batch: int, softmax_scale: float):
+    """Call ffa_bwd.  t: tensors q k v out lse dout dq dk dv; strides: (sb, st, sh) each."""
+    import torch
+
+    if not plan.backward:
+        raise ValueError("the plan was built without backward=True")
+    dev = t["q"].device
+    s = torch.cuda.current_stream(dev)
+    meta = plan.device_meta(dev, s)
+    ws, ws_bytes = plan.bwd_workspace(dev, batch)
+    lib = load_library()
+    args = []
+    for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"):
+        args += [t[name].data_ptr(), *strides[name]]
+    st = lib.ffa_bwd(plan.handle, meta.data_ptr(), int(batch), *args, float(softmax_scale),
+                     ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
+    _check(st, "ffa_bwd")
+
+
+def _thd_strides(x):
+    return (0, x.stride(0), x.stride(1))
+
+
+def flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map,
+                        softmax_scale: Optional[float] = None, plan: Optional[Plan] = None):
+    """Gradients (dq, dk, dv) of flex_flash_attn_fwd for the upstream gradient dout.
+
+    q [Tq,Hq,D], k/v [Tk,Hkv,D], out/dout [Tq,Hq,D] bf16 and lse [Tq,Hq] fp32
+    (the forward's outputs) on the device; returns bf16 tensors shaped like
+    q, k and v.  Every step runs in the library's HIP kernels.
+    """
+    import torch
+
+    for name, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _require_bf16_cuda(name, x, 3)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape or k.shape[2] != d:
+        raise ValueError("shape mismatch")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (tq, hq) or lse.device != q.device:
+        raise ValueError("lse must be float32 [Tq, Hq] on the device of q")
+    if plan is None:
+        plan = _cached_plan(_host_i32(q_ranges, (2,)), _host_i32(k_ranges, (2,)), _host_i32(attn_type_map, ()),
+                            tq, tk, hq, hkv, d, 0, backward=True)
+    elif (plan.total_q, plan.total_k, plan.heads_q, plan.heads_kv, plan.head_dim) != (tq, tk, hq, hkv, d):
+        raise ValueError("plan was built for another shape")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    dk = torch.empty((tk, hkv, d), dtype=torch.bfloat16, device=q.device)
+    dv = torch.empty((tk, hkv, d), dtype=torch.bfloat16, device=q.device)
+    t = {"q": q, "k": k, "v": v, "out": out, "lse": lse, "dout": dout, "dq": dq, "dk": dk, "dv": dv}
+    strides = {n: _thd_strides(x) for n, x in t.items()}
+    run_bwd(plan, t, strides, 1, scale)
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class _FlexAttn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, plan, scale):
+            tq, hq, d = q.shape
+            out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+            lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+            strides = {"q": _thd_strides(q), "k": _thd_strides(k), "v": _thd_strides(v),
+                       "out": _thd_strides(out), "lse": _thd_strides(lse)}
+            run_fwd(plan, q, k, v, out, lse, strides, 1, scale)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.plan, ctx.scale = plan, scale
+            ctx.mark_non_differentiable(lse)
+            return out, lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            q, k, v, out, lse = ctx.saved_tensors
+            if dout.stride(-1) != 1 or dout.dtype != torch.bfloat16:
+                dout = dout.to(torch.bfloat16).contiguous()
+            dq, dk, dv = flex_flash_attn_bwd(dout, q, k, v, out, lse, None, None, None, ctx.scale, plan=ctx.plan)
+            return dq, dk, dv, None, None
+
+    return _FlexAttn
+
+
+_FLEX_FN = None
+
+
+def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
+                         softmax_scale: Optional[float] = None, softcap: float = 0.0):
+    """Differentiable flexible-mask attention -> (out, lse).
+
+    Same arguments and results as flex_flash_attn_fwd; gradients flow to q, k
+    and v through out (lse is returned without a gradient).  The backward runs
+    ffa_bwd on a plan built with the backward worklists.
+    """
+    global _FLEX_FN
+    if sink is not None:
+        raise NotImplementedError("attention sink is not supported")
+    if softcap:
+        raise NotImplementedError("softcap is not supported")
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _require_bf16_cuda(name, x, 3)
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    if v.shape != k.shape or dk != d:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    plan = _cached_plan(_host_i32(q_ranges, (2,)), _host_i32(k_ranges, (2,)), _host_i32(attn_type_map, ()),
+                        tq, tk, hq, hkv, d, 0, backward=True)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if _FLEX_FN is None:
+        _FLEX_FN = _autograd_function()
+    return _FLEX_FN.apply(q, k, v, plan, scale)
 
 
 def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = None, dropout_p: float = 0.0,

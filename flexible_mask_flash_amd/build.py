@@ -11,13 +11,14 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libffa.so")
 ARCH = "gfx950"
 
-SOURCES = ["ffa_plan.cpp", "ffa_fwd.hip"]
+SOURCES = ["ffa_plan.cpp", "ffa_fwd.hip", "ffa_bwd.hip"]
 
 # Packed fp32 VALU ops are disabled: the compiler must not form v_pk_{add,mul,fma}_f32.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans"]
@@ -37,6 +38,7 @@ def build(verbose: bool = False, asm: bool = False) -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
+    jobs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(bdir, src + ".o")
@@ -46,11 +48,15 @@ def build(verbose: bool = False, asm: bool = False) -> str:
         else:
             cmd += ["-x", "c++"]
         cmd += ["-c", path, "-o", obj]
-        _run(cmd, verbose)
+        jobs.append(cmd)
         objs.append(obj)
         if asm and src.endswith(".hip"):
             s_out = os.path.join(bdir, src + f".{ARCH}.s")
-            _run([cc, *common, *DEVICE_FLAGS, "--cuda-device-only", "-S", path, "-o", s_out], verbose)
+            jobs.append([cc, *common, *DEVICE_FLAGS, "--cuda-device-only", "-S", path, "-o", s_out])
+    # the sources compile independently
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 4)) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for cmd in jobs]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

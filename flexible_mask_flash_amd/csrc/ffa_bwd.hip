@@ -1,0 +1,641 @@
+// gfx950 (MI355X) kernels and the C ABI call of the flexible-mask attention backward.
+//
+// With P = exp(scale q.k - lse) over the visible keys (the forward's weights,
+// rebuilt from its lse) and an upstream gradient dO, the gradients follow from
+// the softmax Jacobian:
+//   dP = dO V^T,  dS = P * (dP - Dd) with Dd = rowsum(dO * O),
+//   dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q
+// (both pages present the forward as a differentiable training operator:
+// MagiAttention quickstart, "Single-GPU Flex-Flash-Attention"; FlagAttention
+// user guide, "FlashAttention").
+//
+// Three kernels, all on the caller's stream, no atomics (results are bitwise
+// reproducible):
+//   ffa_bwd_pre          Dd and lse * log2 e per (head, row) into the workspace
+//   ffa_bwd_main<D, 0>   dQ, query-major: a workgroup owns the rows of one
+//                        forward item (unsplit) and walks its key tiles
+//   ffa_bwd_main<D, 1>   dK and dV, key-major: a workgroup owns 128 keys of one
+//                        kv head and walks the query tiles of the transposed
+//                        slices once per query head of that kv head
+// Both main kernels are one template: a lane owns one "row" (a query for dQ, a
+// key for dK/dV) whose two operand fragments stay in registers (q and dO, or k
+// and v), and 64-row tiles of the other side stream through LDS (k and v, or q
+// and dO), double-buffered and filled by global_load_lds.  Per tile:
+//   X1 = A F1^T, X2 = B F2^T       (v_mfma_f32_32x32x16_bf16, A/B rows from LDS)
+//   P = exp2(X1 c2 - L), dS = P (X2 - Dd)   (fp32)
+//   acc1 += A^T dS  (dQ^T or dK^T),  acc2 += B^T P  (dV^T, key-major only)
+// with A^T / B^T read from LDS by ds_read_b64_tr_b16.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <type_traits>
+
+#include "ffa_device.h"
+
+namespace {
+
+using namespace ffa::dev;
+using ffa::kBlockN;
+using ffa::kItemRec;
+using ffa::kRec;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct PreArgs {
+  const __bf16* out;
+  const __bf16* dout;
+  const float* lse;
+  float* lw;  // [batch][heads_q][total_q]
+  float* dw;  // [batch][heads_q][total_q]
+  int64_t o_sb, o_st, o_sh;
+  int64_t d_sb, d_st, d_sh;
+  int64_t l_sb, l_st, l_sh;
+  int32_t total_q, heads_q;
+};
+
+struct BwdArgs {
+  const int32_t* items;
+  const int32_t* runs;
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dout;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  int64_t q_sb, q_st, q_sh;
+  int64_t k_sb, k_st, k_sh;
+  int64_t v_sb, v_st, v_sh;
+  int64_t d_sb, d_st, d_sh;
+  int64_t dq_sb, dq_st, dq_sh;
+  int64_t dk_sb, dk_st, dk_sh;
+  int64_t dv_sb, dv_st, dv_sh;
+  const float* lw;
+  const float* dw;
+  float scale_log2;  // softmax_scale * log2(e)
+  float scale;
+  int32_t total_q, total_k, heads_q, batch;
+  int32_t heads_per_item;  // query heads per query-major item
+  int32_t kv_ratio;        // heads_q / heads_kv
+};
+
+// Dd[b,h,t] = sum_d dO[b,t,h,d] O[b,t,h,d] (fp32 from the bf16 values) and
+// L[b,h,t] = lse * log2 e, with +inf for rows that see no key (their P is 0).
+template <int D>
+__global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
+  constexpr int TPP = D / 8;      // lanes per (row, head), 8 values each
+  constexpr int PPB = 256 / TPP;  // (row, head) pairs per workgroup
+  const int b = blockIdx.y;
+  const int64_t pairs = (int64_t)a.total_q * a.heads_q;
+  const int64_t p = (int64_t)blockIdx.x * PPB + threadIdx.x / TPP;
+  const int c = threadIdx.x % TPP;
+  float acc = 0.0f;
+  int64_t t = 0;
+  int h = 0;
+  if (p < pairs) {
+    t = p / a.heads_q;
+    h = (int)(p - t * a.heads_q);
+    const bf16x8_t o = *reinterpret_cast<const bf16x8_t*>(a.out + (int64_t)b * a.o_sb + t * a.o_st +
+                                                          (int64_t)h * a.o_sh + c * 8);
+    const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(a.dout + (int64_t)b * a.d_sb + t * a.d_st +
+                                                          (int64_t)h * a.d_sh + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int m = TPP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (p < pairs && c == 0) {
+    const int64_t idx = ((int64_t)b * a.heads_q + h) * a.total_q + t;
+    a.dw[idx] = acc;
+    const float l = a.lse[(int64_t)b * a.l_sb + t * a.l_st + (int64_t)h * a.l_sh];
+    a.lw[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// LDS swizzle of tiles that are read both as MFMA A rows (16 consecutive rows,
+// one 16-byte chunk each) and transposed (4 consecutive rows, two chunks, per
+// 16-lane group): the XOR spreads both patterns over all bank groups, and it is
+// the same for rows r and r + 16, so tiles can be addressed with compile-time
+// row offsets in steps of 16 (the rows r + 8 get their own address).
+template <int D>
+__device__ __forceinline__ int swz_b(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+template <int D, bool KV>
+__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffa_bwd_main(BwdArgs a) {
+  constexpr int BN = kBlockN;          // 64 rows per streamed tile
+  constexpr int ROWB = D * 2;          // bytes of one row
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int KSTEPS = D / 16;       // MFMA k-steps over the head dim
+  constexpr int DBLK = D / 32;         // 32-wide head-dim blocks of the accumulators
+  constexpr int TILE = BN * ROWB;      // bytes of one streamed tile
+  constexpr int W = ffa::kWaves;
+  constexpr int NLD = TILE / (1024 * W);  // DMA instructions per thread per tile
+  constexpr int RPL = 1024 * W / ROWB;    // rows between consecutive DMA instructions
+  static_assert(NLD * 1024 * W == TILE, "DMA split");
+  static_assert(BN == 64 && (D == 64 || D == 128), "tile shape");
+  // LDS: A0 | B0 | A1 | B1 (double-buffered tiles), then (key-major) L and Dd of
+  // the 64 streamed rows per buffer, 1 KiB each (one DMA instruction writes
+  // 64 x 16 bytes; the first 256 count).  The L / Dd block has its own base
+  // address so that every read offset fits the 16-bit immediate.
+  constexpr int BUFB = 2 * TILE;
+  constexpr int LDB = KV ? 2048 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUFB + 2 * LDB];
+
+  const int bid = blockIdx.x;
+  const int item_idx = bid / a.batch;
+  const int b = bid - item_idx * a.batch;
+  const FFA_CONST int32_t* itp = (const FFA_CONST int32_t*)(a.items + (int64_t)item_idx * kItemRec);
+  const int r0 = itp[0], nrows = itp[1], h0 = itp[2], run_off = itp[3], n_runs = itp[4];
+  const int total_tiles = itp[6];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int G = KV ? 1 : a.heads_per_item;
+  const int g = wave % G, rsub = wave / G;
+  const int lrow = rsub * 32 + (lane & 31);
+  const int row = r0 + lrow;
+  const bool row_ok = lrow < nrows;
+  const int hk = KV ? h0 : h0 / a.kv_ratio;  // kv head
+  const int hq = h0 + g;                     // query head of the row (query-major)
+
+  // ---- the row's fragments (B operands, head-dim half hh): q and dO, or k and v
+  bf16x8_t f1[KSTEPS], f2[KSTEPS];
+  {
+    const __bf16* p1 = KV ? a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh + (int64_t)row * a.k_st
+                          : a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)row * a.q_st;
+    const __bf16* p2 = KV ? a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh + (int64_t)row * a.v_st
+                          : a.dout + (int64_t)b * a.d_sb + (int64_t)hq * a.d_sh + (int64_t)row * a.d_st;
+    const bool load = row_ok && n_runs > 0;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      if (load) {
+        f1[s] = reinterpret_cast<const bf16x8_t*>(p1 + hh * (D / 2))[s];
+        f2[s] = reinterpret_cast<const bf16x8_t*>(p2 + hh * (D / 2))[s];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          f1[s][j] = (__bf16)0.0f;
+          f2[s][j] = (__bf16)0.0f;
+        }
+      }
+    }
+  }
+  // query-major: the row's L and Dd are per lane
+  float l_row = 0.0f, d_row = 0.0f;
+  if (!KV && row_ok && n_runs > 0) {
+    const int64_t idx = ((int64_t)b * a.heads_q + hq) * a.total_q + row;
+    l_row = a.lw[idx];
+    d_row = a.dw[idx];
+  }
+
+  f32x16_t acc1[DBLK], acc2[KV ? DBLK : 1];
+#pragma unroll
+  for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc1[d][i] = 0.0f;
+#pragma unroll
+  for (int d = 0; d < (KV ? DBLK : 1); ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc2[d][i] = 0.0f;
+
+  // ---- per-lane LDS read addresses (the low 10 bits of the LDS base are zero)
+  const uint32_t lds = (uint32_t)(uintptr_t)(FFA_LDS char*)smem;
+  // A operand rows: row (lane & 31) (+32 for the second block), chunk (D/16) hh + s
+  uint32_t r_addr[KSTEPS];
+  {
+    const int r = lane & 31;
+    const uint32_t a0 = lds + r * ROWB + ((((D / 16) * hh) ^ swz_b<D>(r)) << 4);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) r_addr[s] = a0 ^ (s << 4);
+  }
+  // transposed reads of head-dim block d: rows 4 hh + j/4 (lo) and 8 + 4 hh + j/4
+  // (hi), +16 t; columns 32 d + 16 (grp & 1) + 4 (j & 3)
+  uint32_t t_lo[DBLK], t_hi[DBLK];
+  {
+    const int grp = lane >> 4, jl = lane & 15;
+    const int vr = 4 * hh + (jl >> 2);
+    const int cl = 2 * (grp & 1) + ((jl & 3) >> 1);
+    const uint32_t lo = lds + vr * ROWB + ((cl ^ swz_b<D>(vr)) << 4) + (jl & 1) * 8;
+    const uint32_t hi = lds + (vr + 8) * ROWB + ((cl ^ swz_b<D>(vr + 8)) << 4) + (jl & 1) * 8;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d) {
+      t_lo[d] = lo ^ (d << 6);
+      t_hi[d] = hi ^ (d << 6);
+    }
+  }
+  // key-major: L / Dd of rows 32 blk + 8 gq + 4 hh .. +3 are one 16-byte read
+  const uint32_t ld_addr = lds + 2 * BUFB + 16 * hh;
+
+  // ---- DMA of a streamed tile: as in the forward, instruction i of wave w fills
+  // LDS block (W i + w); lane l's 16 bytes are chunk (lin % CH) of row (lin / CH),
+  // loaded from the swizzled global chunk.  Rows past `total` re-read the last
+  // row (their scores are masked).
+  const int lin0 = wave * 64 + lane;
+  const int dr0 = lin0 / CH, dp = lin0 % CH;
+  const int sw0 = swz_b<D>(dr0);
+  auto dma = [&](const char* base, int64_t st_b, int dst_off, int kstart, int total) {
+    if (kstart + BN <= total) {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kstart * st_b), (short)0, 0x7fffffff, kBufferFlags);
+      const uint32_t goff = (uint32_t)(dr0 * st_b) + ((dp ^ sw0) << 4);
+      uint32_t ldst = (uint32_t)(uintptr_t)(FFA_LDS char*)smem + dst_off + wave * 1024;
+      int32_t rstep = (int32_t)(RPL * st_b);
+      asm volatile("" : "+s"(ldst), "+s"(rstep));
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(uintptr_t)(ldst + i * W * 1024), 16, goff,
+                                                 i * rstep, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int r = min(kstart + dr0 + i * RPL, total - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)r * st_b + ((dp ^ sw0) << 4)),
+                                         (FFA_LDS void*)(smem + dst_off + (i * W + wave) * 1024), 16, 0, 0);
+      }
+    }
+  };
+  // key-major: L and Dd of the 64 streamed queries, one DMA instruction each
+  // (wave 0; lanes 16-63 repeat lanes 0-15 into padding).  Reads past total_q
+  // return zeros (the buffer's size ends there).
+  auto dma_ld = [&](int dst_off, int head, int kstart) {
+    if (wave == 0) {
+      const int64_t rowoff = ((int64_t)b * a.heads_q + head) * a.total_q + kstart;
+      const int nrec = max(0, a.total_q - kstart) * 4;
+      const __amdgpu_buffer_rsrc_t rl =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.lw + rowoff), (short)0, nrec, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rd =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.dw + rowoff), (short)0, nrec, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FFA_LDS void*)(smem + dst_off), 16, (lane & 15) * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FFA_LDS void*)(smem + dst_off + 1024), 16, (lane & 15) * 16, 0,
+                                               0, 0);
+    }
+  };
+
+  // ---- X = T F^T for the streamed tile T at LDS offset OFF: two 32-row blocks
+  // (xa, xb); hook(m) runs after the m-th MFMA is issued
+  auto rowprod = [&](auto off_tag, const bf16x8_t(&f)[KSTEPS], f32x16_t& xa, f32x16_t& xb, auto&& hook) {
+    constexpr int OFF = decltype(off_tag)::value;
+    constexpr int NQ = 2 * KSTEPS;
+    constexpr int KIF = 4;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { xa[i] = 0.0f; xb[i] = 0.0f; }
+    f32x4_t rf[KIF];
+    static_for<KIF>([&](auto m_tag) {
+      constexpr int m = decltype(m_tag)::value;
+      rf[m] = lds_read_b128<OFF + (m % 2) * 32 * ROWB>(r_addr[m / 2]);
+    });
+    static_for<NQ>([&](auto m_tag) {
+      constexpr int m = decltype(m_tag)::value;
+      constexpr int later = (m + KIF - 1 < NQ - 1) ? KIF - 1 : NQ - 1 - m;
+      lds_wait<later>();
+      fence(rf[m % KIF]);
+      if constexpr (m % 2 == 0)
+        xa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(rf[m % KIF]), f[m / 2], xa, 0, 0, 0);
+      else
+        xb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(rf[m % KIF]), f[m / 2], xb, 0, 0, 0);
+      if constexpr (m + KIF < NQ) {
+        constexpr int r = m + KIF;
+        rf[m % KIF] = lds_read_b128<OFF + (r % 2) * 32 * ROWB>(r_addr[r / 2]);
+      }
+      hook(std::integral_constant<int, m>{});
+    });
+  };
+
+  // ---- acc^T += T^T X for the streamed tile T at LDS offset OFF (16 rows per
+  // MFMA, the reads of step t+1 in flight during the MFMAs of step t)
+  auto trprod = [&](auto off_tag, const bf16x8_t(&xf)[4], f32x16_t(&acc)[DBLK]) {
+    constexpr int OFF = decltype(off_tag)::value;
+    s16x4_t vlo[2][DBLK], vhi[2][DBLK];
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d) {
+      vlo[0][d] = lds_read_tr16<OFF>(t_lo[d]);
+      vhi[0][d] = lds_read_tr16<OFF>(t_hi[d]);
+    }
+    static_for<4>([&](auto t_tag) {
+      constexpr int t = decltype(t_tag)::value;
+      constexpr int cur = t & 1, nxt = cur ^ 1;
+      if constexpr (t + 1 < 4) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) {
+          vlo[nxt][d] = lds_read_tr16<OFF + 16 * (t + 1) * ROWB>(t_lo[d]);
+          vhi[nxt][d] = lds_read_tr16<OFF + 16 * (t + 1) * ROWB>(t_hi[d]);
+        }
+      }
+      constexpr int ahead = (t + 1 < 4) ? 2 * DBLK : 0;
+      static_for<DBLK>([&](auto d_tag) {
+        constexpr int d = decltype(d_tag)::value;
+        lds_wait<2 * (DBLK - 1 - d) + ahead>();
+        fence(vlo[cur][d]);
+        fence(vhi[cur][d]);
+        const s16x8_t vv = {vlo[cur][d][0], vlo[cur][d][1], vlo[cur][d][2], vlo[cur][d][3],
+                            vhi[cur][d][0], vhi[cur][d][1], vhi[cur][d][2], vhi[cur][d][3]};
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), xf[t], acc[d], 0, 0, 0);
+      });
+    });
+  };
+
+  // edge mask: streamed position j (absolute) is visible from the lane's row iff
+  // row + lo_base <= j < min(k_hi, row + edge_base)
+  auto mask = [&](const TileIt& t, f32x16_t& xa, f32x16_t& xb) {
+    const int base = t.kstart() + 4 * hh;
+    const int lim = min(t.khi, row + t.eb) - base;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rel = 8 * (i >> 2) + (i & 3);
+      if (rel >= lim) xa[i] = -INFINITY;
+      if (rel + 32 >= lim) xb[i] = -INFINITY;
+    }
+    if (t.lb != -ffa::kNoEdge) {
+      const int low = row + t.lb - base;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rel = 8 * (i >> 2) + (i & 3);
+        if (rel < low) xa[i] = -INFINITY;
+        if (rel + 32 < low) xb[i] = -INFINITY;
+      }
+    }
+  };
+
+  const float c2 = a.scale_log2;
+  const FFA_CONST int32_t* rp = (const FFA_CONST int32_t*)(a.runs + (int64_t)run_off * kRec);
+  const int64_t ast_b = KV ? a.q_st * 2 : a.k_st * 2;
+  const int64_t bst_b = KV ? a.d_st * 2 : a.v_st * 2;
+  const int total = KV ? a.total_q : a.total_k;
+  // streamed tensors of a query head (key-major) or of the kv head (query-major)
+  auto a_base = [&](int head) -> const char* {
+    return KV ? (const char*)(a.q + (int64_t)b * a.q_sb + (int64_t)head * a.q_sh)
+              : (const char*)(a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh);
+  };
+  auto b_base = [&](int head) -> const char* {
+    return KV ? (const char*)(a.dout + (int64_t)b * a.d_sb + (int64_t)head * a.d_sh)
+              : (const char*)(a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
+  };
+
+  // one step: a tile of the runs for one query head (key-major: every tile of
+  // the item once per query head of the kv head)
+  struct Step {
+    TileIt t;
+    int head, jt;
+  };
+  const int heads_per_step = KV ? a.kv_ratio : 1;
+  const int steps = total_tiles * heads_per_step;
+  auto load = [&](auto buf_tag, const Step& s) {
+    constexpr int OB = decltype(buf_tag)::value * BUFB;
+    dma(a_base(s.head), ast_b, OB, s.t.kstart(), total);
+    dma(b_base(s.head), bst_b, OB + TILE, s.t.kstart(), total);
+    if constexpr (KV) dma_ld(2 * BUFB + decltype(buf_tag)::value * LDB, s.head, s.t.kstart());
+  };
+  auto advance = [&](Step& s) {
+    if (++s.jt >= total_tiles) {
+      s.jt = 0;
+      ++s.head;
+      tile_first(s.t, itp + 8);
+    } else {
+      tile_next(s.t, rp, n_runs);
+    }
+  };
+
+  auto compute = [&](auto buf_tag, const Step& s) {
+    constexpr int OA = decltype(buf_tag)::value * BUFB;
+    constexpr int OB = OA + TILE;
+    constexpr int OL = decltype(buf_tag)::value * LDB;  // relative to ld_addr
+    f32x16_t xa, xb, ya, yb;
+    // key-major: this tile's L and Dd for the lane's 32 elements
+    f32x4_t lv[8], dv[8];
+    if constexpr (KV) {
+      static_for<8>([&](auto i_tag) {
+        constexpr int i = decltype(i_tag)::value;  // block i / 4, group i % 4
+        lv[i] = lds_read_b128<OL + ((i >> 2) * 32 + (i & 3) * 8) * 4>(ld_addr);
+        dv[i] = lds_read_b128<OL + 1024 + ((i >> 2) * 32 + (i & 3) * 8) * 4>(ld_addr);
+      });
+    }
+    rowprod(std::integral_constant<int, OA>{}, f1, xa, xb, [](auto) {});
+    if constexpr (KV) {
+      lds_wait<0>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        fence(lv[i]);
+        fence(dv[i]);
+      }
+    }
+    if (s.t.edge()) mask(s.t, xa, xb);
+    // P = exp2(X1 c2 - L) in place, between the MFMAs of X2
+    auto lval = [&](int e) -> float { return KV ? lv[e >> 2][e & 3] : l_row; };
+    auto dval = [&](int e) -> float { return KV ? dv[e >> 2][e & 3] : d_row; };
+    constexpr int EPQ = 32 / (2 * KSTEPS);  // score elements per MFMA of X2
+    rowprod(std::integral_constant<int, OB>{}, f2, ya, yb, [&](auto m_tag) {
+      constexpr int m = decltype(m_tag)::value;
+#pragma unroll
+      for (int e = EPQ * m; e < EPQ * (m + 1); ++e) {
+        if (e < 16) xa[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xa[e], c2, -lval(e)));
+        else xb[e - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(xb[e - 16], c2, -lval(e)));
+      }
+      fence(xa);
+      fence(xb);
+    });
+    // dS = P (X2 - Dd); bf16 operands of the transposed products
+    bf16x8_t pf[4], sf[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = 8 * t + u;
+        const float p = e < 16 ? xa[e] : xb[e - 16];
+        const float y = e < 16 ? ya[e] : yb[e - 16];
+        pf[t][u] = (__bf16)p;
+        sf[t][u] = (__bf16)(p * (y - dval(e)));
+      }
+    if constexpr (KV) trprod(std::integral_constant<int, OB>{}, pf, acc2);
+    trprod(std::integral_constant<int, OA>{}, sf, acc1);
+  };
+
+  if (steps > 0) {
+    Step cur;
+    tile_first(cur.t, itp + 8);
+    cur.head = KV ? hk * a.kv_ratio : hq;
+    cur.jt = 0;
+    load(std::integral_constant<int, 0>{}, cur);
+    auto iter = [&](auto buf_tag, int j) {
+      constexpr int P = decltype(buf_tag)::value;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      wg_barrier();
+      Step nxt = cur;
+      if (j + 1 < steps) {
+        advance(nxt);
+        load(std::integral_constant<int, 1 - P>{}, nxt);
+      }
+      compute(std::integral_constant<int, P>{}, cur);
+      cur = nxt;
+    };
+    int j = 0;
+    for (; j + 1 < steps; j += 2) {
+      iter(std::integral_constant<int, 0>{}, j);
+      iter(std::integral_constant<int, 1>{}, j + 1);
+    }
+    if (j < steps) iter(std::integral_constant<int, 0>{}, j);
+  }
+
+  // ---- epilogue: lane holds head-dim values 32 d + 8 gq + 4 hh + e of its row
+  if (row_ok) {
+    auto store = [&](__bf16* dst, const f32x16_t(&acc)[DBLK], float mul) {
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          bf16x4_t w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * gq + e] * mul);
+          *reinterpret_cast<bf16x4_t*>(dst + 32 * d + 8 * gq + 4 * hh) = w;
+        }
+    };
+    if constexpr (KV) {
+      store(a.dk + (int64_t)b * a.dk_sb + (int64_t)row * a.dk_st + (int64_t)hk * a.dk_sh, acc1, a.scale);
+      store(a.dv + (int64_t)b * a.dv_sb + (int64_t)row * a.dv_st + (int64_t)hk * a.dv_sh, acc2, 1.0f);
+    } else {
+      store(a.dq + (int64_t)b * a.dq_sb + (int64_t)row * a.dq_st + (int64_t)hq * a.dq_sh, acc1, a.scale);
+    }
+  }
+}
+
+}  // namespace
+
+static ffa_status hip_fail_b(hipError_t e, const char* what) {
+  return ffa::set_error(FFA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+extern "C" {
+
+ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const void* q, int64_t q_sb, int64_t q_st,
+                   int64_t q_sh, const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh, const void* v, int64_t v_sb,
+                   int64_t v_st, int64_t v_sh, const void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                   const float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh, const void* dout, int64_t d_sb,
+                   int64_t d_st, int64_t d_sh, void* dq, int64_t dq_sb, int64_t dq_st, int64_t dq_sh, void* dk,
+                   int64_t dk_sb, int64_t dk_st, int64_t dk_sh, void* dv, int64_t dv_sb, int64_t dv_st, int64_t dv_sh,
+                   float softmax_scale, void* d_workspace, size_t workspace_bytes, void* stream) {
+  ffa::clear_error();
+  if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
+  const ffa::Plan& p = plan->plan;
+  if (p.bwd_off == 0)
+    return ffa::set_error(FFA_ERR_ARG, "the plan has no backward worklists (plan with FFA_PLAN_BACKWARD)");
+  if (batch < 1) return ffa::set_error(FFA_ERR_ARG, "batch must be >= 1");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return ffa::set_error(FFA_ERR_ARG, "softmax_scale must be finite and > 0");
+  if (!d_meta) return ffa::set_error(FFA_ERR_NULL, "d_meta is NULL");
+  const bool has_q = p.total_q > 0, has_k = p.total_k > 0;
+  if (has_q && (!q || !out || !lse || !dout || !dq))
+    return ffa::set_error(FFA_ERR_NULL, "q, out, lse, dout and dq must be non-NULL");
+  if (has_k && (!k || !v || !dk || !dv)) return ffa::set_error(FFA_ERR_NULL, "k, v, dk and dv must be non-NULL");
+  const int64_t ws_need = (int64_t)batch * p.bwd_workspace_bytes();
+  if (ws_need > 0 && (!d_workspace || (int64_t)workspace_bytes < ws_need))
+    return ffa::set_error(FFA_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                                 " bytes, the backward needs " + std::to_string(ws_need));
+  auto al16 = [](const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; };
+  auto st8 = [](int64_t s) { return (s & 7) == 0; };
+  if ((has_q && (!al16(q) || !al16(out) || !al16(dout) || !al16(dq))) ||
+      (has_k && (!al16(k) || !al16(v) || !al16(dk) || !al16(dv))))
+    return ffa::set_error(FFA_ERR_ALIGN, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  const int64_t sts[] = {q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh, d_sb, d_st, d_sh,
+                         dq_sb, dq_st, dq_sh, dk_sb, dk_st, dk_sh, dv_sb, dv_st, dv_sh};
+  for (int64_t x : sts)
+    if (!st8(x)) return ffa::set_error(FFA_ERR_ALIGN, "bf16 tensor strides must be multiples of 8 elements");
+  // the kernels address one 64-row tile with 32-bit offsets
+  const int64_t lim = ((int64_t)1 << 31) / (2 * ffa::kBlockN);
+  if (std::llabs(k_st) >= lim || std::llabs(v_st) >= lim || std::llabs(q_st) >= lim || std::llabs(d_st) >= lim)
+    return ffa::set_error(FFA_ERR_ARG, "q / k / v / dout token strides must be below 2^24 elements");
+  if (((int64_t)p.num_dq_items + p.num_kv_items) * batch > INT32_MAX) return ffa::set_error(FFA_ERR_ARG, "grid too large");
+  if ((int64_t)p.total_q * p.heads_q > ((int64_t)INT32_MAX) * 16) return ffa::set_error(FFA_ERR_ARG, "grid too large");
+
+  hipStream_t s = (hipStream_t)stream;
+  float* lw = static_cast<float*>(d_workspace);
+  float* dwp = lw ? lw + (size_t)batch * p.heads_q * p.total_q : nullptr;
+  if (has_q) {
+    PreArgs pa;
+    pa.out = static_cast<const __bf16*>(out);
+    pa.dout = static_cast<const __bf16*>(dout);
+    pa.lse = lse;
+    pa.lw = lw;
+    pa.dw = dwp;
+    pa.o_sb = o_sb; pa.o_st = o_st; pa.o_sh = o_sh;
+    pa.d_sb = d_sb; pa.d_st = d_st; pa.d_sh = d_sh;
+    pa.l_sb = l_sb; pa.l_st = l_st; pa.l_sh = l_sh;
+    pa.total_q = p.total_q;
+    pa.heads_q = p.heads_q;
+    const int ppb = 256 / (p.head_dim / 8);
+    const int64_t pairs = (int64_t)p.total_q * p.heads_q;
+    const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL(ffa_bwd_pre<128>, grid, dim3(256), 0, s, pa);
+    else
+      hipLaunchKernelGGL(ffa_bwd_pre<64>, grid, dim3(256), 0, s, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_pre");
+  }
+
+  const int32_t* meta = static_cast<const int32_t*>(d_meta);
+  const int32_t* bw = meta + p.bwd_off + ffa::kBwdHdr;
+  const int32_t* dq_items = bw;
+  const int32_t* dq_runs = dq_items + (size_t)p.num_dq_items * kItemRec;
+  const int32_t* kv_items = dq_runs + (size_t)p.num_dq_runs * kRec;
+  const int32_t* kv_runs = kv_items + (size_t)p.num_kv_items * kItemRec;
+
+  BwdArgs ba;
+  ba.q = static_cast<const __bf16*>(q);
+  ba.k = static_cast<const __bf16*>(k);
+  ba.v = static_cast<const __bf16*>(v);
+  ba.dout = static_cast<const __bf16*>(dout);
+  ba.dq = static_cast<__bf16*>(dq);
+  ba.dk = static_cast<__bf16*>(dk);
+  ba.dv = static_cast<__bf16*>(dv);
+  ba.q_sb = q_sb; ba.q_st = q_st; ba.q_sh = q_sh;
+  ba.k_sb = k_sb; ba.k_st = k_st; ba.k_sh = k_sh;
+  ba.v_sb = v_sb; ba.v_st = v_st; ba.v_sh = v_sh;
+  ba.d_sb = d_sb; ba.d_st = d_st; ba.d_sh = d_sh;
+  ba.dq_sb = dq_sb; ba.dq_st = dq_st; ba.dq_sh = dq_sh;
+  ba.dk_sb = dk_sb; ba.dk_st = dk_st; ba.dk_sh = dk_sh;
+  ba.dv_sb = dv_sb; ba.dv_st = dv_st; ba.dv_sh = dv_sh;
+  ba.lw = lw;
+  ba.dw = dwp;
+  ba.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  ba.scale = softmax_scale;
+  ba.total_q = p.total_q;
+  ba.total_k = p.total_k;
+  ba.heads_q = p.heads_q;
+  ba.batch = batch;
+  ba.heads_per_item = p.heads_per_item;
+  ba.kv_ratio = p.heads_q / p.heads_kv;
+
+  const dim3 block(64 * ffa::kWaves);
+  if (p.num_dq_items > 0) {
+    ba.items = dq_items;
+    ba.runs = dq_runs;
+    const dim3 grid((unsigned)((int64_t)p.num_dq_items * batch));
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL((ffa_bwd_main<128, false>), grid, block, 0, s, ba);
+    else
+      hipLaunchKernelGGL((ffa_bwd_main<64, false>), grid, block, 0, s, ba);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dq)");
+  }
+  if (p.num_kv_items > 0) {
+    ba.items = kv_items;
+    ba.runs = kv_runs;
+    const dim3 grid((unsigned)((int64_t)p.num_kv_items * batch));
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL((ffa_bwd_main<128, true>), grid, block, 0, s, ba);
+    else
+      hipLaunchKernelGGL((ffa_bwd_main<64, true>), grid, block, 0, s, ba);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dk, dv)");
+  }
+  return FFA_OK;
+}
+
+}  // extern "C"

@@ -25,6 +25,19 @@
 // Combine: q0, nrows, h0, n_chunks, slot0, 0, 0, 0
 //          chunk c of row (q0 + r), head (h0 + g) is partial slot
 //          slot0 + c * kSlotsPerItem + r * heads_per_item + g.
+//
+// With FFA_PLAN_BACKWARD the same buffer continues (header[kHdrBwd] = offset
+// in int32 of this section) with the backward worklists:
+//
+//   bwd header [8]               n_dq_items, n_dq_runs, n_kv_items, n_kv_runs,
+//                                kv_rows_per_item, dq_heads_per_item, 0, 0
+//   dq items   [n_dq_items][16]  the forward's items without split (query-major)
+//   dq runs    [n_dq_runs][8]
+//   kv items   [n_kv_items][16]  key-major: q0/nrows are a key block, h0 is the
+//                                kv head; the item walks its runs once per query
+//                                head of that kv head
+//   kv runs    [n_kv_runs][8]    runs of the transposed slices: k0 / k_hi are
+//                                query positions and "row" is the key
 // A workgroup (kWaves wavefronts) covers kSlotsPerItem = 128 (row, head) pairs
 // that share one kv head: 32 rows x 4 heads, 64 x 2 or 128 x 1.
 #pragma once
@@ -49,8 +62,10 @@ constexpr int kHdr = 16;                // int32 in the header
 
 enum HeaderField {
   kHdrMagic = 0, kHdrVersion, kHdrItems, kHdrRuns, kHdrCombine, kHdrHeadsPerItem, kHdrRowsPerItem,
-  kHdrBlockN, kHdrHeadDim, kHdrHeadsQ, kHdrHeadsKv, kHdrTotalQ, kHdrTotalK, kHdrSlots
+  kHdrBlockN, kHdrHeadDim, kHdrHeadsQ, kHdrHeadsKv, kHdrTotalQ, kHdrTotalK, kHdrSlots, kHdrBwd
 };
+constexpr int kBwdHdr = 8;              // int32 in the backward section's header
+constexpr int32_t kKvRowsPerItem = kWaveRows * kWaves;  // keys per key-major backward item
 
 struct Plan {
   int32_t total_q = 0, total_k = 0, heads_q = 0, heads_kv = 0, head_dim = 0;
@@ -58,9 +73,14 @@ struct Plan {
   int32_t num_items = 0, num_runs = 0, num_combine = 0, num_split_items = 0;
   int32_t num_slots = 0, max_item_tiles = 0;
   int64_t visible_pairs = 0, computed_pairs = 0, total_tiles = 0;
-  std::vector<int32_t> meta;  // header + items + runs + combine
+  // backward worklists (bwd_off == 0: not planned)
+  int32_t bwd_off = 0, num_dq_items = 0, num_dq_runs = 0, num_kv_items = 0, num_kv_runs = 0;
+  int64_t dq_tiles = 0, kv_tiles = 0;
+  std::vector<int32_t> meta;  // header + items + runs + combine (+ backward section)
   int64_t meta_bytes() const { return (int64_t)meta.size() * 4; }
   int64_t workspace_bytes() const { return (int64_t)num_slots * (head_dim + 1) * 4; }
+  // backward: fp32 lse * log2 e and rowsum(dout * out) per (head, row)
+  int64_t bwd_workspace_bytes() const { return bwd_off ? (int64_t)2 * heads_q * total_q * 4 : 0; }
   const int32_t* items() const { return meta.data() + kHdr; }
   const int32_t* runs() const { return items() + (size_t)num_items * kItemRec; }
   const int32_t* combine() const { return runs() + (size_t)num_runs * kRec; }
@@ -78,3 +98,8 @@ void clear_error();
 const char* last_error();
 
 }  // namespace ffa
+
+// The opaque handle of the C ABI.
+struct ffa_plan_s {
+  ffa::Plan plan;
+};

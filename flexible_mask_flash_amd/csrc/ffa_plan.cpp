@@ -42,19 +42,43 @@ namespace ffa {
 namespace {
 thread_local std::string g_last_error;
 
+// A slice as a band: row i (qs <= i < qe) sees keys
+// [max(ks, i + lo_base), min(ke, i + edge_base)); lo_base = -kNoEdge and
+// edge_base = kNoEdge stand for "no bound".  The mask types of the interface
+// are the cases lo_base = ks - qs (bit 1 of the type) and edge_base = ke - qe + 1
+// (bit 0): the kv-interval formula of the MagiAttention blog page "Calculate
+// KV Interval Boundaries for Mask Types".  The transpose of a band (keys as
+// rows) is again a band, which is how the key-major backward worklist is made.
 struct Slice {
   int32_t qs, qe, ks, ke, type, id;
+  int32_t lo_base, edge_base;
+  bool has_lo() const { return lo_base != -kNoEdge; }
+  bool has_hi() const { return edge_base != kNoEdge; }
 };
 
-// Keys row i sees through slice s: [row_start, row_end) (the kv-interval
-// formula: bit 1 of the type moves the start by the row's offset from qs, bit 0
-// moves the end back by its distance to qe - 1).  Both are nondecreasing in i;
-// the interval may be empty.
+Slice make_slice(int32_t qs, int32_t qe, int32_t ks, int32_t ke, int32_t type, int32_t id) {
+  Slice s{qs, qe, ks, ke, type, id, -kNoEdge, kNoEdge};
+  if (type & 2) s.lo_base = ks - qs;
+  if (type & 1) s.edge_base = ke - qe + 1;
+  return s;
+}
+
+// Key j is visible from row i iff i + lo <= j < i + hi; with the key j as the
+// row, i runs over [j + 1 - hi, j + 1 - lo).
+Slice transpose(const Slice& s) {
+  Slice t{s.ks, s.ke, s.qs, s.qe, -1, s.id, -kNoEdge, kNoEdge};
+  if (s.has_hi()) t.lo_base = 1 - s.edge_base;
+  if (s.has_lo()) t.edge_base = 1 - s.lo_base;
+  return t;
+}
+
+// Keys row i sees through slice s: [row_start, row_end), clamped to [ks, ke]
+// (the interval may be empty).  Both are nondecreasing in i.
 inline int64_t row_start(const Slice& s, int64_t i) {
-  return (s.type & 2) ? (int64_t)s.ks + (i - s.qs) : (int64_t)s.ks;
+  return s.has_lo() ? std::max<int64_t>(s.ks, i + s.lo_base) : (int64_t)s.ks;
 }
 inline int64_t row_end(const Slice& s, int64_t i) {
-  return (s.type & 1) ? (int64_t)s.ke - ((int64_t)s.qe - 1 - i) : (int64_t)s.ke;
+  return s.has_hi() ? std::min<int64_t>(s.ke, i + s.edge_base) : (int64_t)s.ke;
 }
 
 int64_t slice_visible_pairs(const Slice& s) {
@@ -70,35 +94,46 @@ int64_t slice_visible_pairs(const Slice& s) {
   return (c + m0 + N) * (M - m0) / 2;
 }
 
+// Rows where a piecewise-linear row function built from the slices' bounds can
+// turn: where a bound that moves with the row (slope 1, i + c) meets a fixed
+// one (a range end); with the ends of [r0, r1] and their neighbours.
+void kink_rows(const Slice* const* sl, int n, int64_t r0, int64_t r1, std::vector<int64_t>& out) {
+  out.assign({r0, r1});
+  std::vector<int64_t> moving, fixed;
+  for (int x = 0; x < n; ++x) {
+    if (sl[x]->has_lo()) moving.push_back(sl[x]->lo_base);
+    if (sl[x]->has_hi()) moving.push_back(sl[x]->edge_base);
+    fixed.push_back(sl[x]->ks);
+    fixed.push_back(sl[x]->ke);
+  }
+  for (int64_t c : moving)
+    for (int64_t f : fixed)
+      for (int64_t d = -1; d <= 1; ++d) out.push_back(std::min(r1, std::max(r0, f - c + d)));
+}
+
 // Largest number of keys two slices share on one row over the rows both cover
 // (0: disjoint).  The shared count min(ends) - max(starts) is concave and
 // piecewise linear in the row (slopes 0 / 1), so its maximum lies at an end of
-// the shared rows or where two of the bounding lines cross.
+// the shared rows or where a moving bound meets a fixed one.
 int64_t max_shared_keys(const Slice& a, const Slice& b) {
   const int64_t r0 = std::max(a.qs, b.qs), r1 = std::min(a.qe, b.qe) - 1;
   if (r1 < r0) return 0;
-  auto shared = [&](int64_t i) {
-    const int64_t lo = std::max({row_start(a, i), row_start(b, i), (int64_t)a.ks, (int64_t)b.ks});
-    const int64_t hi = std::min({row_end(a, i), row_end(b, i), (int64_t)a.ke, (int64_t)b.ke});
-    return hi - lo;
-  };
-  // each bound is c + slope * i; crossings of two lines with different slopes
-  std::vector<int64_t> cand = {r0, r1};
-  const int64_t ca[4] = {row_start(a, 0), row_start(b, 0), row_end(a, 0), row_end(b, 0)};
-  const int64_t sl[4] = {(a.type & 2) ? 1 : 0, (b.type & 2) ? 1 : 0, (a.type & 1) ? 1 : 0, (b.type & 1) ? 1 : 0};
-  const int64_t cst[4] = {a.ks, b.ks, a.ke, b.ke};
-  for (int x = 0; x < 4; ++x) {
-    for (int y = 0; y < 4; ++y) {
-      if (sl[x] == 1 && sl[y] == 0) cand.push_back(ca[y] - ca[x]);       // line x meets line y
-      if (sl[x] == 1) cand.push_back(cst[x] - ca[x]);                    // line x meets its clamp
-    }
-  }
+  const Slice* both[2] = {&a, &b};
+  std::vector<int64_t> cand;
+  kink_rows(both, 2, r0, r1, cand);
   int64_t best = 0;
-  for (int64_t c : cand)
-    for (int64_t d = -1; d <= 1; ++d) {
-      const int64_t i = std::min(r1, std::max(r0, c + d));
-      best = std::max(best, shared(i));
-    }
+  for (int64_t i : cand)
+    best = std::max(best, std::min(row_end(a, i), row_end(b, i)) - std::max(row_start(a, i), row_start(b, i)));
+  return best;
+}
+
+// Largest number of keys one row of [r0, r1] sees through s (concave in the row).
+int64_t max_row_width(const Slice& s, int64_t r0, int64_t r1) {
+  const Slice* one[1] = {&s};
+  std::vector<int64_t> cand;
+  kink_rows(one, 1, r0, r1, cand);
+  int64_t best = 0;
+  for (int64_t i : cand) best = std::max(best, row_end(s, i) - row_start(s, i));
   return best;
 }
 
@@ -137,6 +172,61 @@ double lpt_makespan(std::vector<int64_t>& costs, int64_t slots) {
 }
 constexpr int64_t kMaxTokens = (int64_t)1 << 30;
 
+// Steps 1-3: q segments, q tiles of rows_per_item rows and their key runs.
+std::vector<QTile> make_tiles(const std::vector<Slice>& slices, int32_t total_rows, int32_t rows_per_item) {
+  std::vector<int32_t> bounds = {0, total_rows};
+  for (const Slice& s : slices) {
+    bounds.push_back(s.qs);
+    bounds.push_back(s.qe);
+  }
+  std::sort(bounds.begin(), bounds.end());
+  bounds.erase(std::unique(bounds.begin(), bounds.end()), bounds.end());
+
+  std::vector<int> by_qs(slices.size());
+  std::iota(by_qs.begin(), by_qs.end(), 0);
+  std::sort(by_qs.begin(), by_qs.end(), [&](int a, int b) { return slices[a].qs < slices[b].qs; });
+
+  std::vector<QTile> tiles;
+  std::vector<int> active;
+  size_t next_slice = 0;
+  for (size_t bi = 0; bi + 1 < bounds.size(); ++bi) {
+    const int32_t a = bounds[bi], b = bounds[bi + 1];
+    if (b <= a) continue;
+    while (next_slice < by_qs.size() && slices[by_qs[next_slice]].qs <= a) active.push_back(by_qs[next_slice++]);
+    active.erase(std::remove_if(active.begin(), active.end(), [&](int s) { return slices[s].qe <= a; }),
+                 active.end());
+    for (int32_t r0 = a; r0 < b; r0 += rows_per_item) {
+      QTile t;
+      t.q0 = r0;
+      t.nrows = std::min(rows_per_item, b - r0);
+      const int64_t r_last = (int64_t)r0 + t.nrows - 1;
+      for (int si : active) {
+        const Slice& s = slices[si];
+        // starts and ends are nondecreasing in the row: the tile sees
+        // [lo_first, e_last) in total and every row of it sees [lo_last, e_first)
+        if (max_row_width(s, r0, r_last) <= 0) continue;  // no row sees this slice
+        const int64_t lo_first = row_start(s, r0), lo_last = row_start(s, r_last);
+        const int64_t e_first = row_end(s, r0), e_last = row_end(s, r_last);
+        const int64_t t_first = (lo_first - s.ks) / kBlockN;  // tiles aligned to ks
+        const int64_t k0 = s.ks + t_first * kBlockN;
+        TileRun run;
+        run.k0 = (int32_t)k0;
+        run.n_tiles = (int32_t)((e_last - k0 + kBlockN - 1) / kBlockN);
+        run.n_lead = (int32_t)std::min<int64_t>(run.n_tiles, (std::max<int64_t>(lo_last - k0, 0) + kBlockN - 1) / kBlockN);
+        run.n_full = (int32_t)std::max<int64_t>(0, std::min<int64_t>(run.n_tiles, (e_first - k0) / kBlockN) - run.n_lead);
+        run.k_hi = s.ke;
+        run.edge_base = s.edge_base;
+        run.lo_base = s.lo_base;
+        t.runs.push_back(run);
+        t.tiles += run.n_tiles;
+      }
+      std::sort(t.runs.begin(), t.runs.end(), [](const TileRun& x, const TileRun& y) { return x.k0 < y.k0; });
+      tiles.push_back(std::move(t));
+    }
+  }
+  return tiles;
+}
+
 }  // namespace
 
 ffa_status set_error(ffa_status st, const std::string& msg) {
@@ -170,7 +260,8 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   slices.reserve(num_slices);
   int64_t visible = 0;
   for (int32_t s = 0; s < num_slices; ++s) {
-    Slice x{q_ranges[2 * s], q_ranges[2 * s + 1], k_ranges[2 * s], k_ranges[2 * s + 1], mask_types[s], s};
+    const Slice x = make_slice(q_ranges[2 * s], q_ranges[2 * s + 1], k_ranges[2 * s], k_ranges[2 * s + 1],
+                               mask_types[s], s);
     if (x.qs < 0 || x.qe > total_q || x.qs > x.qe)
       return set_error(FFA_ERR_RANGE, "slice " + std::to_string(s) + ": q_range [" + std::to_string(x.qs) + ", " +
                                           std::to_string(x.qe) + ") outside [0, " + std::to_string(total_q) + "]");
@@ -217,59 +308,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   const int32_t n_groups = heads_q / G;
 
   // ---------------------------------------------------------------- segments and q tiles
-  std::vector<int32_t> bounds = {0, total_q};
-  for (const Slice& s : slices) {
-    bounds.push_back(s.qs);
-    bounds.push_back(s.qe);
-  }
-  std::sort(bounds.begin(), bounds.end());
-  bounds.erase(std::unique(bounds.begin(), bounds.end()), bounds.end());
-
-  std::vector<int> by_qs(slices.size());
-  std::iota(by_qs.begin(), by_qs.end(), 0);
-  std::sort(by_qs.begin(), by_qs.end(), [&](int a, int b) { return slices[a].qs < slices[b].qs; });
-
-  std::vector<QTile> tiles;
-  std::vector<int> active;
-  size_t next_slice = 0;
-  for (size_t bi = 0; bi + 1 < bounds.size(); ++bi) {
-    const int32_t a = bounds[bi], b = bounds[bi + 1];
-    if (b <= a) continue;
-    while (next_slice < by_qs.size() && slices[by_qs[next_slice]].qs <= a) active.push_back(by_qs[next_slice++]);
-    active.erase(std::remove_if(active.begin(), active.end(), [&](int s) { return slices[s].qe <= a; }),
-                 active.end());
-    for (int32_t r0 = a; r0 < b; r0 += rows_per_item) {
-      QTile t;
-      t.q0 = r0;
-      t.nrows = std::min(rows_per_item, b - r0);
-      const int64_t r_last = (int64_t)r0 + t.nrows - 1;
-      for (int si : active) {
-        const Slice& s = slices[si];
-        // starts and ends are nondecreasing in the row, and so is neither width
-        // bound's direction: the tile sees [lo_first, e_last) in total, every
-        // row of it sees [lo_last, e_first), and a row sees something iff the
-        // wider of its first and last rows does
-        const int64_t lo_first = row_start(s, r0), lo_last = row_start(s, r_last);
-        const int64_t e_first = std::min<int64_t>(row_end(s, r0), s.ke);
-        const int64_t e_last = std::min<int64_t>(row_end(s, r_last), s.ke);
-        if (std::max(e_first - lo_first, e_last - lo_last) <= 0) continue;  // no row sees this slice
-        const int64_t t_first = (lo_first - s.ks) / kBlockN;                 // tiles aligned to ks
-        const int64_t k0 = s.ks + t_first * kBlockN;
-        TileRun run;
-        run.k0 = (int32_t)k0;
-        run.n_tiles = (int32_t)((e_last - k0 + kBlockN - 1) / kBlockN);
-        run.n_lead = (int32_t)std::min<int64_t>(run.n_tiles, (std::max<int64_t>(lo_last - k0, 0) + kBlockN - 1) / kBlockN);
-        run.n_full = (int32_t)std::max<int64_t>(0, std::min<int64_t>(run.n_tiles, (e_first - k0) / kBlockN) - run.n_lead);
-        run.k_hi = s.ke;
-        run.edge_base = (s.type & 1) ? s.ke - s.qe + 1 : kNoEdge;
-        run.lo_base = (s.type & 2) ? s.ks - s.qs : -kNoEdge;
-        t.runs.push_back(run);
-        t.tiles += run.n_tiles;
-      }
-      std::sort(t.runs.begin(), t.runs.end(), [](const TileRun& x, const TileRun& y) { return x.k0 < y.k0; });
-      tiles.push_back(std::move(t));
-    }
-  }
+  const std::vector<QTile> tiles = make_tiles(slices, total_q, rows_per_item);
 
   // ---------------------------------------------------------------- split-K decision
   // number of chunks of a q tile for a chunk target (0: no split)
@@ -386,7 +425,42 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
     });
   }
 
-  if (items.size() > (size_t)INT32_MAX / kItemRec || runs.size() > (size_t)INT32_MAX)
+  // ---------------------------------------------------------------- backward worklists
+  // dQ: the query-major tiles of the forward without split (a row's dQ sums
+  // over all its keys inside one workgroup).  dK / dV: the same construction on
+  // the transposed slices, one item per (key block, kv head); the item visits
+  // its query tiles once for each query head that shares the kv head.
+  std::vector<ItemRec> dq_items, kv_items;
+  std::vector<int32_t> dq_runs, kv_runs;
+  int64_t dq_tiles = 0, kv_tiles = 0;
+  const bool want_bwd = (flags & FFA_PLAN_BACKWARD) != 0;
+  if (want_bwd) {
+    auto emit = [&](const std::vector<QTile>& ts, int32_t n_heads, int32_t head_step, std::vector<ItemRec>& its,
+                    std::vector<int32_t>& rs, int64_t& total) {
+      for (const QTile& t : ts) {
+        const int32_t off = (int32_t)(rs.size() / kRec);
+        for (const TileRun& r : t.runs) {
+          const int32_t rec[kRec] = {r.k0, r.n_tiles, r.n_full, r.k_hi, r.edge_base, r.n_lead, r.lo_base, 0};
+          rs.insert(rs.end(), rec, rec + kRec);
+        }
+        for (int32_t g = 0; g < n_heads; ++g)
+          its.push_back({t.q0, t.nrows, g * head_step, off, (int32_t)t.runs.size(), -1, (int32_t)t.tiles});
+        total += t.tiles * n_heads;
+      }
+      if (!(flags & 1u))
+        std::stable_sort(its.begin(), its.end(), [](const ItemRec& x, const ItemRec& y) { return x.tiles > y.tiles; });
+    };
+    emit(tiles, n_groups, G, dq_items, dq_runs, dq_tiles);
+    std::vector<Slice> tr;
+    tr.reserve(slices.size());
+    for (const Slice& s : slices) tr.push_back(transpose(s));
+    emit(make_tiles(tr, total_k, kKvRowsPerItem), heads_kv, 1, kv_items, kv_runs, kv_tiles);
+    kv_tiles *= ratio;
+  }
+
+  if (items.size() > (size_t)INT32_MAX / kItemRec || runs.size() > (size_t)INT32_MAX ||
+      dq_items.size() + kv_items.size() > (size_t)INT32_MAX / kItemRec ||
+      dq_runs.size() + kv_runs.size() > (size_t)INT32_MAX)
     return set_error(FFA_ERR_ARG, "plan too large");
 
   Plan p;
@@ -409,8 +483,12 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   for (const ItemRec& it : items) max_item = std::max(max_item, it.tiles);
   p.max_item_tiles = max_item;
 
+  const size_t fwd_size = kHdr + items.size() * kItemRec + runs.size() + combine.size();
+  const size_t bwd_size =
+      want_bwd ? kBwdHdr + (dq_items.size() + kv_items.size()) * kItemRec + dq_runs.size() + kv_runs.size() : 0;
+  if (fwd_size + bwd_size > (size_t)INT32_MAX) return set_error(FFA_ERR_ARG, "plan too large");
   try {
-    p.meta.assign(kHdr + items.size() * kItemRec + runs.size() + combine.size(), 0);
+    p.meta.assign(fwd_size + bwd_size, 0);
   } catch (...) {
     return set_error(FFA_ERR_HOST_OOM, "host allocation of the plan failed");
   }
@@ -430,15 +508,35 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   h[kHdrTotalK] = total_k;
   h[kHdrSlots] = n_slots;
   int32_t* w = h + kHdr;
-  for (const ItemRec& it : items) {
-    int32_t rec[kItemRec] = {it.q0, it.nrows, it.h0, it.run_off, it.n_runs, it.slot, it.tiles, 0};
-    if (it.n_runs > 0) std::memcpy(rec + 8, runs.data() + (size_t)it.run_off * kRec, kRec * 4);
-    std::memcpy(w, rec, sizeof(rec));
-    w += kItemRec;
-  }
-  if (!runs.empty()) std::memcpy(w, runs.data(), runs.size() * 4);
-  w += runs.size();
+  // items (with the inline copy of their first run), then their runs
+  auto put_items = [&](const std::vector<ItemRec>& its, const std::vector<int32_t>& rs) {
+    for (const ItemRec& it : its) {
+      int32_t rec[kItemRec] = {it.q0, it.nrows, it.h0, it.run_off, it.n_runs, it.slot, it.tiles, 0};
+      if (it.n_runs > 0) std::memcpy(rec + 8, rs.data() + (size_t)it.run_off * kRec, kRec * 4);
+      std::memcpy(w, rec, sizeof(rec));
+      w += kItemRec;
+    }
+    if (!rs.empty()) std::memcpy(w, rs.data(), rs.size() * 4);
+    w += rs.size();
+  };
+  put_items(items, runs);
   if (!combine.empty()) std::memcpy(w, combine.data(), combine.size() * 4);
+  w += combine.size();
+  if (want_bwd) {
+    p.bwd_off = (int32_t)fwd_size;
+    p.num_dq_items = (int32_t)dq_items.size();
+    p.num_dq_runs = (int32_t)(dq_runs.size() / kRec);
+    p.num_kv_items = (int32_t)kv_items.size();
+    p.num_kv_runs = (int32_t)(kv_runs.size() / kRec);
+    p.dq_tiles = dq_tiles;
+    p.kv_tiles = kv_tiles;
+    h[kHdrBwd] = p.bwd_off;
+    const int32_t bh[kBwdHdr] = {p.num_dq_items, p.num_dq_runs, p.num_kv_items, p.num_kv_runs, kKvRowsPerItem, G, 0, 0};
+    std::memcpy(w, bh, sizeof(bh));
+    w += kBwdHdr;
+    put_items(dq_items, dq_runs);
+    put_items(kv_items, kv_runs);
+  }
   *plan = std::move(p);
   return FFA_OK;
 }

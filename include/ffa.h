@@ -27,6 +27,8 @@
  *   ffa_plan_export copy the same metadata to host memory (inspection, tests)
  *   ffa_fwd         run the forward on a stream (main kernel, then the split
  *                   combine when the plan has split rows)
+ *   ffa_bwd         gradients dq, dk, dv from the forward's out and lse and the
+ *                   upstream gradient dout (plan built with FFA_PLAN_BACKWARD)
  *   ffa_plan_destroy, ffa_status_string, ffa_last_error, ffa_abi_version
  *
  * Ownership.  The library owns only the host plan.  All device memory (meta,
@@ -49,12 +51,15 @@
 extern "C" {
 #endif
 
-#define FFA_ABI_VERSION 1
+#define FFA_ABI_VERSION 2
 
 #define FFA_MASK_FULL 0
 #define FFA_MASK_CAUSAL 1
 #define FFA_MASK_INVCAUSAL 2
 #define FFA_MASK_BICAUSAL 3
+
+#define FFA_PLAN_NATURAL_ORDER 1u
+#define FFA_PLAN_BACKWARD 2u
 
 typedef enum {
   FFA_OK = 0,
@@ -87,7 +92,9 @@ typedef struct {
   int32_t max_splits;
   /* Compute units to plan for (0: query the current HIP device). */
   int32_t num_cus;
-  /* Bit 0: keep items in natural order (no longest-first ordering). */
+  /* Bit 0 (FFA_PLAN_NATURAL_ORDER): keep items in natural order (no
+   * longest-first ordering).  Bit 1 (FFA_PLAN_BACKWARD): also plan the
+   * backward worklists that ffa_bwd needs. */
   uint32_t flags;
 } ffa_plan_opts;
 
@@ -106,6 +113,12 @@ typedef struct {
   int32_t block_n;           /* keys per tile                                               */
   int32_t max_item_tiles;    /* longest item, in key tiles                                  */
   int64_t total_tiles;       /* key tiles over all items                                    */
+  /* backward (zero unless the plan was built with FFA_PLAN_BACKWARD) */
+  int64_t bwd_workspace_bytes; /* ffa_bwd workspace per batch element: 2 * 4 * Hq * total_q  */
+  int64_t dq_tiles;          /* key tiles of the dQ kernel over all its items                 */
+  int64_t kv_tiles;          /* query tiles of the dK/dV kernel, counted once per query head  */
+  int32_t num_dq_items;      /* workgroups of the dQ kernel per batch element                 */
+  int32_t num_kv_items;      /* workgroups of the dK/dV kernel per batch element              */
 } ffa_plan_info;
 
 /*
@@ -130,7 +143,10 @@ ffa_status ffa_plan_upload(ffa_plan_t plan, void* d_meta, size_t meta_bytes, voi
 /* Copy the same metadata to host memory h_meta (>= info.meta_bytes bytes).
  * Layout: int32 header[16], then items[num_items][16] (8 item fields followed
  * by a copy of the item's first run), runs[num_runs][8],
- * combine[num_combine][8]; see the planner source for the field order. */
+ * combine[num_combine][8]; with FFA_PLAN_BACKWARD, header[14] is the int32
+ * offset of the backward section: a header[8], then the dQ items and runs and
+ * the dK/dV items and runs in the same formats.  See the planner source for
+ * the field order. */
 ffa_status ffa_plan_export(ffa_plan_t plan, void* h_meta, size_t meta_bytes);
 
 /*
@@ -154,6 +170,39 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
                    const void* v, int64_t v_sb, int64_t v_st, int64_t v_sh,
                    void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
                    float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                   float softmax_scale, void* d_workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Backward.  The derivative of the operation above for a loss L with
+ * dout = dL/dout (the softmax Jacobian; both pages present the forward as a
+ * differentiable training operator: MagiAttention quickstart, "Single-GPU
+ * Flex-Flash-Attention"; FlagAttention user guide, "FlashAttention"): with
+ * P[i,h,j] = exp(s_ij - lse[i,h]) on visible pairs (0 elsewhere),
+ *   dv[j,g] = sum_{h in g} sum_i P dout[i,h]
+ *   dS      = P * (dout[i,h] . v[j,g] - sum_d dout[i,h,d] out[i,h,d])
+ *   dq[i,h] = softmax_scale * sum_j dS k[j,g]
+ *   dk[j,g] = softmax_scale * sum_{h in g} sum_i dS q[i,h]
+ * q, k, v, out, lse are the forward's inputs and outputs (out bf16, lse fp32
+ * as ffa_fwd wrote them, -inf for rows that see nothing); dout, dq, dk, dv are
+ * bf16 with the layout and stride rules of q (dout, dq) and k (dk, dv).
+ * Every element of dq, dk and dv is written (zero where nothing is visible).
+ * Accumulation is fp32; results are bitwise reproducible (no atomics).
+ * d_workspace: >= batch * info.bwd_workspace_bytes bytes of device memory
+ * (fp32 lse * log2 e and rowsum(dout * out) per head and row).  The plan must
+ * have been built with FFA_PLAN_BACKWARD (FFA_ERR_ARG otherwise); token
+ * strides of q, k, v and dout must be below 2^24 elements.
+ */
+ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
+                   const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                   const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh,
+                   const void* v, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                   const void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                   const float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                   const void* dout, int64_t d_sb, int64_t d_st, int64_t d_sh,
+                   void* dq, int64_t dq_sb, int64_t dq_st, int64_t dq_sh,
+                   void* dk, int64_t dk_sb, int64_t dk_st, int64_t dk_sh,
+                   void* dv, int64_t dv_sb, int64_t dv_st, int64_t dv_sh,
                    float softmax_scale, void* d_workspace, size_t workspace_bytes,
                    void* stream);
 

@@ -1,0 +1,264 @@
+"""GPU parity of the backward (dq, dk, dv) through the C ABI against the fp64 oracle.
+
+Inputs: seeded bf16 q, k, v, dout (workloads.make_qkv / make_dout); the
+forward's out and lse come from the library's own forward, as in training.
+The oracle (oracle.attend_backward) differentiates the exact fp64 forward.
+
+Tolerance.  The FlagAttention user guide's accuracy rule, as for the forward:
+against the fp64 oracle, the kernel's error may be at most twice the error of
+the same computation done by PyTorch at the kernel's precision (bf16 autograd
+of an explicit-mask attention on the CPU), plus an allowance of 1e-3 of
+max(max|ref|, 0.01) (fp32 rounding where the exact gradient is 0: a window of
+one key gives dS = P (dP - Dd) = 0 exactly, the kernel's two fp32 dot products
+of the same values differ in their last bits); applied to the max-abs and the mean-abs error of each of dq, dk, dv.
+Gradients can be small through cancellation (a row with two keys), so a
+tolerance relative to the gradient's own size alone would not be meaningful
+there; where PyTorch cannot run the case (full sizes) the bound is
+max-abs <= 2e-2 * max|ref| and mean-abs <= 1e-2 * mean|ref|, on workloads
+where the gradients do not cancel.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GRAD_MAX_REL, GRAD_MEAN_REL = 2e-2, 1e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_bwd(ffa, p, q, k, v, dout, scale=None):
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dd = q.to(dev), k.to(dev), v.to(dev), dout.to(dev)
+    out, lse = ffa.flex_flash_attn_fwd(qd, kd, vd, p.q_ranges, p.k_ranges, p.mask_types, softmax_scale=scale)
+    dq, dk, dv = ffa.flex_flash_attn_bwd(dd, qd, kd, vd, out, lse, p.q_ranges, p.k_ranges, p.mask_types,
+                                         softmax_scale=scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def rel_errors(g, ref):
+    g = g.double().numpy() if isinstance(g, torch.Tensor) else g
+    err = np.abs(g - ref)
+    scale_max = max(np.abs(ref).max(), 1e-30)
+    scale_mean = max(np.abs(ref).mean(), 1e-30)
+    return err.max() / scale_max, err.mean() / scale_mean, err.max()
+
+
+def compare(grads, refs, what, same_precision=None):
+    """same_precision: PyTorch bf16 gradients of the same case (the FlagAttention rule);
+    None: the size-relative bound."""
+    for i, (name, g, r) in enumerate(zip(("dq", "dk", "dv"), grads, refs)):
+        gn = g.double().numpy()
+        assert not np.isnan(gn).any(), f"{what}: NaN in {name}"
+        err = np.abs(gn - r)
+        mx, mean, abs_mx = rel_errors(gn, r)
+        if same_precision is None:
+            log(f"  {what} {name}: max-abs {abs_mx:.3e} (rel {mx:.2e}), mean rel {mean:.2e}, "
+                f"|ref| max {np.abs(r).max():.3e}")
+            assert mx <= GRAD_MAX_REL, f"{what}: {name} max error {mx:.3e} of max|ref|"
+            assert mean <= GRAD_MEAN_REL, f"{what}: {name} mean error {mean:.3e} of mean|ref|"
+        else:
+            et = np.abs(same_precision[i] - r)
+            allow = 1e-3 * max(np.abs(r).max(), 1e-2)  # a floor for gradients that are exactly 0
+            log(f"  {what} {name}: max-abs {abs_mx:.3e} (torch bf16 {et.max():.3e}), mean {err.mean():.3e} "
+                f"(torch bf16 {et.mean():.3e}), |ref| max {np.abs(r).max():.3e}")
+            assert err.max() <= 2.0 * et.max() + allow, f"{what}: {name} max error {err.max():.3e}"
+            assert err.mean() <= 2.0 * et.mean() + allow, f"{what}: {name} mean error {err.mean():.3e}"
+
+
+def torch_bf16_grads(p, q, k, v, dout, scale=None):
+    """Same-precision PyTorch backward on the CPU: bf16 autograd of attention with the
+    oracle's explicit mask (rows that see nothing give 0 and no gradient)."""
+    mask = torch.from_numpy(oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k))
+    has = mask.any(1)
+    m2 = mask | ~has[:, None]
+    rep = p.heads_q // p.heads_kv
+    sc = (1.0 / p.head_dim ** 0.5) if scale is None else scale
+    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
+    a = qq.permute(1, 0, 2)
+    b = kk.repeat_interleave(rep, 1).permute(1, 2, 0).contiguous()
+    c = vv.repeat_interleave(rep, 1).permute(1, 0, 2).contiguous()
+    s = torch.matmul(a, b) * sc
+    s = s.masked_fill(~m2[None], float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), c) * has[None, :, None]
+    (o.permute(1, 0, 2).float() * dout.float()).sum().backward()
+    return [x.grad.double().numpy() for x in (qq, kk, vv)]
+
+
+def oracle_grads(p, q, k, v, dout, scale=None):
+    return oracle.attend_backward(q, k, v, dout, p.q_ranges, p.k_ranges, p.mask_types, scale)
+
+
+def case(ffa, p, what, scale=None):
+    log(f"  {what}: Tq {p.total_q} Tk {p.total_k} Hq {p.heads_q} Hkv {p.heads_kv} D {p.head_dim} "
+        f"slices {p.num_slices}")
+    q, k, v = W.make_qkv(p)
+    dout = W.make_dout(p)
+    grads = run_bwd(ffa, p, q, k, v, dout, scale)
+    compare(grads, oracle_grads(p, q, k, v, dout, scale), what, torch_bf16_grads(p, q, k, v, dout, scale))
+    return q, k, v, dout, grads
+
+
+def test_bwd_config1_tiny_causal(gpu_lib):
+    case(gpu_lib, W.config(1), "config 1")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bwd_random_slices_all_mask_types(gpu_lib, seed):
+    rng = np.random.default_rng(800 + seed)
+    tq, tk = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    p = W.random_problem(800 + seed, tq, tk, hq, hkv, d, n_types=4)
+    case(gpu_lib, p, f"random {seed}")
+
+
+@pytest.mark.parametrize("cfg,div", [(2, 4), (3, 8), (4, 16)])
+def test_bwd_scaled_configs(gpu_lib, cfg, div):
+    case(gpu_lib, W.scaled(cfg, div), f"config {cfg} / {div}")
+
+
+@pytest.mark.parametrize("w", [1, 100])
+def test_bwd_sliding_window(gpu_lib, w):
+    p = W.sliding_window_problem(700, w, [0, 250, 700], 4, 2, 128, seed=40 + w)
+    case(gpu_lib, p, f"window {w}")
+
+
+def test_bwd_softmax_scale(gpu_lib):
+    p = W.random_problem(31, 200, 300, 2, 1, 64, n_types=4)
+    case(gpu_lib, p, "scale 0.37", scale=0.37)
+
+
+def test_bwd_rows_and_keys_that_see_nothing(gpu_lib):
+    # rows [0, 40) and keys [150, 200) are in no slice; row 60's causal window
+    # is empty in a 10 x 5 causal slice: their gradients are exactly zero
+    p = W.make_problem("holes", 200, 200, 2, 1, 64,
+                       [((40, 120), (0, 150), W.FULL), ((120, 130), (0, 5), W.CAUSAL)])
+    q, k, v, dout, (dq, dk, dv) = case(gpu_lib, p, "holes")
+    assert (dq[:40] == 0).all() and (dq[130:] == 0).all()
+    assert (dk[150:] == 0).all() and (dv[150:] == 0).all()
+
+
+def test_bwd_no_slices(gpu_lib):
+    p = W.make_problem("none", 70, 90, 2, 2, 64, [])
+    q, k, v = W.make_qkv(p)
+    dq, dk, dv = run_bwd(gpu_lib, p, q, k, v, W.make_dout(p))
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+
+
+def _torch_bf16_grads(p, q, k, v, dout):
+    """Same-precision PyTorch backward: bf16 SDPA autograd on the CPU per slice
+    (per-slice causal squares / bottom-right rectangles; GQA by repeating kv heads)."""
+    import torch.nn.functional as F
+
+    rep = p.heads_q // p.heads_kv
+    qq = q.clone().requires_grad_(True)
+    kk = k.clone().requires_grad_(True)
+    vv = v.clone().requires_grad_(True)
+    loss = 0
+    for (qs, qe), (ks, ke), t in zip(p.q_ranges.tolist(), p.k_ranges.tolist(), p.mask_types.tolist()):
+        M, N = qe - qs, ke - ks
+        a = qq[qs:qe].permute(1, 0, 2).unsqueeze(0)
+        b = kk[ks:ke].repeat_interleave(rep, dim=1).permute(1, 0, 2).unsqueeze(0).contiguous()
+        c = vv[ks:ke].repeat_interleave(rep, dim=1).permute(1, 0, 2).unsqueeze(0).contiguous()
+        mask = None
+        if t == W.CAUSAL:
+            mask = torch.arange(N)[None, :] <= (N - M + torch.arange(M))[:, None]
+        o = F.scaled_dot_product_attention(a, b, c, attn_mask=mask)
+        loss = loss + (o[0].permute(1, 0, 2).float() * dout[qs:qe].float()).sum()
+    loss.backward()
+    return [x.grad.double().numpy() for x in (qq, kk, vv)]
+
+
+@pytest.mark.parametrize("cfg,div", [(1, 1), (2, 8)])
+def test_bwd_error_within_twice_same_precision_torch(gpu_lib, cfg, div):
+    # FlagAttention's accuracy rule for the backward as for the forward: against the
+    # fp64 oracle, the kernel's error is at most twice the same-precision PyTorch error.
+    p = W.config(cfg) if div == 1 else W.scaled(cfg, div)
+    q, k, v = W.make_qkv(p)
+    dout = W.make_dout(p)
+    grads = run_bwd(gpu_lib, p, q, k, v, dout)
+    refs = oracle_grads(p, q, k, v, dout)
+    tb = _torch_bf16_grads(p, q, k, v, dout)
+    for name, g, r, t in zip(("dq", "dk", "dv"), grads, refs, tb):
+        e_gpu = np.abs(g.double().numpy() - r).max()
+        e_t = np.abs(t - r).max()
+        log(f"  config {cfg}/{div} {name}: max error GPU {e_gpu:.3e}, torch bf16 {e_t:.3e}, ratio {e_gpu / e_t:.2f}")
+        assert e_gpu <= 2.0 * e_t + 1e-3 * np.abs(r).max(), name
+
+
+def test_bwd_full_size_packed_docs_identities(gpu_lib):
+    # Any size: sum_j P_ij = 1 on rows that see a key, so sum_j dv[j,g] equals the
+    # sum of dout over those rows and the heads of group g; and sum_j dS_ij = 0,
+    # so sum_j dk[j,g] = 0.  Sampled rows of dq against the oracle on the
+    # one-row sub-problems (a row's dq depends on its own keys only).
+    p = W.config(3)
+    q, k, v = W.make_qkv(p)
+    dout = W.make_dout(p)
+    dq, dk, dv = run_bwd(gpu_lib, p, q, k, v, dout)
+    rep = p.heads_q // p.heads_kv
+    d64 = dout.double().numpy()
+    ivs = [[] for _ in range(p.total_q)]
+    for (qs, qe), (ks, ke), t in zip(p.q_ranges.tolist(), p.k_ranges.tolist(), p.mask_types.tolist()):
+        for i in range(qs, qe):
+            a, b = oracle.slice_row_interval(i, qs, qe, ks, ke, t)
+            if b > a:
+                ivs[i].append((a, b))
+    seen = np.array([len(x) > 0 for x in ivs])
+    want = d64[seen].sum(axis=0).reshape(p.heads_kv, rep, p.head_dim).sum(axis=1)
+    got = dv.double().numpy().sum(axis=0)
+    err = np.abs(got - want).max() / np.abs(want).max()
+    log(f"  sum dv vs sum dout: rel {err:.2e}")
+    assert err <= 1e-2
+    sk = np.abs(dk.double().numpy().sum(axis=0)).max() / np.abs(dk.double().numpy()).sum(axis=0).max()
+    log(f"  |sum dk| / sum |dk|: {sk:.2e}")
+    assert sk <= 1e-2
+    # sampled rows of dq: the oracle on single-row slices with the row's key interval
+    rows = W.sample_rows(p, 48, seed=3)
+    assert all(len(ivs[r]) == 1 for r in rows)  # one causal slice per document
+    iv = [ivs[r][0] for r in rows]
+    sub_q = np.array([[i, i + 1] for i in range(len(rows))], np.int32)
+    sub_k = np.array([[a, b] for a, b in iv], np.int32)
+    assert len(iv) == len(rows)
+    ref_dq, _, _ = oracle.attend_backward(q[rows], k, v, dout[rows], sub_q, sub_k,
+                                          np.zeros(len(rows), np.int32))
+    mx, mean, abs_mx = rel_errors(dq[rows], ref_dq)
+    log(f"  dq sampled rows: max-abs {abs_mx:.3e} rel {mx:.2e} mean rel {mean:.2e}")
+    assert mx <= GRAD_MAX_REL and mean <= GRAD_MEAN_REL
+
+
+def test_bwd_bitwise_deterministic(gpu_lib):
+    p = W.scaled(3, 8)
+    q, k, v = W.make_qkv(p)
+    dout = W.make_dout(p)
+    a = run_bwd(gpu_lib, p, q, k, v, dout)
+    b = run_bwd(gpu_lib, p, q, k, v, dout)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_autograd_function_matches_direct_call(gpu_lib):
+    p = W.random_problem(12, 300, 260, 4, 2, 128, n_types=4)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x.to(dev) for x in W.make_qkv(p))
+    dout = W.make_dout(p).to(dev)
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out, lse = gpu_lib.flex_flash_attn_func(qa, ka, va, p.q_ranges, p.k_ranges, p.mask_types)
+    assert not lse.requires_grad
+    out.backward(dout)
+    out2, lse2 = gpu_lib.flex_flash_attn_fwd(q, k, v, p.q_ranges, p.k_ranges, p.mask_types)
+    dq, dk, dv = gpu_lib.flex_flash_attn_bwd(dout, q, k, v, out2, lse2, p.q_ranges, p.k_ranges, p.mask_types)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), out2)
+    assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)

@@ -283,24 +283,11 @@ def test_random_slices_all_mask_types(gpu_lib, seed):
             what=f"random all types {seed} T=({tq},{tk}) H=({hq},{hkv}) D={d} types={p.mask_types.tolist()}")
 
 
-def sliding_window_problem(T, w, docs, hq, hkv, d, seed):
-    """Per-document sliding window of w keys: row i sees keys [max(s, i - w + 1), i + 1).
-    The first w - 1 rows of a document are a causal slice; the rest a bi-causal band."""
-    sl = []
-    for s0, e0 in zip(docs[:-1], docs[1:]):
-        h = min(e0, s0 + w - 1)
-        if h > s0:
-            sl.append(((s0, h), (s0, h), W.CAUSAL))
-        if e0 > h:
-            sl.append(((h, e0), (h - w + 1, e0), W.BICAUSAL))
-    return W.make_problem(f"window{w}", T, T, hq, hkv, d, sl, seed=seed)
-
-
 @pytest.mark.parametrize("w,split", [(1, 0), (200, 0), (513, 0), (513, 3)])
 def test_sliding_window(gpu_lib, w, split):
     T = 3000
     docs = [0, 1100, 1130, 3000]
-    p = sliding_window_problem(T, w, docs, 8, 2, 128, seed=31)
+    p = W.sliding_window_problem(T, w, docs, 8, 2, 128, seed=31)
     q, k, v = W.make_qkv(p)
     out, lse = run(gpu_lib, p, q, k, v, split_tiles=split)
     compare(out, lse, *oracle_ref(p, q, k, v), what=f"sliding window w={w} split={split}")

@@ -49,7 +49,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ffa_abi_version() == 1
+    assert lib.ffa_abi_version() == 2
     for code in range(12):
         assert lib.ffa_status_string(code).decode() not in ("", "unknown status")
     assert lib.ffa_status_string(99).decode() == "unknown status"

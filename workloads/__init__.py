@@ -211,6 +211,27 @@ def make_qkv(p: Problem, seed: Optional[int] = None, q_zero: bool = False):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def sliding_window_problem(T, w, docs, hq, hkv, d, seed):
+    """Per-document sliding window of w keys: row i sees keys [max(s, i - w + 1), i + 1).
+    The first w - 1 rows of a document are a causal slice; the rest a bi-causal band."""
+    sl = []
+    for s0, e0 in zip(docs[:-1], docs[1:]):
+        h = min(e0, s0 + w - 1)
+        if h > s0:
+            sl.append(((s0, h), (s0, h), CAUSAL))
+        if e0 > h:
+            sl.append(((h, e0), (h - w + 1, e0), BICAUSAL))
+    return make_problem(f"window{w}", T, T, hq, hkv, d, sl, seed=seed)
+
+
+def make_dout(p: Problem, seed: Optional[int] = None):
+    """Draw an upstream gradient dout [Tq,Hq,D] (CPU, bfloat16) for problem `p`."""
+    import torch
+
+    g = torch.Generator().manual_seed((p.seed if seed is None else seed) + 7919)
+    return torch.randn(p.total_q, p.heads_q, p.head_dim, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
 def sample_rows(p: Problem, n: int, seed: int = 0) -> np.ndarray:
     """A seeded sample of query rows: slice boundaries +/- 1, first/last rows, and random rows."""
     rng = np.random.default_rng(1000 + seed)
