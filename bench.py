@@ -11,7 +11,8 @@ HIP events recorded on the stream the kernels are launched on.
 
 Prints one JSON line.  `roofline` refers to the dominant kernel (ffa_fwd_main,
 bound by bf16 MFMA); `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the same workload.
+sample of the same workload; `backward` times ffa_bwd (dq, dk, dv from the
+forward's out and lse) on the same workload, outside the forward's step.
 """
 from __future__ import annotations
 
@@ -41,6 +42,9 @@ def parse():
     ap.add_argument("--workload", default="packed_docs", choices=sorted(WORKLOADS))
     ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
@@ -169,6 +173,12 @@ def main():
     def step():
         ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale)
 
+    if args.backward_only:
+        step()
+        torch.cuda.synchronize()
+        print(json.dumps({"backward": backward_leg(args, p, qd, kd, vd, out, lse, strides, scale)}), flush=True)
+        return
+
     warm = 0
     t_w = time.perf_counter()
     while warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_seconds:
@@ -235,9 +245,68 @@ def main():
             "algorithmic_flops_per_launch": flops,
         },
     }
+    if not args.no_backward:
+        res["backward"] = backward_leg(args, p, qd, kd, vd, out, lse, strides, scale)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, q, k, v, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale):
+    """Time ffa_bwd (preprocess, dQ kernel, dK/dV kernel) on the same workload, with the
+    forward's out and lse.  FLOPs counted as 10 * D * Hq * visible pairs: the five products
+    of the gradient (dP, dV, dQ, dK and the recomputed scores), none of the recomputation."""
+    import torch
+
+    import flexible_mask_flash_amd as ffa
+    import workloads as W
+
+    dev = qd.device
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, backward=True)
+    plan.device_meta(dev)
+    dout = W.make_dout(p).to(dev)
+    dq = torch.empty_like(qd)
+    dk = torch.empty_like(kd)
+    dv = torch.empty_like(vd)
+    t = {"q": qd, "k": kd, "v": vd, "out": out, "lse": lse, "dout": dout, "dq": dq, "dk": dk, "dv": dv}
+    st = dict(strides)
+    for n in ("dout", "dq", "dk", "dv"):
+        st[n] = (0, t[n].stride(0), t[n].stride(1))
+
+    def step():
+        ffa.run_bwd(plan, t, st, 1, scale)
+
+    warm = 0
+    t_w = time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_seconds:
+        step()
+        warm += 1
+        if warm % 5 == 0:
+            torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 10.0 * p.head_dim * p.heads_q * plan.info["visible_pairs"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "masked-attn bwd TFLOPS (10 * D * Hq * unmasked pairs)",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "ms_per_step": round(ms, 4),
+        "steps": args.steps,
+        "warmup": warm,
+        "flops_per_step": flops,
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "plan": {k_: int(v_) for k_, v_ in plan.info.items() if k_ in
+                 ("num_dq_items", "num_kv_items", "dq_tiles", "kv_tiles", "bwd_workspace_bytes")},
+    }
 
 
 if __name__ == "__main__":
