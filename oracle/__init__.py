@@ -22,6 +22,8 @@ from .fwd import (  # noqa: F401
     count_visible_pairs,
     attend,
     attend_dense,
+    capped_scores,
+    sink_logits,
     merge_partials,
 )
 from .bwd import attend_backward  # noqa: F401,E402

@@ -141,12 +141,51 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def sink_logits(sink, sink_layout: str, rows: np.ndarray, hq: int) -> Optional[np.ndarray]:
+    """Sink logits per selected row: [R, S_sink, Hq] float64, or None.
+
+    The MagiAttention quickstart passes `sink` as float32 [S_sink, Hq] (layout
+    "sh": the same logits for every query row) or [Tq, S_sink, Hq] ("ssh": per
+    row) ("Single-GPU Flex-Flash-Attention" and the sink examples of the
+    extension functions).  Reading: each sink logit is one more term of the
+    row's softmax denominator, exp(sink), with no value vector; it is not scaled
+    by softmax_scale and not soft-capped.
+    """
+    if sink is None:
+        return None
+    sk = _as_f64(sink)
+    if sink_layout == "sh":
+        if sk.ndim != 2 or sk.shape[1] != hq:
+            raise ValueError("sink layout 'sh' needs [S_sink, Hq]")
+        return np.broadcast_to(sk[None], (rows.shape[0],) + sk.shape)
+    if sink_layout == "ssh":
+        if sk.ndim != 3 or sk.shape[2] != hq:
+            raise ValueError("sink layout 'ssh' needs [Tq, S_sink, Hq]")
+        return sk[rows]
+    raise ValueError(f"unknown sink layout {sink_layout!r}")
+
+
+def capped_scores(raw: np.ndarray, softcap: float) -> np.ndarray:
+    """Soft-capped scores: softcap * tanh(raw / softcap) for softcap > 0, else raw.
+
+    Reading (the quickstart lists `softcap`, default 0, without defining it): the
+    usual logit soft-capping applied to the scaled scores before the mask and
+    the softmax; 0 disables it.
+    """
+    if softcap and softcap > 0:
+        return softcap * np.tanh(raw / softcap)
+    return raw
+
+
 def attend(q, k, v, q_ranges, k_ranges, mask_types, softmax_scale: Optional[float] = None,
-           rows: Optional[Sequence[int]] = None, block_rows: int = 256):
+           rows: Optional[Sequence[int]] = None, block_rows: int = 256, sink=None, sink_layout: str = "sh",
+           softcap: float = 0.0):
     """Reference forward.  Returns (out [R,Hq,D] float64, lse [R,Hq] float64).
 
     q [Tq,Hq,D], k/v [Tk,Hkv,D] (torch or numpy, any float dtype; converted
-    exactly to float64).  `rows` selects query rows (default: all).
+    exactly to float64).  `rows` selects query rows (default: all).  With
+    `sink`, lse is the log of the full denominator (keys and sinks) and a row
+    that sees no key has out 0 and lse = ln sum exp(sink).
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -160,31 +199,32 @@ def attend(q, k, v, q_ranges, k_ranges, mask_types, softmax_scale: Optional[floa
     grp = hq // hkv
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     rows = np.arange(tq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    sinks = sink_logits(sink, sink_layout, rows, hq)  # [R, S, Hq] or None
     out = np.zeros((rows.shape[0], hq, d), dtype=np.float64)
     lse = np.full((rows.shape[0], hq), -np.inf, dtype=np.float64)
     for b0 in range(0, rows.shape[0], block_rows):
         rb = rows[b0:b0 + block_rows]
+        nb = rb.shape[0]
         mask = mask_rows(rb, q_ranges, k_ranges, mask_types, tk)
         cols = np.nonzero(mask.any(axis=0))[0]
-        if cols.size == 0:
-            continue
         mk = mask[:, cols]  # [B, C]
         for g in range(hkv):
             kg = k[cols, g, :]  # [C, D]
             vg = v[cols, g, :]
             for hh in range(grp):
                 h = g * grp + hh
-                s = (q[rb, h, :] @ kg.T) * scale  # [B, C]
+                s = capped_scores((q[rb, h, :] @ kg.T) * scale, softcap)  # [B, C]
                 s = np.where(mk, s, -np.inf)
-                mx = s.max(axis=1)
+                sk = sinks[b0:b0 + nb, :, h] if sinks is not None else np.zeros((nb, 0))  # [B, S]
+                mx = np.maximum(s.max(axis=1, initial=-np.inf), sk.max(axis=1, initial=-np.inf))
                 safe = np.where(np.isfinite(mx), mx, 0.0)
                 p = np.exp(s - safe[:, None])  # masked entries -> exp(-inf) = 0
-                den = p.sum(axis=1)
+                den = p.sum(axis=1) + np.exp(sk - safe[:, None]).sum(axis=1)
                 nonempty = den > 0
                 l = np.where(nonempty, safe + np.log(np.where(nonempty, den, 1.0)), -np.inf)
                 o = (p @ vg) / np.where(nonempty, den, 1.0)[:, None]
-                out[b0:b0 + rb.shape[0], h, :] = np.where(nonempty[:, None], o, 0.0)
-                lse[b0:b0 + rb.shape[0], h] = l
+                out[b0:b0 + nb, h, :] = np.where(nonempty[:, None], o, 0.0)
+                lse[b0:b0 + nb, h] = l
     return out, lse
 
 

@@ -9,7 +9,7 @@ import oracle.bwd as oracle_bwd
 from tests import test_oracle_bwd_pins as pins
 
 MUTATIONS = {
-    "jacobian_term_dropped": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "jacobian_term_dropped": ("ds = p * (dp - dd)", "ds = p * dp"),
     "dk_scale_dropped": ("dk[cols, g, :] += scale * (ds.T @ q[rb, h, :])", "dk[cols, g, :] += ds.T @ q[rb, h, :]"),
     "dv_squared_weights": ("dv[cols, g, :] += p.T @ do", "dv[cols, g, :] += (p * p).T @ do"),
     "dq_uses_v": ("dq[rb, h, :] = scale * (ds @ kg)", "dq[rb, h, :] = scale * (ds @ vg)"),

@@ -20,7 +20,8 @@ MUTATIONS = {
     "causal_off_by_one": ("end = ke - (qe - 1 - rows)", "end = ke - (qe - rows)"),
     "causal_top_left": ("end = ke - (qe - 1 - rows)", "end = ks + (rows - qs) + 1"),
     "gqa_interleaved": ("h = g * grp + hh", "h = hh * hkv + g"),
-    "scale_dropped": ("s = (q[rb, h, :] @ kg.T) * scale", "s = (q[rb, h, :] @ kg.T)"),
+    "scale_dropped": ("s = capped_scores((q[rb, h, :] @ kg.T) * scale, softcap)",
+                      "s = capped_scores((q[rb, h, :] @ kg.T), softcap)"),
     "v_replaced_by_k": ("o = (p @ vg)", "o = (p @ kg)"),
     "lse_drops_max": ("l = np.where(nonempty, safe + np.log(", "l = np.where(nonempty, 0.0 + np.log("),
     "union_lost": ("m |= vis", "m = vis"),
