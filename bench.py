@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--softcap", type=float, default=0.0, help="soft-capping of the scores (0: off)")
+    ap.add_argument("--sinks", type=int, default=0, help="sink logits per head (layout sh; 0: none)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
@@ -169,14 +171,20 @@ def main():
                "v": (0, vd.stride(0), vd.stride(1)), "out": (0, out.stride(0), out.stride(1)),
                "lse": (0, lse.stride(0), lse.stride(1))}
     scale = 1.0 / math.sqrt(p.head_dim)
+    sink = None
+    if args.sinks > 0:
+        g = torch.Generator().manual_seed(17)
+        sink = torch.randn((args.sinks, p.heads_q), generator=g, dtype=torch.float32).to(dev)
+    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q)
 
     def step():
-        ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale)
+        ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale, extras)
 
     if args.backward_only:
         step()
         torch.cuda.synchronize()
-        print(json.dumps({"backward": backward_leg(args, p, qd, kd, vd, out, lse, strides, scale)}), flush=True)
+        print(json.dumps({"backward": backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink)}),
+              flush=True)
         return
 
     warm = 0
@@ -226,6 +234,8 @@ def main():
             "plan": {k_: int(v_) for k_, v_ in plan.info.items()},
             "plan_ms": round(plan_ms, 2),
             "split_tiles": args.split_tiles,
+            "softcap": args.softcap,
+            "sinks": args.sinks,
         },
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_median": round(med, 4),
@@ -246,13 +256,13 @@ def main():
         },
     }
     if not args.no_backward:
-        res["backward"] = backward_leg(args, p, qd, kd, vd, out, lse, strides, scale)
+        res["backward"] = backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, q, k, v, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
-def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale):
+def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink=None):
     """Time ffa_bwd (preprocess, dQ kernel, dK/dV kernel) on the same workload, with the
     forward's out and lse.  FLOPs counted as 10 * D * Hq * visible pairs: the five products
     of the gradient (dP, dV, dQ, dK and the recomputed scores), none of the recomputation."""
@@ -274,8 +284,11 @@ def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale):
     for n in ("dout", "dq", "dk", "dv"):
         st[n] = (0, t[n].stride(0), t[n].stride(1))
 
+    dsink = torch.empty_like(sink) if sink is not None else None
+    extras = ffa.make_extras(sink, "sh", args.softcap, dsink=dsink, total_q=p.total_q, heads_q=p.heads_q)
+
     def step():
-        ffa.run_bwd(plan, t, st, 1, scale)
+        ffa.run_bwd(plan, t, st, 1, scale, extras)
 
     warm = 0
     t_w = time.perf_counter()

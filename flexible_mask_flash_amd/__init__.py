@@ -96,6 +96,12 @@ class PlanInfo(ctypes.Structure):
     ]
 
 
+class AttnExtras(ctypes.Structure):
+    """ffa_attn_extras: optional sink logits (and their gradient) and softcap."""
+    _fields_ = [("sink", _vp), ("dsink", _vp), ("sink_sb", _i64), ("sink_st", _i64), ("sink_ss", _i64),
+                ("sink_sh", _i64), ("n_sink", _i32), ("softcap", _f32)]
+
+
 # (name, restype, argtypes) of every function in include/ffa.h
 _SIGNATURES = [
     ("ffa_abi_version", _i32, []),
@@ -112,7 +118,7 @@ _SIGNATURES = [
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
-                       _f32, _vp, _sz, _vp]),
+                       _f32, ctypes.POINTER(AttnExtras), _vp, _sz, _vp]),
     ("ffa_bwd", _i32, [_vp, _vp, _i32,
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
@@ -123,7 +129,7 @@ _SIGNATURES = [
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
-                       _f32, _vp, _sz, _vp]),
+                       _f32, ctypes.POINTER(AttnExtras), _vp, _sz, _vp]),
     ("ffa_plan_destroy", None, [_vp]),
 ]
 
@@ -308,7 +314,40 @@ def _require_bf16_cuda(name, t, ndim):
         raise ValueError(f"{name} must have a contiguous head_dim")
 
 
-def run_fwd(plan: Plan, q, k, v, out, lse, strides, batch: int, softmax_scale: float):
+def make_extras(sink=None, sink_layout: str = "sh", softcap: float = 0.0, dsink=None, total_q=None, heads_q=None):
+    """ffa_attn_extras for a sink tensor (fp32 device; layout "sh" [S, Hq] or "ssh" [Tq, S, Hq])
+    and a softcap; None when neither is used."""
+    import torch
+
+    if sink is None and not softcap:
+        return None
+    ex = AttnExtras()
+    ex.softcap = float(softcap or 0.0)
+    if sink is not None:
+        if not isinstance(sink, torch.Tensor) or sink.dtype != torch.float32 or not sink.is_cuda:
+            raise TypeError("sink must be a float32 device tensor")
+        if sink_layout == "sh":
+            if sink.dim() != 2 or (heads_q is not None and sink.shape[1] != heads_q):
+                raise ValueError("sink layout 'sh' needs [S_sink, Hq]")
+            ex.sink_st, ex.sink_ss, ex.sink_sh = 0, sink.stride(0), sink.stride(1)
+            ex.n_sink = sink.shape[0]
+        elif sink_layout == "ssh":
+            if sink.dim() != 3 or (heads_q is not None and sink.shape[2] != heads_q) or \
+                    (total_q is not None and sink.shape[0] != total_q):
+                raise ValueError("sink layout 'ssh' needs [Tq, S_sink, Hq]")
+            ex.sink_st, ex.sink_ss, ex.sink_sh = sink.stride(0), sink.stride(1), sink.stride(2)
+            ex.n_sink = sink.shape[1]
+        else:
+            raise ValueError(f"unknown sink layout {sink_layout!r}")
+        ex.sink = sink.data_ptr()
+        if dsink is not None:
+            if dsink.shape != sink.shape or dsink.stride() != sink.stride() or dsink.dtype != torch.float32:
+                raise ValueError("dsink must match sink in shape, strides and dtype")
+            ex.dsink = dsink.data_ptr()
+    return ex
+
+
+def run_fwd(plan: Plan, q, k, v, out, lse, strides, batch: int, softmax_scale: float, extras=None):
     """Call ffa_fwd.  strides: dict of (sb, st, sh) per tensor, in elements."""
     import torch
 
@@ -324,27 +363,27 @@ def run_fwd(plan: Plan, q, k, v, out, lse, strides, batch: int, softmax_scale: f
                      v.data_ptr(), *vs,
                      out.data_ptr(), *os_,
                      lse.data_ptr(), *ls,
-                     float(softmax_scale), ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
+                     float(softmax_scale), ctypes.byref(extras) if extras is not None else None,
+                     ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
     _check(st, "ffa_fwd")
 
 
 def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
                         softmax_scale: Optional[float] = None, softcap: float = 0.0,
-                        plan: Optional[Plan] = None, split_tiles: int = 0):
+                        plan: Optional[Plan] = None, split_tiles: int = 0, sink_layout: str = "sh"):
     """Forward of flexible-mask attention on packed THD tensors -> (out, lse).
 
     q [Tq,Hq,D], k/v [Tk,Hkv,D] bf16 device tensors (head_dim contiguous);
-    q_ranges / k_ranges int32 [S,2], attn_type_map int32 [S] (0 full, 1 causal),
-    host or device (device ranges are copied to the host, which synchronises).
-    Returns out [Tq,Hq,D] bf16 and lse [Tq,Hq] fp32 (natural log; -inf and a
-    zero output for rows that see no key).
+    q_ranges / k_ranges int32 [S,2], attn_type_map int32 [S] (0 full, 1 causal,
+    2 inverse causal, 3 bi-causal), host or device (device ranges are copied to
+    the host, which synchronises).  Optional: sink, fp32 logits [S_sink, Hq]
+    ("sh") or [Tq, S_sink, Hq] ("ssh") that join each row's softmax denominator
+    without a value; softcap > 0 maps a scaled score s to softcap*tanh(s/softcap).
+    Returns out [Tq,Hq,D] bf16 and lse [Tq,Hq] fp32 (natural log, sinks included;
+    -inf and a zero output for rows that see no key and no sink).
     """
     import torch
 
-    if sink is not None:
-        raise NotImplementedError("attention sink is not supported by this forward")
-    if softcap:
-        raise NotImplementedError("softcap is not supported by this forward")
     _require_bf16_cuda("q", q, 3)
     _require_bf16_cuda("k", k, 3)
     _require_bf16_cuda("v", v, 3)
@@ -369,11 +408,12 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
         "out": (0, out.stride(0), out.stride(1)),
         "lse": (0, lse.stride(0), lse.stride(1)),
     }
-    run_fwd(plan, q, k, v, out, lse, strides, 1, scale)
+    ex = make_extras(sink, sink_layout, softcap, total_q=tq, heads_q=hq)
+    run_fwd(plan, q, k, v, out, lse, strides, 1, scale, ex)
     return out, lse
 
 
-def run_bwd(plan: Plan, t: dict, strides: dict, batch: int, softmax_scale: float):
+def run_bwd(plan: Plan, t: dict, strides: dict, batch: int, softmax_scale: float, extras=None):
     """Call ffa_bwd.  t: tensors q k v out lse dout dq dk dv; strides: (sb, st, sh) each."""
     import torch
 
@@ -388,6 +428,7 @@ def run_bwd(plan: Plan, t: dict, strides: dict, batch: int, softmax_scale: float
     for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"):
         args += [t[name].data_ptr(), *strides[name]]
     st = lib.ffa_bwd(plan.handle, meta.data_ptr(), int(batch), *args, float(softmax_scale),
+                     ctypes.byref(extras) if extras is not None else None,
                      ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
     _check(st, "ffa_bwd")
 
@@ -397,12 +438,14 @@ def _thd_strides(x):
 
 
 def flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map,
-                        softmax_scale: Optional[float] = None, plan: Optional[Plan] = None):
+                        softmax_scale: Optional[float] = None, plan: Optional[Plan] = None, sink=None,
+                        sink_layout: str = "sh", softcap: float = 0.0):
     """Gradients (dq, dk, dv) of flex_flash_attn_fwd for the upstream gradient dout.
 
     q [Tq,Hq,D], k/v [Tk,Hkv,D], out/dout [Tq,Hq,D] bf16 and lse [Tq,Hq] fp32
-    (the forward's outputs) on the device; returns bf16 tensors shaped like
-    q, k and v.  Every step runs in the library's HIP kernels.
+    (the forward's outputs, with the same sink / softcap) on the device; returns
+    bf16 tensors shaped like q, k and v, and the fp32 gradient of sink as a
+    fourth result when sink is given.  Every step runs in the library's HIP kernels.
     """
     import torch
 
@@ -425,7 +468,11 @@ def flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_m
     dv = torch.empty((tk, hkv, d), dtype=torch.bfloat16, device=q.device)
     t = {"q": q, "k": k, "v": v, "out": out, "lse": lse, "dout": dout, "dq": dq, "dk": dk, "dv": dv}
     strides = {n: _thd_strides(x) for n, x in t.items()}
-    run_bwd(plan, t, strides, 1, scale)
+    dsink = torch.empty_like(sink) if sink is not None else None
+    ex = make_extras(sink, sink_layout, softcap, dsink=dsink, total_q=tq, heads_q=hq)
+    run_bwd(plan, t, strides, 1, scale, ex)
+    if sink is not None:
+        return dq, dk, dv, dsink
     return dq, dk, dv
 
 
@@ -434,25 +481,29 @@ def _autograd_function():
 
     class _FlexAttn(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, plan, scale):
+        def forward(ctx, q, k, v, sink, plan, scale, sink_layout, softcap):
             tq, hq, d = q.shape
             out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
             lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
             strides = {"q": _thd_strides(q), "k": _thd_strides(k), "v": _thd_strides(v),
                        "out": _thd_strides(out), "lse": _thd_strides(lse)}
-            run_fwd(plan, q, k, v, out, lse, strides, 1, scale)
-            ctx.save_for_backward(q, k, v, out, lse)
-            ctx.plan, ctx.scale = plan, scale
+            sk = sink.detach() if sink is not None else None
+            run_fwd(plan, q, k, v, out, lse, strides, 1, scale, make_extras(sk, sink_layout, softcap,
+                                                                           total_q=tq, heads_q=hq))
+            ctx.save_for_backward(q, k, v, out, lse, sk)
+            ctx.plan, ctx.scale, ctx.sink_layout, ctx.softcap = plan, scale, sink_layout, softcap
             ctx.mark_non_differentiable(lse)
             return out, lse
 
         @staticmethod
         def backward(ctx, dout, _dlse):
-            q, k, v, out, lse = ctx.saved_tensors
+            q, k, v, out, lse, sink = ctx.saved_tensors
             if dout.stride(-1) != 1 or dout.dtype != torch.bfloat16:
                 dout = dout.to(torch.bfloat16).contiguous()
-            dq, dk, dv = flex_flash_attn_bwd(dout, q, k, v, out, lse, None, None, None, ctx.scale, plan=ctx.plan)
-            return dq, dk, dv, None, None
+            g = flex_flash_attn_bwd(dout, q, k, v, out, lse, None, None, None, ctx.scale, plan=ctx.plan,
+                                    sink=sink, sink_layout=ctx.sink_layout, softcap=ctx.softcap)
+            dsink = g[3] if sink is not None else None
+            return g[0], g[1], g[2], dsink, None, None, None, None
 
     return _FlexAttn
 
@@ -461,18 +512,14 @@ _FLEX_FN = None
 
 
 def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
-                         softmax_scale: Optional[float] = None, softcap: float = 0.0):
+                         softmax_scale: Optional[float] = None, softcap: float = 0.0, sink_layout: str = "sh"):
     """Differentiable flexible-mask attention -> (out, lse).
 
-    Same arguments and results as flex_flash_attn_fwd; gradients flow to q, k
-    and v through out (lse is returned without a gradient).  The backward runs
-    ffa_bwd on a plan built with the backward worklists.
+    Same arguments and results as flex_flash_attn_fwd; gradients flow to q, k,
+    v and sink through out (lse is returned without a gradient).  The backward
+    runs ffa_bwd on a plan built with the backward worklists.
     """
     global _FLEX_FN
-    if sink is not None:
-        raise NotImplementedError("attention sink is not supported")
-    if softcap:
-        raise NotImplementedError("softcap is not supported")
     for name, x in (("q", q), ("k", k), ("v", v)):
         _require_bf16_cuda(name, x, 3)
     tq, hq, d = q.shape
@@ -484,7 +531,7 @@ def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if _FLEX_FN is None:
         _FLEX_FN = _autograd_function()
-    return _FLEX_FN.apply(q, k, v, plan, scale)
+    return _FLEX_FN.apply(q, k, v, sink, plan, scale, sink_layout, float(softcap or 0.0))
 
 
 def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = None, dropout_p: float = 0.0,

@@ -81,7 +81,47 @@ struct BwdArgs {
   int32_t total_q, total_k, heads_q, batch;
   int32_t heads_per_item;  // query heads per query-major item
   int32_t kv_ratio;        // heads_q / heads_kv
+  float cap_log2;          // softcap * log2(e)          (CAP instances)
+  float cap_arg;           // 2 * log2(e) * scale / softcap
 };
+
+struct SinkArgs {
+  const float* sink;
+  float* dsink;
+  const float* lw;
+  const float* dw;
+  int64_t sk_sb, sk_st, sk_ss, sk_sh;
+  int32_t total_q, heads_q, n_sink;
+};
+
+// tanh(y) from z = 2 y log2(e): 1 - 2 / (1 + 2^z); exact limits +-1 for +-inf
+__device__ __forceinline__ float tanh_from_2ylog2e(float z) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+}
+
+// d sink[b, s, h] = -sum_i exp(sink - lse[i,h]) Dd[i,h]   (shared logits, sink_st == 0)
+// d sink[b, i, s, h] = -exp(sink[i] - lse[i,h]) Dd[i,h]     (per-row logits)
+// One workgroup per (sink, head, batch element); the sum runs in a fixed order.
+__global__ __launch_bounds__(256) void ffa_bwd_dsink(SinkArgs a) {
+  const int s = blockIdx.x / a.heads_q, h = blockIdx.x % a.heads_q, b = blockIdx.y;
+  const int64_t row0 = ((int64_t)b * a.heads_q + h) * a.total_q;
+  const float* sp = a.sink + (int64_t)b * a.sk_sb + (int64_t)s * a.sk_ss + (int64_t)h * a.sk_sh;
+  float* dp = a.dsink + (int64_t)b * a.sk_sb + (int64_t)s * a.sk_ss + (int64_t)h * a.sk_sh;
+  float acc = 0.0f;
+  for (int t = threadIdx.x; t < a.total_q; t += 256) {
+    const float x = sp[(int64_t)t * a.sk_st] * kLog2e;
+    const float c = -__builtin_amdgcn_exp2f(x - a.lw[row0 + t]) * a.dw[row0 + t];
+    if (a.sk_st != 0) dp[(int64_t)t * a.sk_st] = c;
+    else acc += c;
+  }
+  if (a.sk_st != 0) return;
+  __shared__ float part[4];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) *dp = (part[0] + part[1]) + (part[2] + part[3]);
+}
 
 // Dd[b,h,t] = sum_d dO[b,t,h,d] O[b,t,h,d] (fp32 from the bf16 values) and
 // L[b,h,t] = lse * log2 e, with +inf for rows that see no key (their P is 0).
@@ -126,7 +166,7 @@ __device__ __forceinline__ int swz_b(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-template <int D, bool KV>
+template <int D, bool KV, bool CAP>
 __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffa_bwd_main(BwdArgs a) {
   constexpr int BN = kBlockN;          // 64 rows per streamed tile
   constexpr int ROWB = D * 2;          // bytes of one row
@@ -427,22 +467,35 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       }
     }
     if (s.t.edge()) mask(s.t, xa, xb);
-    // P = exp2(X1 c2 - L) in place, between the MFMAs of X2
+    // P = exp2(X1 c2 - L) in place, between the MFMAs of X2.  Soft-capped:
+    // P = exp2(cap_log2 tanh - L) (masked scores stay at P = 0), and what stays in
+    // place is P (1 - tanh^2), the factor of dS; P itself goes to bf16 at once.
     auto lval = [&](int e) -> float { return KV ? lv[e >> 2][e & 3] : l_row; };
     auto dval = [&](int e) -> float { return KV ? dv[e >> 2][e & 3] : d_row; };
     constexpr int EPQ = 32 / (2 * KSTEPS);  // score elements per MFMA of X2
+    bf16x8_t pf[4], sf[4];
     rowprod(std::integral_constant<int, OB>{}, f2, ya, yb, [&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
 #pragma unroll
       for (int e = EPQ * m; e < EPQ * (m + 1); ++e) {
-        if (e < 16) xa[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xa[e], c2, -lval(e)));
-        else xb[e - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(xb[e - 16], c2, -lval(e)));
+        if constexpr (CAP) {
+          const float x = e < 16 ? xa[e] : xb[e - 16];
+          const float th = tanh_from_2ylog2e(x * a.cap_arg);
+          const float arg = x == -INFINITY ? -INFINITY : __builtin_fmaf(a.cap_log2, th, -lval(e));
+          const float pr = __builtin_amdgcn_exp2f(arg);
+          if constexpr (KV) pf[e >> 3][e & 7] = (__bf16)pr;
+          const float keep = pr * __builtin_fmaf(-th, th, 1.0f);
+          if (e < 16) xa[e] = keep;
+          else xb[e - 16] = keep;
+        } else {
+          if (e < 16) xa[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xa[e], c2, -lval(e)));
+          else xb[e - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(xb[e - 16], c2, -lval(e)));
+        }
       }
       fence(xa);
       fence(xb);
     });
     // dS = P (X2 - Dd); bf16 operands of the transposed products
-    bf16x8_t pf[4], sf[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -450,7 +503,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         const int e = 8 * t + u;
         const float p = e < 16 ? xa[e] : xb[e - 16];
         const float y = e < 16 ? ya[e] : yb[e - 16];
-        pf[t][u] = (__bf16)p;
+        if constexpr (!CAP) pf[t][u] = (__bf16)p;
         sf[t][u] = (__bf16)(p * (y - dval(e)));
       }
     if constexpr (KV) trprod(std::integral_constant<int, OB>{}, pf, acc2);
@@ -519,7 +572,8 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
                    const float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh, const void* dout, int64_t d_sb,
                    int64_t d_st, int64_t d_sh, void* dq, int64_t dq_sb, int64_t dq_st, int64_t dq_sh, void* dk,
                    int64_t dk_sb, int64_t dk_st, int64_t dk_sh, void* dv, int64_t dv_sb, int64_t dv_st, int64_t dv_sh,
-                   float softmax_scale, void* d_workspace, size_t workspace_bytes, void* stream) {
+                   float softmax_scale, const ffa_attn_extras* extras, void* d_workspace, size_t workspace_bytes,
+                   void* stream) {
   ffa::clear_error();
   if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
   const ffa::Plan& p = plan->plan;
@@ -530,6 +584,10 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     return ffa::set_error(FFA_ERR_ARG, "softmax_scale must be finite and > 0");
   if (!d_meta) return ffa::set_error(FFA_ERR_NULL, "d_meta is NULL");
   const bool has_q = p.total_q > 0, has_k = p.total_k > 0;
+  const ffa_status xs = ffa::check_extras(extras, has_q);
+  if (xs != FFA_OK) return xs;
+  ffa_attn_extras ex = {};
+  if (extras) ex = *extras;
   if (has_q && (!q || !out || !lse || !dout || !dq))
     return ffa::set_error(FFA_ERR_NULL, "q, out, lse, dout and dq must be non-NULL");
   if (has_k && (!k || !v || !dk || !dv)) return ffa::set_error(FFA_ERR_NULL, "k, v, dk and dv must be non-NULL");
@@ -611,16 +669,22 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   ba.batch = batch;
   ba.heads_per_item = p.heads_per_item;
   ba.kv_ratio = p.heads_q / p.heads_kv;
+  const bool cap = ex.softcap > 0.0f;
+  ba.cap_log2 = cap ? (float)((double)ex.softcap * 1.4426950408889634074) : 0.0f;
+  ba.cap_arg = cap ? (float)(2.0 * 1.4426950408889634074 * (double)softmax_scale / (double)ex.softcap) : 0.0f;
 
   const dim3 block(64 * ffa::kWaves);
   if (p.num_dq_items > 0) {
     ba.items = dq_items;
     ba.runs = dq_runs;
     const dim3 grid((unsigned)((int64_t)p.num_dq_items * batch));
-    if (p.head_dim == 128)
-      hipLaunchKernelGGL((ffa_bwd_main<128, false>), grid, block, 0, s, ba);
-    else
-      hipLaunchKernelGGL((ffa_bwd_main<64, false>), grid, block, 0, s, ba);
+    if (p.head_dim == 128) {
+      if (cap) hipLaunchKernelGGL((ffa_bwd_main<128, false, true>), grid, block, 0, s, ba);
+      else hipLaunchKernelGGL((ffa_bwd_main<128, false, false>), grid, block, 0, s, ba);
+    } else {
+      if (cap) hipLaunchKernelGGL((ffa_bwd_main<64, false, true>), grid, block, 0, s, ba);
+      else hipLaunchKernelGGL((ffa_bwd_main<64, false, false>), grid, block, 0, s, ba);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dq)");
   }
@@ -628,12 +692,30 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     ba.items = kv_items;
     ba.runs = kv_runs;
     const dim3 grid((unsigned)((int64_t)p.num_kv_items * batch));
-    if (p.head_dim == 128)
-      hipLaunchKernelGGL((ffa_bwd_main<128, true>), grid, block, 0, s, ba);
-    else
-      hipLaunchKernelGGL((ffa_bwd_main<64, true>), grid, block, 0, s, ba);
+    if (p.head_dim == 128) {
+      if (cap) hipLaunchKernelGGL((ffa_bwd_main<128, true, true>), grid, block, 0, s, ba);
+      else hipLaunchKernelGGL((ffa_bwd_main<128, true, false>), grid, block, 0, s, ba);
+    } else {
+      if (cap) hipLaunchKernelGGL((ffa_bwd_main<64, true, true>), grid, block, 0, s, ba);
+      else hipLaunchKernelGGL((ffa_bwd_main<64, true, false>), grid, block, 0, s, ba);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dk, dv)");
+  }
+  if (ex.n_sink > 0 && ex.dsink && has_q) {
+    SinkArgs sa;
+    sa.sink = ex.sink;
+    sa.dsink = ex.dsink;
+    sa.lw = lw;
+    sa.dw = dwp;
+    sa.sk_sb = ex.sink_sb; sa.sk_st = ex.sink_st; sa.sk_ss = ex.sink_ss; sa.sk_sh = ex.sink_sh;
+    sa.total_q = p.total_q;
+    sa.heads_q = p.heads_q;
+    sa.n_sink = ex.n_sink;
+    const dim3 grid((unsigned)((int64_t)ex.n_sink * p.heads_q), (unsigned)batch);
+    hipLaunchKernelGGL(ffa_bwd_dsink, grid, dim3(256), 0, s, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_dsink");
   }
   return FFA_OK;
 }

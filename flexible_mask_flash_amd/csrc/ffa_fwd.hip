@@ -68,6 +68,13 @@ struct FwdArgs {
   int32_t batch;
   int32_t heads_per_item;
   int32_t kv_ratio;  // heads_q / heads_kv
+  // soft-capping (CAP instances): score -> softcap * tanh(scale q.k / softcap)
+  float cap_log2;    // softcap * log2(e)
+  float cap_arg;     // 2 * log2(e) * scale / softcap: tanh(y) = 1 - 2 / (1 + exp2(cap_arg * q.k))
+  // attention sink: n_sink logits per (row, head) at sink[b*sk_sb + row*sk_st + s*sk_ss + h*sk_sh]
+  const float* sink;
+  int64_t sk_sb, sk_st, sk_ss, sk_sh;
+  int32_t n_sink;
 };
 
 struct CombineArgs {
@@ -81,9 +88,19 @@ struct CombineArgs {
   int64_t l_sb, l_st, l_sh;
   int32_t batch;
   int32_t heads_per_item;
+  const float* sink;
+  int64_t sk_sb, sk_st, sk_ss, sk_sh;
+  int32_t n_sink;
 };
 
+// tanh(y) with y given as 2 y log2(e): 1 - 2 / (1 + 2^(2 y log2 e)); exact limits
+// +-1 for +-inf, absolute error ~1e-7 near 0 (fp32 rounding of 1)
+__device__ __forceinline__ float tanh_from_2ylog2e(float z) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+}
+
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 // A row keeps its reference point (log2 units) until one of its probabilities
 // would exceed 2^64: a lane's per-tile partial sum above kOverflow sends the
 // whole wave through the exact rescale path.  Values up to 2^64 are exact
@@ -104,7 +121,7 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
-template <int D>
+template <int D, bool CAP>
 __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
   constexpr int BN = kBlockN;          // 64 keys per tile
   constexpr int ROWB = D * 2;          // bytes of one K/V row
@@ -333,6 +350,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   };
 
   const float c2 = a.scale_log2;
+  const float cap_arg = a.cap_arg;
   const FFA_CONST int32_t* rp = (const FFA_CONST int32_t*)(a.runs + (int64_t)run_off * kRec);
 
   if (total_tiles > 0) {
@@ -364,21 +382,31 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     // exponentials restores the exact max when a tile's scores outgrow it by
     // more than 2^64.  msub_next is the reference the arguments were taken with.
     float msub_next = 0.0f;
+    // soft-capped argument of a raw score (masked scores stay -inf)
+    auto capped = [&](float x) -> float {
+      const float th = tanh_from_2ylog2e(x * cap_arg);
+      return x == -INFINITY ? -INFINITY : a.cap_log2 * th;
+    };
     auto reference = [&](f32x16_t& xa, f32x16_t& xb) {
       if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, xa[i]), xb[i]);
         mx = partner_max(mx);
-        if (m_run == -INFINITY) m_run = mx * c2;
+        if (m_run == -INFINITY) m_run = CAP ? capped(mx) : mx * c2;
       }
       msub_next = (m_run == -INFINITY) ? 0.0f : m_run;
     };
     auto prep = [&](f32x16_t& xa, f32x16_t& xb, int e0, int e1) {
 #pragma unroll
       for (int e = e0; e < e1; ++e) {
-        if (e < 16) xa[e] = __builtin_fmaf(xa[e], c2, -msub_next);
-        else xb[e - 16] = __builtin_fmaf(xb[e - 16], c2, -msub_next);
+        if constexpr (CAP) {
+          if (e < 16) xa[e] = capped(xa[e]) - msub_next;
+          else xb[e - 16] = capped(xb[e - 16]) - msub_next;
+        } else {
+          if (e < 16) xa[e] = __builtin_fmaf(xa[e], c2, -msub_next);
+          else xb[e - 16] = __builtin_fmaf(xb[e - 16], c2, -msub_next);
+        }
       }
     };
     reference(sa0, sb0);
@@ -504,8 +532,25 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const FFA_CONST FwdArgs* ea = (const FFA_CONST FwdArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+s"(ea));
   const float lsum = partner_sum(l_run);
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-  const float lse_v = lsum > 0.0f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+  float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  float lse_v = lsum > 0.0f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+  const int n_sink = ea->n_sink;
+  if (n_sink > 0 && slot < 0 && row_ok) {
+    // sink logits join the denominator (split rows get them in the combine)
+    const float* sp = ea->sink + (int64_t)b * ea->sk_sb + (int64_t)row * ea->sk_st + (int64_t)h * ea->sk_sh;
+    const int64_t ss = ea->sk_ss;
+    float ms = -INFINITY;
+    for (int s = 0; s < n_sink; ++s) ms = fmaxf(ms, sp[s * ss] * kLog2e);
+    const float mk = lsum > 0.0f ? m_run : -INFINITY;
+    const float mt = fmaxf(mk, ms);
+    if (mt != -INFINITY) {
+      const float fk = __builtin_amdgcn_exp2f(mk - mt);  // 0 when the row sees no key
+      float lt = lsum * fk;
+      for (int s = 0; s < n_sink; ++s) lt += __builtin_amdgcn_exp2f(sp[s * ss] * kLog2e - mt);
+      inv = fk / lt;
+      lse_v = (mt + __log2f(lt)) * kLn2;
+    }
+  }
   if (slot < 0) {
     // all the output arguments in one round trip (each use would otherwise
     // reload its own field right before its store)
@@ -596,6 +641,10 @@ __global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
       mx = fmaxf(fmaxf(mx, fmaxf(l0, l1)), fmaxf(l2, l3));
     }
     for (; c < nch; ++c) mx = fmaxf(mx, lsep[(int64_t)c * kSlotsPerItem]);
+    const int row = q0 + p / G, h = h0 + p % G;
+    const float* sp = a.n_sink > 0 ? a.sink + (int64_t)b * a.sk_sb + (int64_t)row * a.sk_st + (int64_t)h * a.sk_sh
+                                    : nullptr;
+    for (int s = 0; s < a.n_sink; ++s) mx = fmaxf(mx, sp[s * a.sk_ss]);
     const float msafe = mx == -INFINITY ? 0.0f : mx;
     float den = 0.0f;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -621,8 +670,9 @@ __global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
       den += w;
       acc += w * x;
     }
+    // sink logits: denominator terms without a value
+    for (int s = 0; s < a.n_sink; ++s) den += __expf(sp[s * a.sk_ss] - msafe);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    const int row = q0 + p / G, h = h0 + p % G;
     bf16x4_t w4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(acc[e] * inv);
@@ -749,14 +799,18 @@ void ffa_plan_destroy(ffa_plan_t plan) { delete plan; }
 ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const void* q, int64_t q_sb, int64_t q_st,
                    int64_t q_sh, const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh, const void* v, int64_t v_sb,
                    int64_t v_st, int64_t v_sh, void* out, int64_t o_sb, int64_t o_st, int64_t o_sh, float* lse,
-                   int64_t l_sb, int64_t l_st, int64_t l_sh, float softmax_scale, void* d_workspace,
-                   size_t workspace_bytes, void* stream) {
+                   int64_t l_sb, int64_t l_st, int64_t l_sh, float softmax_scale, const ffa_attn_extras* extras,
+                   void* d_workspace, size_t workspace_bytes, void* stream) {
   ffa::clear_error();
   if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
   const ffa::Plan& p = plan->plan;
   if (batch < 1) return ffa::set_error(FFA_ERR_ARG, "batch must be >= 1");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return ffa::set_error(FFA_ERR_ARG, "softmax_scale must be finite and > 0");
+  const ffa_status xs = ffa::check_extras(extras, p.total_q > 0);
+  if (xs != FFA_OK) return xs;
+  ffa_attn_extras ex = {};
+  if (extras) ex = *extras;
   if (!d_meta) return ffa::set_error(FFA_ERR_NULL, "d_meta is NULL");
   if (p.total_q > 0 && (!q || !out || !lse)) return ffa::set_error(FFA_ERR_NULL, "q, out and lse must be non-NULL");
   const bool need_kv = p.total_tiles > 0;
@@ -802,13 +856,23 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   fa.batch = batch;
   fa.heads_per_item = p.heads_per_item;
   fa.kv_ratio = p.heads_q / p.heads_kv;
+  const bool cap = ex.softcap > 0.0f;
+  fa.cap_log2 = cap ? (float)((double)ex.softcap * 1.4426950408889634074) : 0.0f;
+  fa.cap_arg = cap ? (float)(2.0 * 1.4426950408889634074 * (double)softmax_scale / (double)ex.softcap) : 0.0f;
+  fa.sink = ex.n_sink > 0 ? ex.sink : nullptr;
+  fa.sk_sb = ex.sink_sb; fa.sk_st = ex.sink_st; fa.sk_ss = ex.sink_ss; fa.sk_sh = ex.sink_sh;
+  fa.n_sink = ex.n_sink;
 
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)((int64_t)p.num_items * batch));
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(ffa_fwd_main<128>, grid, dim3(64 * ffa::kWaves), 0, s, fa);
-  else
-    hipLaunchKernelGGL(ffa_fwd_main<64>, grid, dim3(64 * ffa::kWaves), 0, s, fa);
+  const dim3 blk(64 * ffa::kWaves);
+  if (p.head_dim == 128) {
+    if (cap) hipLaunchKernelGGL((ffa_fwd_main<128, true>), grid, blk, 0, s, fa);
+    else hipLaunchKernelGGL((ffa_fwd_main<128, false>), grid, blk, 0, s, fa);
+  } else {
+    if (cap) hipLaunchKernelGGL((ffa_fwd_main<64, true>), grid, blk, 0, s, fa);
+    else hipLaunchKernelGGL((ffa_fwd_main<64, false>), grid, blk, 0, s, fa);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch ffa_fwd_main");
 
@@ -824,6 +888,9 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     ca.l_sb = l_sb; ca.l_st = l_st; ca.l_sh = l_sh;
     ca.batch = batch;
     ca.heads_per_item = p.heads_per_item;
+    ca.sink = fa.sink;
+    ca.sk_sb = fa.sk_sb; ca.sk_st = fa.sk_st; ca.sk_ss = fa.sk_ss; ca.sk_sh = fa.sk_sh;
+    ca.n_sink = fa.n_sink;
     const dim3 cgrid((unsigned)((int64_t)p.num_combine * batch));
     if (p.head_dim == 128)
       hipLaunchKernelGGL(ffa_combine<128>, cgrid, dim3(256), 0, s, ca);

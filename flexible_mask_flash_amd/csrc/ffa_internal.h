@@ -94,6 +94,8 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
                       int32_t num_cus, uint32_t flags, Plan* plan);
 
 ffa_status set_error(ffa_status st, const std::string& msg);
+// Validates the optional sink / softcap arguments (NULL: none).
+ffa_status check_extras(const ffa_attn_extras* ex, bool has_rows);
 void clear_error();
 const char* last_error();
 

@@ -234,6 +234,15 @@ ffa_status set_error(ffa_status st, const std::string& msg) {
   return st;
 }
 void clear_error() { g_last_error.clear(); }
+
+ffa_status check_extras(const ffa_attn_extras* ex, bool has_rows) {
+  if (!ex) return FFA_OK;
+  if (!(ex->softcap >= 0.0f) || !std::isfinite(ex->softcap))
+    return set_error(FFA_ERR_ARG, "softcap must be finite and >= 0 (0: off)");
+  if (ex->n_sink < 0) return set_error(FFA_ERR_ARG, "n_sink must be >= 0");
+  if (ex->n_sink > 0 && has_rows && !ex->sink) return set_error(FFA_ERR_NULL, "n_sink > 0 but sink is NULL");
+  return FFA_OK;
+}
 const char* last_error() { return g_last_error.c_str(); }
 
 ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* mask_types,

@@ -76,6 +76,29 @@ typedef enum {
   FFA_ERR_ARG = 11         /* any other invalid argument (batch, scale, plan state)        */
 } ffa_status;
 
+/*
+ * Optional arguments of ffa_fwd / ffa_bwd (pass NULL for none; zero fields are
+ * "off").  MagiAttention quickstart, "Single-GPU Flex-Flash-Attention": the FFA
+ * call takes an optional fp32 `sink` of [S_sink, Hq] logits (or [Tq, S_sink, Hq]
+ * per row in the extension functions' "ssh" layout) and a `softcap` (0 = off).
+ * Readings (the pages name them without formulas):
+ *   sink    each logit adds exp(sink) to the row's softmax denominator and
+ *           carries no value; it is neither scaled nor capped.  lse includes
+ *           it; a row that sees no key gets out = 0 and lse = ln sum exp(sink).
+ *   softcap score s = softmax_scale q.k becomes softcap * tanh(s / softcap).
+ * sink element (b, row, s, h) is at sink[b*sink_sb + row*sink_st + s*sink_ss +
+ * h*sink_sh] (sink_st = 0: the same logits for every row).  ffa_bwd writes
+ * d sink to dsink with the same strides when dsink is not NULL (summed over
+ * rows when sink_st == 0, in a fixed order).
+ */
+typedef struct {
+  const float* sink;
+  float* dsink;
+  int64_t sink_sb, sink_st, sink_ss, sink_sh;
+  int32_t n_sink;   /* sink logits per (row, head); 0: no sink */
+  float softcap;    /* 0: off; must be finite and >= 0 */
+} ffa_attn_extras;
+
 /* Opaque host plan; immutable after ffa_plan, safe to share between threads. */
 typedef struct ffa_plan_s* ffa_plan_t;
 
@@ -159,6 +182,7 @@ ffa_status ffa_plan_export(ffa_plan_t plan, void* h_meta, size_t meta_bytes);
  *   lse: fp32, (b, t, h) at lse[b*l_sb + t*l_st + h*l_sh]
  * q, k, v, out bases and their strides must be multiples of 8 elements (16 B).
  * softmax_scale must be finite and > 0 (callers resolve "None" to 1/sqrt(D)).
+ * extras: sink / softcap (see ffa_attn_extras), NULL for plain attention.
  * d_meta: the buffer filled by ffa_plan_upload.  d_workspace: workspace_bytes
  * >= batch * info.workspace_bytes, may be NULL when that is 0.
  * Kernels are enqueued on `stream` (a hipStream_t); the call does not block.
@@ -170,8 +194,8 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
                    const void* v, int64_t v_sb, int64_t v_st, int64_t v_sh,
                    void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
                    float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
-                   float softmax_scale, void* d_workspace, size_t workspace_bytes,
-                   void* stream);
+                   float softmax_scale, const ffa_attn_extras* extras,
+                   void* d_workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward.  The derivative of the operation above for a loss L with
@@ -191,7 +215,9 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
  * d_workspace: >= batch * info.bwd_workspace_bytes bytes of device memory
  * (fp32 lse * log2 e and rowsum(dout * out) per head and row).  The plan must
  * have been built with FFA_PLAN_BACKWARD (FFA_ERR_ARG otherwise); token
- * strides of q, k, v and dout must be below 2^24 elements.
+ * strides of q, k, v and dout must be below 2^24 elements.  extras: the same
+ * sink / softcap as the forward call (dS is multiplied by 1 - tanh^2 under a
+ * softcap; d sink = -sum_i exp(sink - lse) * rowsum(dout * out)).
  */
 ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
                    const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
@@ -203,8 +229,8 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
                    void* dq, int64_t dq_sb, int64_t dq_st, int64_t dq_sh,
                    void* dk, int64_t dk_sb, int64_t dk_st, int64_t dk_sh,
                    void* dv, int64_t dv_sb, int64_t dv_st, int64_t dv_sh,
-                   float softmax_scale, void* d_workspace, size_t workspace_bytes,
-                   void* stream);
+                   float softmax_scale, const ffa_attn_extras* extras,
+                   void* d_workspace, size_t workspace_bytes, void* stream);
 
 void ffa_plan_destroy(ffa_plan_t plan);
 const char* ffa_status_string(ffa_status status);

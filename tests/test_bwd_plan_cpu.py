@@ -10,6 +10,8 @@ The backward plan holds two worklists (include/ffa.h, FFA_PLAN_BACKWARD):
   Visited once per query head of the kv head, it must cover the mask of every
   query head exactly once, too.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -173,7 +175,7 @@ def test_bwd_rejects_bad_arguments_without_launching():
         t = lambda n: (a[n], 0, a["st"], a["sh"])
         args = [*t("q"), *t("k"), *t("v"), *t("out"), a["lse"], 0, 2, 1, *t("dout"), *t("dq"), *t("dk"), *t("dv")]
         return lib.ffa_bwd(plan.handle if plan is not None else None, a["meta"], a["batch"], *args, a["scale"],
-                           a["ws"], a["wsb"], None)
+                           a.get("ex"), a["ws"], a["wsb"], None)
 
     assert call(plan=pf) == 11          # planned without FFA_PLAN_BACKWARD
     assert call(plan=None) == 1
@@ -187,3 +189,8 @@ def test_bwd_rejects_bad_arguments_without_launching():
     assert call(dq=fake + 4) == 10
     assert call(st=2 * 128 + 2) == 10
     assert call(st=(1 << 24) * 8) == 11  # token stride beyond the 32-bit tile addressing
+    ex = ffa.AttnExtras()
+    ex.n_sink = 1  # no sink pointer
+    assert call(ex=ctypes.byref(ex)) == 1
+    ex.n_sink, ex.softcap = 0, float("inf")
+    assert call(ex=ctypes.byref(ex)) == 11

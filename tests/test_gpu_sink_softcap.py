@@ -1,0 +1,199 @@
+"""GPU parity of attention sink and soft-capping through the C ABI (forward and backward)
+against the fp64 oracle (``oracle.attend`` / ``attend_backward`` with sink / softcap).
+
+Forward tolerances as for plain attention: out max-abs <= 2e-2, mean-abs <= 2e-3,
+lse abs <= 1e-3.  Backward: the FlagAttention rule of test_gpu_bwd (error at most
+twice that of the same-precision PyTorch backward, plus 1e-3 of max(max|ref|, 0.01)),
+for dq, dk, dv and d sink.  Sink layouts: "sh" [S_sink, Hq] (shared by every row) and
+"ssh" [Tq, S_sink, Hq] (per row).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+OUT_MAX, OUT_MEAN, LSE_ABS = 2e-2, 2e-3, 1e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_sink(p, layout, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    shape = (n, p.heads_q) if layout == "sh" else (p.total_q, n, p.heads_q)
+    return 2.0 * torch.randn(shape, generator=g, dtype=torch.float32)
+
+
+def fwd(ffa, p, q, k, v, sink, layout, cap, **kw):
+    dev = torch.device("cuda", 0)
+    out, lse = ffa.flex_flash_attn_fwd(q.to(dev), k.to(dev), v.to(dev), p.q_ranges, p.k_ranges, p.mask_types,
+                                       sink=sink.to(dev) if sink is not None else None, sink_layout=layout,
+                                       softcap=cap, **kw)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def check_fwd(out, lse, ref_out, ref_lse, what):
+    o = out.double().numpy()
+    l = lse.double().numpy()
+    assert not np.isnan(o).any() and not np.isnan(l).any(), f"{what}: NaN"
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(l), empty), f"{what}: -inf pattern of lse differs"
+    err = np.abs(o - ref_out)
+    lerr = np.abs(l[~empty] - ref_lse[~empty]) if (~empty).any() else np.zeros(1)
+    log(f"  {what}: out max {err.max():.3e} mean {err.mean():.3e} | lse max {lerr.max():.3e}")
+    assert err.max() <= OUT_MAX and err.mean() <= OUT_MEAN and lerr.max() <= LSE_ABS, what
+
+
+CASES = [(layout, n, cap) for layout in ("sh", "ssh") for n, cap in ((1, 0.0), (3, 0.0), (2, 8.0))] + \
+        [(None, 0, 8.0), (None, 0, 30.0)]
+
+
+@pytest.mark.parametrize("layout,n,cap", CASES)
+@pytest.mark.parametrize("seed", range(3))
+def test_forward_sink_softcap_random_slices(gpu_lib, seed, layout, n, cap):
+    rng = np.random.default_rng(1500 + seed)
+    tq, tk = int(rng.integers(1, 500)), int(rng.integers(1, 500))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    p = W.random_problem(1500 + seed, tq, tk, hq, hkv, d, n_types=4)
+    q, k, v = W.make_qkv(p)
+    q = q * 3  # scores large enough for the cap to bend them
+    sink = make_sink(p, layout, n, seed) if layout else None
+    out, lse = fwd(gpu_lib, p, q, k, v, sink, layout or "sh", cap)
+    ref = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink, sink_layout=layout or "sh",
+                        softcap=cap)
+    check_fwd(out, lse, *ref, f"seed {seed} sink {layout}/{n} cap {cap}")
+
+
+@pytest.mark.parametrize("layout", ["sh", "ssh"])
+def test_forward_sink_on_split_rows(gpu_lib, layout):
+    # forced split-K: the sinks join in the combine kernel
+    p = W.make_problem("split", 64, 6000, 4, 1, 128, [((0, 64), (0, 6000), W.CAUSAL)], seed=5)
+    q, k, v = W.make_qkv(p)
+    sink = make_sink(p, layout, 2, 7)
+    out, lse = fwd(gpu_lib, p, q, k, v, sink, layout, 5.0, split_tiles=16)
+    plan = gpu_lib._plan_cache[next(reversed(gpu_lib._plan_cache))]
+    assert plan.info["num_split_items"] > 0
+    ref = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink, sink_layout=layout, softcap=5.0)
+    check_fwd(out, lse, *ref, f"split, sink {layout}")
+
+
+def test_rows_without_keys_take_the_sink_normaliser(gpu_lib):
+    p = W.make_problem("holes", 300, 300, 2, 1, 64, [((100, 200), (0, 150), W.CAUSAL)], seed=3)
+    q, k, v = W.make_qkv(p)
+    sink = make_sink(p, "sh", 2, 3)
+    out, lse = fwd(gpu_lib, p, q, k, v, sink, "sh", 0.0)
+    want = torch.logsumexp(sink.double(), dim=0).numpy()
+    assert (out[:100] == 0).all() and (out[200:] == 0).all()
+    np.testing.assert_allclose(lse[:100].double().numpy(), np.broadcast_to(want, (100, 2)), atol=1e-5)
+    ref = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink)
+    check_fwd(out, lse, *ref, "holes with sink")
+
+
+def test_forward_full_size_packed_docs_sampled_with_sink_and_cap(gpu_lib):
+    p = W.config(3)
+    q, k, v = W.make_qkv(p)
+    sink = make_sink(p, "sh", 4, 11)
+    out, lse = fwd(gpu_lib, p, q, k, v, sink, "sh", 20.0)
+    rows = W.sample_rows(p, 96, seed=9)
+    ref = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, rows=rows, sink=sink, softcap=20.0)
+    check_fwd(out[rows], lse[rows], *ref, "packed docs, sampled rows")
+
+
+# ---------------------------------------------------------------- backward
+
+def torch_bf16_grads(p, q, k, v, dout, sink, layout, cap):
+    """Same-precision PyTorch backward on the CPU: bf16 autograd with the oracle's mask,
+    the cap as cap*tanh(s/cap) and the sinks as extra score columns with zero value."""
+    mask = torch.from_numpy(oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k))
+    has = mask.any(1)
+    rep = p.heads_q // p.heads_kv
+    sc = 1.0 / p.head_dim ** 0.5
+    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
+    sk = sink.clone().requires_grad_(True) if sink is not None else None
+    a = qq.permute(1, 0, 2)
+    b = kk.repeat_interleave(rep, 1).permute(1, 2, 0).contiguous()
+    c = vv.repeat_interleave(rep, 1).permute(1, 0, 2).contiguous()
+    s = torch.matmul(a, b) * sc
+    if cap:
+        s = cap * torch.tanh(s / cap)
+    if sk is not None:
+        s = s.masked_fill(~mask[None], float("-inf"))
+        extra = (sk.t()[:, None, :].expand(-1, p.total_q, -1) if layout == "sh" else sk.permute(2, 0, 1))
+        full = torch.cat([s, extra.to(torch.bfloat16)], dim=-1)
+        pr = torch.softmax(full, dim=-1)[..., :p.total_k]
+        o = torch.matmul(pr, c)
+    else:
+        m2 = mask | ~has[:, None]
+        s = s.masked_fill(~m2[None], float("-inf"))
+        o = torch.matmul(torch.softmax(s, dim=-1), c) * has[None, :, None]
+    (o.permute(1, 0, 2).float() * dout.float()).sum().backward()
+    res = [x.grad.double().numpy() for x in (qq, kk, vv)]
+    if sk is not None:
+        res.append(sk.grad.double().numpy())
+    return res
+
+
+@pytest.mark.parametrize("layout,n,cap", [("sh", 2, 0.0), ("ssh", 1, 0.0), (None, 0, 6.0), ("sh", 3, 6.0)])
+@pytest.mark.parametrize("seed", range(3))
+def test_backward_sink_softcap(gpu_lib, seed, layout, n, cap):
+    rng = np.random.default_rng(1600 + seed)
+    tq, tk = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    p = W.random_problem(1600 + seed, tq, tk, hq, hkv, d, n_types=4)
+    q, k, v = W.make_qkv(p)
+    q = q * 3
+    dout = W.make_dout(p)
+    sink = make_sink(p, layout, n, seed) if layout else None
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dd = q.to(dev), k.to(dev), v.to(dev), dout.to(dev)
+    sd = sink.to(dev) if sink is not None else None
+    lay = layout or "sh"
+    out, lse = gpu_lib.flex_flash_attn_fwd(qd, kd, vd, p.q_ranges, p.k_ranges, p.mask_types, sink=sd,
+                                           sink_layout=lay, softcap=cap)
+    g = gpu_lib.flex_flash_attn_bwd(dd, qd, kd, vd, out, lse, p.q_ranges, p.k_ranges, p.mask_types, sink=sd,
+                                    sink_layout=lay, softcap=cap)
+    torch.cuda.synchronize()
+    ref = oracle.attend_backward(q, k, v, dout, p.q_ranges, p.k_ranges, p.mask_types, sink=sink, sink_layout=lay,
+                                 softcap=cap)
+    tb = torch_bf16_grads(p, q, k, v, dout, sink, lay, cap)
+    names = ("dq", "dk", "dv", "dsink")[:len(ref)]
+    for name, x, r, t in zip(names, g, ref, tb):
+        xn = x.double().cpu().numpy()
+        assert not np.isnan(xn).any(), name
+        err, et = np.abs(xn - r), np.abs(t - r)
+        allow = 1e-3 * max(np.abs(r).max(), 1e-2)
+        log(f"  seed {seed} sink {layout}/{n} cap {cap} {name}: max {err.max():.3e} (torch bf16 {et.max():.3e}) "
+            f"mean {err.mean():.3e} (torch bf16 {et.mean():.3e})")
+        assert err.max() <= 2.0 * et.max() + allow, name
+        assert err.mean() <= 2.0 * et.mean() + allow, name
+
+
+def test_autograd_with_sink_and_cap(gpu_lib):
+    p = W.random_problem(21, 250, 300, 4, 2, 128, n_types=4)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x.to(dev) for x in W.make_qkv(p))
+    dout = W.make_dout(p).to(dev)
+    sink = make_sink(p, "sh", 2, 21).to(dev)
+    qa, ka, va, sa = (x.clone().requires_grad_(True) for x in (q, k, v, sink))
+    out, lse = gpu_lib.flex_flash_attn_func(qa, ka, va, p.q_ranges, p.k_ranges, p.mask_types, sink=sa, softcap=7.0)
+    out.backward(dout)
+    out2, lse2 = gpu_lib.flex_flash_attn_fwd(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink, softcap=7.0)
+    dq, dk, dv, ds = gpu_lib.flex_flash_attn_bwd(dout, q, k, v, out2, lse2, p.q_ranges, p.k_ranges, p.mask_types,
+                                                 sink=sink, softcap=7.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), out2) and torch.equal(lse, lse2)
+    assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)
+    assert torch.equal(sa.grad, ds)

@@ -321,7 +321,7 @@ def test_fwd_rejects_bad_arguments_without_launching(lib):
         a.update(kw)
         return lib.ffa_fwd(p.handle, a["meta"], a["batch"], a["q"], 0, a["st"], a["sh"], a["k"], 0, a["st"],
                            a["sh"], a["v"], 0, a["st"], a["sh"], a["out"], 0, a["st"], a["sh"], a["lse"], 0, 2, 1,
-                           a["scale"], a["ws"], a["wsb"], None)
+                           a["scale"], a.get("ex"), a["ws"], a["wsb"], None)
     assert call(batch=0) == 11
     assert call(scale=float("nan")) == 11
     assert call(scale=0.0) == 11
@@ -331,9 +331,19 @@ def test_fwd_rejects_bad_arguments_without_launching(lib):
     assert call(q=fake + 2) == 10
     assert call(st=2 * 128 + 4) == 10
     assert lib.ffa_fwd(None, fake, 1, fake, 0, 1, 1, fake, 0, 1, 1, fake, 0, 1, 1, fake, 0, 1, 1, fake, 0, 1, 1,
-                       0.1, None, 0, None) == 1
+                       0.1, None, None, 0, None) == 1
+    # sink / softcap arguments
+    ex = ffa.AttnExtras()
+    ex.softcap = -1.0
+    assert call(ex=ctypes.byref(ex)) == 11
+    ex.softcap = float("nan")
+    assert call(ex=ctypes.byref(ex)) == 11
+    ex.softcap, ex.n_sink = 0.0, -1
+    assert call(ex=ctypes.byref(ex)) == 11
+    ex.n_sink = 2  # sink pointer NULL
+    assert call(ex=ctypes.byref(ex)) == 1
     # a split plan without workspace
     ps = ffa.Plan([[0, 32]], [[0, 8192]], [0], 32, 8192, 4, 1, 128, num_cus=NCU, split_tiles=16)
     assert ps.info["workspace_bytes"] > 0
     assert lib.ffa_fwd(ps.handle, fake, 1, fake, 0, 512, 128, fake, 0, 128, 128, fake, 0, 128, 128, fake, 0, 512,
-                       128, fake, 0, 4, 1, 0.1, None, 0, None) == 7
+                       128, fake, 0, 4, 1, 0.1, None, None, 0, None) == 7
