@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 METRIC = "masked-attn fwd TFLOPS (unmasked FLOPs) and % of MI355X bf16 MFMA peak"
-WORKLOADS = {name: i for i, name in __import__("workloads").CONFIG_NAMES.items()}
+WORKLOADS = sorted(list(__import__("workloads").CONFIG_NAMES.values()) + list(__import__("workloads").EXTRA_WORKLOADS))
 
 
 def parse():
@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--min-warmup-seconds", type=float, default=0.3,
                     help="keep warming up (untimed) until this much GPU time has passed: the clocks ramp "
                          "over the first tens of milliseconds of sustained load")
-    ap.add_argument("--workload", default="packed_docs", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="packed_docs", choices=WORKLOADS)
     ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
@@ -155,8 +155,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
     dev = torch.device("cuda", 0)
-    cfg = WORKLOADS[args.workload]
-    p = W.config(cfg)
+    p = W.workload(args.workload)
     q, k, v = W.make_qkv(p)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
 

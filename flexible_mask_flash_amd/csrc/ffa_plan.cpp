@@ -297,6 +297,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
       for (size_t ib = ia + 1; ib < ord.size(); ++ib) {
         const Slice& b = slices[ord[ib]];
         if (b.qs >= a.qe) break;
+        if (b.ks >= a.ke || a.ks >= b.ke) continue;  // key ranges apart: nothing shared
         if (max_shared_keys(a, b) > 0)
           return set_error(FFA_ERR_OVERLAP, "slices " + std::to_string(a.id) + " and " + std::to_string(b.id) +
                                                 " overlap");

@@ -194,3 +194,24 @@ def test_bwd_rejects_bad_arguments_without_launching():
     assert call(ex=ctypes.byref(ex)) == 1
     ex.n_sink, ex.softcap = 0, float("inf")
     assert call(ex=ctypes.byref(ex)) == 11
+
+
+@pytest.mark.parametrize("qb,kb", [(64, 64), (16, 64), (64, 16), (64, 1), (8, 64)])
+def test_block_sparse_worklists_cover_mask_exactly_once(qb, kb):
+    # uniform block-sparse masks: many tiny FULL slices (forward and both backward worklists)
+    p = W.block_sparse_problem(256, qb, kb, 0.25, 4, 1, 64, seed=qb * 100 + kb)
+    check_bwd(p)
+    from tests.test_library_cpu import check_plan
+    check_plan(p)
+
+
+def test_block_sparse_full_size_plans_quickly():
+    import time
+    for name in ("block_sparse", "block_sparse_k16", "block_sparse_q16"):
+        p = W.workload(name)
+        t0 = time.perf_counter()
+        plan = make_plan(p)
+        dt = time.perf_counter() - t0
+        assert plan.info["visible_pairs"] == int(oracle.count_visible_pairs(
+            p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k)) if p.num_slices < 3000 else True
+        assert dt < 5.0, f"{name}: planning took {dt:.2f} s for {p.num_slices} slices"

@@ -224,6 +224,49 @@ def sliding_window_problem(T, w, docs, hq, hkv, d, seed):
     return make_problem(f"window{w}", T, T, hq, hkv, d, sl, seed=seed)
 
 
+def block_sparse_problem(total: int, q_block: int, k_block: int, keep: float, hq: int, hkv: int, d: int,
+                         seed: int, name: Optional[str] = None) -> Problem:
+    """Uniform block-sparse mask over `total` tokens (q = k axis).
+
+    The query axis is cut into blocks of q_block rows and the key axis into blocks
+    of k_block keys; every query block keeps the same number of key blocks,
+    round(keep * number of key blocks) (at least 1), drawn without replacement
+    from numpy.random.default_rng(seed); each kept (query block, key block) cell
+    is one FULL slice.  The block-size pairs of the MagiAttention experiment
+    notes (uniform block sparse: 64/64 and 128/128, small query blocks 8-32
+    against 64-key blocks, small key blocks 1-64 against 64-row blocks) name the
+    shapes; the kept fraction is not given there (a quarter is used here).
+    """
+    rng = np.random.default_rng(seed)
+    nq, nk = -(-total // q_block), -(-total // k_block)
+    n_keep = max(1, int(round(keep * nk)))
+    sl = []
+    for bq in range(nq):
+        qs, qe = bq * q_block, min(total, (bq + 1) * q_block)
+        for bk in sorted(rng.choice(nk, size=n_keep, replace=False).tolist()):
+            sl.append(((qs, qe), (bk * k_block, min(total, (bk + 1) * k_block)), FULL))
+    return make_problem(name or f"block_sparse_q{q_block}_k{k_block}", total, total, hq, hkv, d, sl, seed=seed)
+
+
+# Extra workloads beyond the five configurations (by name): block-sparse planner
+# stress cases at the packed-document head shape (Hq 32, Hkv 8, D 128).
+EXTRA_WORKLOADS = {
+    "block_sparse": lambda: block_sparse_problem(16384, 64, 64, 0.25, 32, 8, 128, 31, "block_sparse"),
+    "block_sparse_k16": lambda: block_sparse_problem(16384, 64, 16, 0.25, 32, 8, 128, 32, "block_sparse_k16"),
+    "block_sparse_q16": lambda: block_sparse_problem(16384, 16, 64, 0.25, 32, 8, 128, 33, "block_sparse_q16"),
+}
+
+
+def workload(name: str) -> Problem:
+    """A configuration by name (CONFIG_NAMES) or an extra workload (EXTRA_WORKLOADS)."""
+    for i, n in CONFIG_NAMES.items():
+        if n == name:
+            return config(i)
+    if name in EXTRA_WORKLOADS:
+        return EXTRA_WORKLOADS[name]()
+    raise ValueError(f"unknown workload {name!r}")
+
+
 def make_dout(p: Problem, seed: Optional[int] = None):
     """Draw an upstream gradient dout [Tq,Hq,D] (CPU, bfloat16) for problem `p`."""
     import torch
