@@ -166,8 +166,15 @@ __device__ __forceinline__ int swz_b(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
+// Occupancy: the query-major kernel fits 256 registers (two waves per SIMD, so one
+// wave's VALU work hides behind the other's MFMAs); the key-major kernel holds
+// two fp32 accumulators and the k, v fragments (~480 registers at D = 128; at
+// D = 64 it would spill under 256), one wave per SIMD.
+template <int D, bool KV>
+constexpr int kBwdWaves = KV ? 1 : 2;
+
 template <int D, bool KV, bool CAP>
-__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffa_bwd_main(BwdArgs a) {
+__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(kBwdWaves<D, KV>, kBwdWaves<D, KV>))) void ffa_bwd_main(BwdArgs a) {
   constexpr int BN = kBlockN;          // 64 rows per streamed tile
   constexpr int ROWB = D * 2;          // bytes of one row
   constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -351,7 +358,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 
   // ---- acc^T += T^T X for the streamed tile T at LDS offset OFF (16 rows per
   // MFMA, the reads of step t+1 in flight during the MFMAs of step t)
-  auto trprod = [&](auto off_tag, const bf16x8_t(&xf)[4], f32x16_t(&acc)[DBLK]) {
+  auto trprod = [&](auto off_tag, const bf16x8_t(&xf)[4], f32x16_t(&acc)[DBLK], auto&& hook) {
     constexpr int OFF = decltype(off_tag)::value;
     s16x4_t vlo[2][DBLK], vhi[2][DBLK];
 #pragma unroll
@@ -379,6 +386,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
                             vhi[cur][d][0], vhi[cur][d][1], vhi[cur][d][2], vhi[cur][d][3]};
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), xf[t], acc[d], 0, 0, 0);
       });
+      hook(std::integral_constant<int, t>{});
     });
   };
 
@@ -495,19 +503,39 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       fence(xa);
       fence(xb);
     });
-    // dS = P (X2 - Dd); bf16 operands of the transposed products
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
+    // dS = P (X2 - Dd) and the bf16 operands of the transposed products, one
+    // 16-row step t at a time, so that the VALU work of a step runs behind MFMAs:
+    // key-major, all of dS behind the dV product (which needs only P); query-
+    // major, step t + 1 behind the MFMAs of step t.
+    auto make_ds = [&](int t) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = 8 * t + u;
         const float p = e < 16 ? xa[e] : xb[e - 16];
         const float y = e < 16 ? ya[e] : yb[e - 16];
-        if constexpr (!CAP) pf[t][u] = (__bf16)p;
         sf[t][u] = (__bf16)(p * (y - dval(e)));
       }
-    if constexpr (KV) trprod(std::integral_constant<int, OB>{}, pf, acc2);
-    trprod(std::integral_constant<int, OA>{}, sf, acc1);
+      fence(sf[t]);
+    };
+    if constexpr (!CAP && KV) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = 8 * t + u;
+          pf[t][u] = (__bf16)(e < 16 ? xa[e] : xb[e - 16]);
+        }
+    }
+    if constexpr (KV) {
+      trprod(std::integral_constant<int, OB>{}, pf, acc2, [&](auto t_tag) { make_ds(decltype(t_tag)::value); });
+      trprod(std::integral_constant<int, OA>{}, sf, acc1, [](auto) {});
+    } else {
+      make_ds(0);
+      trprod(std::integral_constant<int, OA>{}, sf, acc1, [&](auto t_tag) {
+        constexpr int t = decltype(t_tag)::value;
+        if constexpr (t + 1 < 4) make_ds(t + 1);
+      });
+    }
   };
 
   if (steps > 0) {
