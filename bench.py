@@ -55,7 +55,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "flexible_mask_flash_amd", "csrc", f)
-                  for f in ("ffa_fwd.hip", "ffa_internal.h", "ffa_plan.cpp")]
+                  for f in ("ffa_fwd.hip", "ffa_device.h", "ffa_internal.h", "ffa_plan.cpp")]
 
 
 def kernel_source_hash() -> str:
