@@ -163,7 +163,9 @@ __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
 // row offsets in steps of 16 (the rows r + 8 get their own address).
 template <int D>
 __device__ __forceinline__ int swz_b(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+         : D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
+                   : ((r >> 2) & 3);  // 64-byte rows: four rows per bank window already
 }
 
 // Occupancy: the query-major kernel fits 256 registers (two waves per SIMD, so one
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   constexpr int NLD = TILE / (1024 * W);  // DMA instructions per thread per tile
   constexpr int RPL = 1024 * W / ROWB;    // rows between consecutive DMA instructions
   static_assert(NLD * 1024 * W == TILE, "DMA split");
-  static_assert(BN == 64 && (D == 64 || D == 128), "tile shape");
+  static_assert(BN == 64 && (D == 32 || D == 64 || D == 128), "tile shape");
   // LDS: A0 | B0 | A1 | B1 (double-buffered tiles), then (key-major) L and Dd of
   // the 64 streamed rows per buffer, 1 KiB each (one DMA instruction writes
   // 64 x 16 bytes; the first 256 count).  The L / Dd block has its own base
@@ -657,10 +659,9 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     const int ppb = 256 / (p.head_dim / 8);
     const int64_t pairs = (int64_t)p.total_q * p.heads_q;
     const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
-    if (p.head_dim == 128)
-      hipLaunchKernelGGL(ffa_bwd_pre<128>, grid, dim3(256), 0, s, pa);
-    else
-      hipLaunchKernelGGL(ffa_bwd_pre<64>, grid, dim3(256), 0, s, pa);
+    dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+      hipLaunchKernelGGL(ffa_bwd_pre<decltype(d_tag)::value>, grid, dim3(256), 0, s, pa);
+    });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_pre");
   }
@@ -706,13 +707,11 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     ba.items = dq_items;
     ba.runs = dq_runs;
     const dim3 grid((unsigned)((int64_t)p.num_dq_items * batch));
-    if (p.head_dim == 128) {
-      if (cap) hipLaunchKernelGGL((ffa_bwd_main<128, false, true>), grid, block, 0, s, ba);
-      else hipLaunchKernelGGL((ffa_bwd_main<128, false, false>), grid, block, 0, s, ba);
-    } else {
-      if (cap) hipLaunchKernelGGL((ffa_bwd_main<64, false, true>), grid, block, 0, s, ba);
-      else hipLaunchKernelGGL((ffa_bwd_main<64, false, false>), grid, block, 0, s, ba);
-    }
+    dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+      constexpr int D = decltype(d_tag)::value;
+      if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, false, true>), grid, block, 0, s, ba);
+      else hipLaunchKernelGGL((ffa_bwd_main<D, false, false>), grid, block, 0, s, ba);
+    });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dq)");
   }
@@ -720,13 +719,11 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     ba.items = kv_items;
     ba.runs = kv_runs;
     const dim3 grid((unsigned)((int64_t)p.num_kv_items * batch));
-    if (p.head_dim == 128) {
-      if (cap) hipLaunchKernelGGL((ffa_bwd_main<128, true, true>), grid, block, 0, s, ba);
-      else hipLaunchKernelGGL((ffa_bwd_main<128, true, false>), grid, block, 0, s, ba);
-    } else {
-      if (cap) hipLaunchKernelGGL((ffa_bwd_main<64, true, true>), grid, block, 0, s, ba);
-      else hipLaunchKernelGGL((ffa_bwd_main<64, true, false>), grid, block, 0, s, ba);
-    }
+    dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+      constexpr int D = decltype(d_tag)::value;
+      if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true>), grid, block, 0, s, ba);
+      else hipLaunchKernelGGL((ffa_bwd_main<D, true, false>), grid, block, 0, s, ba);
+    });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dk, dv)");
   }

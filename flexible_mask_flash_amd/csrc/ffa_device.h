@@ -113,5 +113,14 @@ __device__ __forceinline__ void tile_next(TileIt& t, const FFA_CONST int32_t* rp
   }
 }
 
+// Host: calls f(std::integral_constant<int, D>{}) for the head dim d (32, 64 or 128;
+// the planner has validated it).
+template <typename F>
+inline void dispatch_head_dim(int d, F&& f) {
+  if (d == 128) f(std::integral_constant<int, 128>{});
+  else if (d == 64) f(std::integral_constant<int, 64>{});
+  else f(std::integral_constant<int, 32>{});
+}
+
 }  // namespace dev
 }  // namespace ffa

@@ -112,13 +112,16 @@ constexpr float kOverflow = 18446744073709551616.0f;  // 2^64
 //  r..r+15, so the XOR spreads those 16 rows over all 16-byte bank groups.
 //  V rows are read transposed: a 16-lane group reads two chunks of four
 //  consecutive rows, so four consecutive rows are spread by 4 chunks.
+//  At D = 32 a row is 64 bytes, so four consecutive rows already fill one
+//  256-byte bank window: the transposed V reads need no swizzle, and the K rows
+//  r .. r+15 only need the XOR by their window index.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return D == 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+  return D == 128 ? ((r & 3) << 2) : D == 64 ? (((r >> 1) & 1) << 2) : 0;
 }
 
 template <int D, bool CAP>
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   static_assert(NLD * 1024 * W == TILE, "DMA split");
   constexpr int QSLOTS = 2 * KSTEPS;   // MFMAs of one K Q^T tile
   constexpr int EPQ = 32 / QSLOTS;     // score elements exponentiated per K Q^T MFMA
-  static_assert(BN == 64 && (D == 64 || D == 128), "tile shape");
+  static_assert(BN == 64 && (D == 32 || D == 64 || D == 128), "tile shape");
   // one LDS array: K0 | V0 | K1 | V1; every read offset is a compile-time immediate
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   constexpr int kOffK[2] = {0, 2 * TILE};
@@ -866,13 +869,11 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)((int64_t)p.num_items * batch));
   const dim3 blk(64 * ffa::kWaves);
-  if (p.head_dim == 128) {
-    if (cap) hipLaunchKernelGGL((ffa_fwd_main<128, true>), grid, blk, 0, s, fa);
-    else hipLaunchKernelGGL((ffa_fwd_main<128, false>), grid, blk, 0, s, fa);
-  } else {
-    if (cap) hipLaunchKernelGGL((ffa_fwd_main<64, true>), grid, blk, 0, s, fa);
-    else hipLaunchKernelGGL((ffa_fwd_main<64, false>), grid, blk, 0, s, fa);
-  }
+  dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    if (cap) hipLaunchKernelGGL((ffa_fwd_main<D, true>), grid, blk, 0, s, fa);
+    else hipLaunchKernelGGL((ffa_fwd_main<D, false>), grid, blk, 0, s, fa);
+  });
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch ffa_fwd_main");
 
@@ -892,10 +893,9 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     ca.sk_sb = fa.sk_sb; ca.sk_st = fa.sk_st; ca.sk_ss = fa.sk_ss; ca.sk_sh = fa.sk_sh;
     ca.n_sink = fa.n_sink;
     const dim3 cgrid((unsigned)((int64_t)p.num_combine * batch));
-    if (p.head_dim == 128)
-      hipLaunchKernelGGL(ffa_combine<128>, cgrid, dim3(256), 0, s, ca);
-    else
-      hipLaunchKernelGGL(ffa_combine<64>, cgrid, dim3(256), 0, s, ca);
+    dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+      hipLaunchKernelGGL(ffa_combine<decltype(d_tag)::value>, cgrid, dim3(256), 0, s, ca);
+    });
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch ffa_combine");
   }

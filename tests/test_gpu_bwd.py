@@ -262,3 +262,13 @@ def test_autograd_function_matches_direct_call(gpu_lib):
     torch.cuda.synchronize()
     assert torch.equal(out.detach(), out2)
     assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_bwd_head_dim_32(gpu_lib, seed):
+    rng = np.random.default_rng(1800 + seed)
+    tq, tk = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    p = W.random_problem(1800 + seed, tq, tk, hq, hkv, 32, n_types=4)
+    case(gpu_lib, p, f"D 32 random {seed}")

@@ -379,3 +379,25 @@ def test_product_path_has_no_fallback(gpu_lib):
     assert ffa._lib is not None
     src = open(ffa.__file__).read()
     assert "import oracle" not in src and "from oracle" not in src
+
+
+# ---------------------------------------------------------------- head_dim 32
+
+@pytest.mark.parametrize("seed", range(4))
+def test_head_dim_32_random_slices(gpu_lib, seed):
+    rng = np.random.default_rng(1700 + seed)
+    tq, tk = int(rng.integers(1, 600)), int(rng.integers(1, 600))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    p = W.random_problem(1700 + seed, tq, tk, hq, hkv, 32, n_types=4)
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v, split_tiles=3 if seed == 3 else 0)
+    compare(out, lse, *oracle_ref(p, q, k, v), what=f"D 32 random {seed}")
+
+
+def test_head_dim_32_packed_docs_scaled(gpu_lib):
+    p = W.scaled(3, 8)
+    p.head_dim = 32
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v)
+    compare(out, lse, *oracle_ref(p, q, k, v), what="D 32 config 3 / 8")

@@ -197,3 +197,13 @@ def test_autograd_with_sink_and_cap(gpu_lib):
     assert torch.equal(out.detach(), out2) and torch.equal(lse, lse2)
     assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)
     assert torch.equal(sa.grad, ds)
+
+
+def test_head_dim_32_sink_and_cap(gpu_lib):
+    p = W.random_problem(1900, 300, 350, 4, 2, 32, n_types=4)
+    q, k, v = W.make_qkv(p)
+    q = q * 3
+    sink = make_sink(p, "sh", 2, 19)
+    out, lse = fwd(gpu_lib, p, q, k, v, sink, "sh", 6.0)
+    ref = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink, softcap=6.0)
+    check_fwd(out, lse, *ref, "D 32 sink + cap")

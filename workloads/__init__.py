@@ -254,7 +254,15 @@ EXTRA_WORKLOADS = {
     "block_sparse": lambda: block_sparse_problem(16384, 64, 64, 0.25, 32, 8, 128, 31, "block_sparse"),
     "block_sparse_k16": lambda: block_sparse_problem(16384, 64, 16, 0.25, 32, 8, 128, 32, "block_sparse_k16"),
     "block_sparse_q16": lambda: block_sparse_problem(16384, 16, 64, 0.25, 32, 8, 128, 33, "block_sparse_q16"),
+    "packed_docs_d32": lambda: _with_head_dim(config(3), 32, "packed_docs_d32"),
 }
+
+
+def _with_head_dim(p: Problem, d: int, name: str) -> Problem:
+    """The same mask and head counts with another head_dim."""
+    return make_problem(name, p.total_q, p.total_k, p.heads_q, p.heads_kv, d,
+                        [((a, b), (c, e), t) for (a, b), (c, e), t in
+                         zip(p.q_ranges.tolist(), p.k_ranges.tolist(), p.mask_types.tolist())], seed=p.seed)
 
 
 def workload(name: str) -> Problem:
