@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--softcap", type=float, default=0.0, help="soft-capping of the scores (0: off)")
+    ap.add_argument("--total", action="store_true", help="also time the total-attention pass")
     ap.add_argument("--sinks", type=int, default=0, help="sink logits per head (layout sh; 0: none)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward (for profiling its kernels)")
@@ -256,9 +257,46 @@ def main():
     }
     if not args.no_backward:
         res["backward"] = backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink)
+    if args.total:
+        res["total_attention"] = total_leg(args, p, qd, kd, lse, scale, sink)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, q, k, v, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def total_leg(args, p, qd, kd, lse, scale, sink=None):
+    """Time ffa_total_attention (key-major pass: scores and probabilities only) on the same
+    workload with the forward's lse.  FLOPs counted: 2 * D * Hq * visible pairs (one product)."""
+    import torch
+
+    import flexible_mask_flash_amd as ffa
+
+    dev = qd.device
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, backward=True)
+    plan.device_meta(dev)
+    tot = torch.empty((p.total_k, p.heads_q), dtype=torch.float32, device=dev)
+    st = {"q": (0, qd.stride(0), qd.stride(1)), "k": (0, kd.stride(0), kd.stride(1)),
+          "lse": (0, lse.stride(0), lse.stride(1)), "total": (0, tot.stride(0), tot.stride(1))}
+    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q)
+
+    def step():
+        ffa.run_total(plan, qd, kd, lse, tot, st, 1, scale, extras)
+
+    for _ in range(max(3, args.warmup)):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 2.0 * p.head_dim * p.heads_q * plan.info["visible_pairs"]
+    return {"value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOPS", "ms_per_step": round(ms, 4),
+            "flops_per_step": flops}
 
 
 def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink=None):

@@ -37,6 +37,7 @@ __all__ = [
     "flex_flash_attn_fwd",
     "flex_flash_attn_bwd",
     "flex_flash_attn_func",
+    "flex_total_attention",
     "flash_attention",
     "load_library",
     "library_path",
@@ -130,6 +131,12 @@ _SIGNATURES = [
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
                        _f32, ctypes.POINTER(AttnExtras), _vp, _sz, _vp]),
+    ("ffa_total_attention", _i32, [_vp, _vp, _i32,
+                                   _vp, _i64, _i64, _i64,
+                                   _vp, _i64, _i64, _i64,
+                                   _vp, _i64, _i64, _i64,
+                                   _vp, _i64, _i64, _i64,
+                                   _f32, ctypes.POINTER(AttnExtras), _vp, _sz, _vp]),
     ("ffa_plan_destroy", None, [_vp]),
 ]
 
@@ -437,6 +444,50 @@ def _thd_strides(x):
     return (0, x.stride(0), x.stride(1))
 
 
+def run_total(plan: Plan, q, k, lse, total, strides: dict, batch: int, softmax_scale: float, extras=None):
+    """Call ffa_total_attention.  strides: (sb, st, sh) for q, k, lse and total (total: (b, key, head))."""
+    import torch
+
+    if not plan.backward:
+        raise ValueError("total attention needs a plan built with backward=True (key-major worklist)")
+    dev = q.device
+    s = torch.cuda.current_stream(dev)
+    meta = plan.device_meta(dev, s)
+    ws, ws_bytes = plan.bwd_workspace(dev, batch)
+    st = load_library().ffa_total_attention(
+        plan.handle, meta.data_ptr(), int(batch), q.data_ptr(), *strides["q"], k.data_ptr(), *strides["k"],
+        lse.data_ptr(), *strides["lse"], total.data_ptr(), *strides["total"], float(softmax_scale),
+        ctypes.byref(extras) if extras is not None else None, ws.data_ptr() if ws is not None else None, ws_bytes,
+        s.cuda_stream)
+    _check(st, "ffa_total_attention")
+
+
+def flex_total_attention(q, k, lse, q_ranges, k_ranges, attn_type_map, softmax_scale: Optional[float] = None,
+                         sink=None, sink_layout: str = "sh", softcap: float = 0.0):
+    """Attention probabilities summed over the query axis, per key and query head -> [Tk, Hq] fp32.
+
+    q [Tq,Hq,D], k [Tk,Hkv,D] bf16 and the forward's lse [Tq,Hq] (with the same
+    sink / softcap); FlagAttention's `total` (user guide, "FlashAttention") on
+    packed THD tensors.
+    """
+    import torch
+
+    _require_bf16_cuda("q", q, 3)
+    _require_bf16_cuda("k", k, 3)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (tq, hq):
+        raise ValueError("lse must be float32 [Tq, Hq]")
+    plan = _cached_plan(_host_i32(q_ranges, (2,)), _host_i32(k_ranges, (2,)), _host_i32(attn_type_map, ()),
+                        tq, tk, hq, hkv, d, 0, backward=True)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    total = torch.empty((tk, hq), dtype=torch.float32, device=q.device)
+    strides = {"q": _thd_strides(q), "k": _thd_strides(k), "lse": _thd_strides(lse), "total": _thd_strides(total)}
+    run_total(plan, q, k, lse, total, strides, 1, scale, make_extras(sink, sink_layout, softcap, total_q=tq,
+                                                                     heads_q=hq))
+    return total
+
+
 def flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map,
                         softmax_scale: Optional[float] = None, plan: Optional[Plan] = None, sink=None,
                         sink_layout: str = "sh", softcap: float = 0.0):
@@ -534,21 +585,62 @@ def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
     return _FLEX_FN.apply(q, k, v, sink, plan, scale, sink_layout, float(softcap or 0.0))
 
 
+def _bhmd_strides(x):
+    """(batch, token, head) element strides of a [B, H, T, D] (or [B, H, T]) tensor."""
+    return (x.stride(0), x.stride(2), x.stride(1))
+
+
+_FLASH_FN = None
+
+
+def _flash_function():
+    import torch
+
+    class _FlashAttn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, plan, scale):
+            b, hq, m, d = q.shape
+            out = torch.empty((b, hq, m, d), dtype=torch.bfloat16, device=q.device)
+            lse = torch.empty((b, hq, m), dtype=torch.float32, device=q.device)
+            strides = {n: _bhmd_strides(x) for n, x in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))}
+            run_fwd(plan, q, k, v, out, lse, strides, b, scale)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.plan, ctx.scale = plan, scale
+            ctx.mark_non_differentiable(lse)
+            return out, lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            q, k, v, out, lse = ctx.saved_tensors
+            if dout.stride(-1) != 1 or dout.dtype != torch.bfloat16:
+                dout = dout.to(torch.bfloat16).contiguous()
+            dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+            dk = torch.empty(k.shape, dtype=torch.bfloat16, device=q.device)
+            dv = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device)
+            t = {"q": q, "k": k, "v": v, "out": out, "lse": lse, "dout": dout, "dq": dq, "dk": dk, "dv": dv}
+            run_bwd(ctx.plan, t, {n: _bhmd_strides(x) for n, x in t.items()}, q.shape[0], ctx.scale)
+            return dq, dk, dv, None, None
+
+    return _FlashAttn
+
+
 def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = None, dropout_p: float = 0.0,
                     return_log_normalizer: bool = False, return_total_attention: bool = False,
                     return_seed_offset: bool = False, split_tiles: int = 0):
-    """FlagAttention-style dense attention forward on [B, H, M, D] tensors.
+    """FlagAttention-style dense attention on [B, H, M, D] tensors, differentiable.
 
     q [B,Hq,M,D], k/v [B,Hkv,N,D] bf16; Hq % Hkv == 0; causal is bottom-right
     aligned.  Every batch element is one slice of a shared plan; the kernels
-    read the [B,H,M,D] layout through strides (no copies).
+    read the [B,H,M,D] layout through strides (no copies).  Gradients flow to
+    q, k and v through out (ffa_bwd).  With an auxiliary flag set it returns
+    (out, lse [B,Hq,M] or None, total [B,Hq,N] or None, None, None); total is
+    the attention probabilities summed over the query axis.
     """
     import torch
 
+    global _FLASH_FN
     if dropout_p:
-        raise NotImplementedError("dropout is not supported by this forward")
-    if return_total_attention:
-        raise NotImplementedError("return_total_attention is not supported by this forward")
+        raise NotImplementedError("dropout is not supported")
     if return_seed_offset:
         raise NotImplementedError("return_seed_offset needs dropout, which is not supported")
     _require_bf16_cuda("q", q, 4)
@@ -559,19 +651,20 @@ def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = N
     if v.shape != k.shape or bk != b or dk != d:
         raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     ty = CAUSAL if causal else FULL
+    need_bwd = return_total_attention or (torch.is_grad_enabled() and
+                                          any(x.requires_grad for x in (q, k, v)))
     plan = _cached_plan(np.array([[0, m]], np.int32), np.array([[0, n]], np.int32), np.array([ty], np.int32),
-                        m, n, hq, hkv, d, split_tiles)
+                        m, n, hq, hkv, d, split_tiles, backward=need_bwd)
     scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-    out = torch.empty((b, hq, m, d), dtype=torch.bfloat16, device=q.device)
-    lse = torch.empty((b, hq, m), dtype=torch.float32, device=q.device)
-    strides = {
-        "q": (q.stride(0), q.stride(2), q.stride(1)),
-        "k": (k.stride(0), k.stride(2), k.stride(1)),
-        "v": (v.stride(0), v.stride(2), v.stride(1)),
-        "out": (out.stride(0), out.stride(2), out.stride(1)),
-        "lse": (lse.stride(0), lse.stride(2), lse.stride(1)),
-    }
-    run_fwd(plan, q, k, v, out, lse, strides, b, scale)
-    if return_log_normalizer:
-        return out, lse, None, None, None
-    return out
+    if _FLASH_FN is None:
+        _FLASH_FN = _flash_function()
+    out, lse = _FLASH_FN.apply(q, k, v, plan, scale)
+    if not (return_log_normalizer or return_total_attention):
+        return out
+    total = None
+    if return_total_attention:
+        total = torch.empty((b, hq, n), dtype=torch.float32, device=q.device)
+        strides = {"q": _bhmd_strides(q), "k": _bhmd_strides(k), "lse": _bhmd_strides(lse),
+                   "total": _bhmd_strides(total)}
+        run_total(plan, q.detach(), k.detach(), lse, total, strides, b, scale)
+    return out, (lse if return_log_normalizer else None), total, None, None

@@ -83,6 +83,8 @@ struct BwdArgs {
   int32_t kv_ratio;        // heads_q / heads_kv
   float cap_log2;          // softcap * log2(e)          (CAP instances)
   float cap_arg;           // 2 * log2(e) * scale / softcap
+  float* tot;              // total attention (TOT instances): tot[b*t_sb + key*t_st + h*t_sh]
+  int64_t t_sb, t_st, t_sh;
 };
 
 struct SinkArgs {
@@ -139,6 +141,8 @@ __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
   if (p < pairs) {
     t = p / a.heads_q;
     h = (int)(p - t * a.heads_q);
+  }
+  if (p < pairs && a.out) {  // no out (total attention): only L
     const bf16x8_t o = *reinterpret_cast<const bf16x8_t*>(a.out + (int64_t)b * a.o_sb + t * a.o_st +
                                                           (int64_t)h * a.o_sh + c * 8);
     const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(a.dout + (int64_t)b * a.d_sb + t * a.d_st +
@@ -172,11 +176,14 @@ __device__ __forceinline__ int swz_b(int r) {
 // wave's VALU work hides behind the other's MFMAs); the key-major kernel holds
 // two fp32 accumulators and the k, v fragments (~480 registers at D = 128; at
 // D = 64 it would spill under 256), one wave per SIMD.
-template <int D, bool KV>
-constexpr int kBwdWaves = KV ? 1 : 2;
+template <int D, bool KV, bool TOT>
+constexpr int kBwdWaves = (KV && !TOT) ? 1 : 2;  // total attention keeps no accumulators: two waves
 
-template <int D, bool KV, bool CAP>
-__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(kBwdWaves<D, KV>, kBwdWaves<D, KV>))) void ffa_bwd_main(BwdArgs a) {
+// TOT (key-major only): FlagAttention's total attention, sum_i P[i,h,j] per key j and
+// query head h -- the same walk over the transposed worklist with only X1 and P.
+template <int D, bool KV, bool CAP, bool TOT = false>
+__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(kBwdWaves<D, KV, TOT>, kBwdWaves<D, KV, TOT>))) void ffa_bwd_main(BwdArgs a) {
+  static_assert(!TOT || KV, "total attention walks the key-major worklist");
   constexpr int BN = kBlockN;          // 64 rows per streamed tile
   constexpr int ROWB = D * 2;          // bytes of one row
   constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   auto load = [&](auto buf_tag, const Step& s) {
     constexpr int OB = decltype(buf_tag)::value * BUFB;
     dma(a_base(s.head), ast_b, OB, s.t.kstart(), total);
-    dma(b_base(s.head), bst_b, OB + TILE, s.t.kstart(), total);
+    if constexpr (!TOT) dma(b_base(s.head), bst_b, OB + TILE, s.t.kstart(), total);
     if constexpr (KV) dma_ld(2 * BUFB + decltype(buf_tag)::value * LDB, s.head, s.t.kstart());
   };
   auto advance = [&](Step& s) {
@@ -453,6 +460,10 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     }
   };
 
+  float tsum = 0.0f;  // TOT: this lane's part of the current head's column sum
+  auto write_total = [&](int head, float v) {
+    if (row_ok && hh == 0) a.tot[(int64_t)b * a.t_sb + (int64_t)row * a.t_st + (int64_t)head * a.t_sh] = v;
+  };
   auto compute = [&](auto buf_tag, const Step& s) {
     constexpr int OA = decltype(buf_tag)::value * BUFB;
     constexpr int OB = OA + TILE;
@@ -477,6 +488,25 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       }
     }
     if (s.t.edge()) mask(s.t, xa, xb);
+    if constexpr (TOT) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float x = e < 16 ? xa[e] : xb[e - 16];
+        float arg;
+        if constexpr (CAP) {
+          const float th = tanh_from_2ylog2e(x * a.cap_arg);
+          arg = x == -INFINITY ? -INFINITY : __builtin_fmaf(a.cap_log2, th, -lv[e >> 2][e & 3]);
+        } else {
+          arg = __builtin_fmaf(x, c2, -lv[e >> 2][e & 3]);
+        }
+        tsum += __builtin_amdgcn_exp2f(arg);
+      }
+      if (s.jt + 1 == total_tiles) {  // the head's last tile: its column sums are complete
+        write_total(s.head, partner_sum(tsum));
+        tsum = 0.0f;
+      }
+      return;
+    }
     // P = exp2(X1 c2 - L) in place, between the MFMAs of X2.  Soft-capped:
     // P = exp2(cap_log2 tanh - L) (masked scores stay at P = 0), and what stays in
     // place is P (1 - tanh^2), the factor of dS; P itself goes to bf16 at once.
@@ -566,6 +596,11 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     if (j < steps) iter(std::integral_constant<int, 0>{}, j);
   }
 
+  if constexpr (TOT) {
+    if (steps == 0)  // keys no query sees: total 0 for every head of the group
+      for (int i = 0; i < heads_per_step; ++i) write_total(hk * a.kv_ratio + i, 0.0f);
+    return;
+  }
   // ---- epilogue: lane holds head-dim values 32 d + 8 gq + 4 hh + e of its row
   if (row_ok) {
     auto store = [&](__bf16* dst, const f32x16_t(&acc)[DBLK], float mul) {
@@ -595,6 +630,100 @@ static ffa_status hip_fail_b(hipError_t e, const char* what) {
 }
 
 extern "C" {
+
+ffa_status ffa_total_attention(ffa_plan_t plan, const void* d_meta, int32_t batch, const void* q, int64_t q_sb,
+                               int64_t q_st, int64_t q_sh, const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh,
+                               const float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh, float* total,
+                               int64_t t_sb, int64_t t_st, int64_t t_sh, float softmax_scale,
+                               const ffa_attn_extras* extras, void* d_workspace, size_t workspace_bytes,
+                               void* stream) {
+  ffa::clear_error();
+  if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
+  const ffa::Plan& p = plan->plan;
+  if (p.bwd_off == 0)
+    return ffa::set_error(FFA_ERR_ARG, "the plan has no key-major worklist (plan with FFA_PLAN_BACKWARD)");
+  if (batch < 1) return ffa::set_error(FFA_ERR_ARG, "batch must be >= 1");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return ffa::set_error(FFA_ERR_ARG, "softmax_scale must be finite and > 0");
+  if (!d_meta) return ffa::set_error(FFA_ERR_NULL, "d_meta is NULL");
+  const bool has_q = p.total_q > 0, has_k = p.total_k > 0;
+  const ffa_status xs = ffa::check_extras(extras, has_q);
+  if (xs != FFA_OK) return xs;
+  ffa_attn_extras ex = {};
+  if (extras) ex = *extras;
+  if (has_q && (!q || !lse)) return ffa::set_error(FFA_ERR_NULL, "q and lse must be non-NULL");
+  if (has_k && (!k || !total)) return ffa::set_error(FFA_ERR_NULL, "k and total must be non-NULL");
+  const int64_t ws_need = (int64_t)batch * p.bwd_workspace_bytes();
+  if (ws_need > 0 && (!d_workspace || (int64_t)workspace_bytes < ws_need))
+    return ffa::set_error(FFA_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                                 " bytes, total attention needs " + std::to_string(ws_need));
+  auto al16 = [](const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; };
+  auto st8 = [](int64_t x) { return (x & 7) == 0; };
+  if ((has_q && !al16(q)) || (has_k && !al16(k)))
+    return ffa::set_error(FFA_ERR_ALIGN, "q and k must be 16-byte aligned");
+  for (int64_t x : {q_sb, q_st, q_sh, k_sb, k_st, k_sh})
+    if (!st8(x)) return ffa::set_error(FFA_ERR_ALIGN, "q and k strides must be multiples of 8 elements");
+  const int64_t lim = ((int64_t)1 << 31) / (2 * ffa::kBlockN);
+  if (std::llabs(k_st) >= lim || std::llabs(q_st) >= lim)
+    return ffa::set_error(FFA_ERR_ARG, "q / k token strides must be below 2^24 elements");
+  if ((int64_t)p.num_kv_items * batch > INT32_MAX) return ffa::set_error(FFA_ERR_ARG, "grid too large");
+  if ((int64_t)p.total_q * p.heads_q > ((int64_t)INT32_MAX) * 16) return ffa::set_error(FFA_ERR_ARG, "grid too large");
+
+  hipStream_t s = (hipStream_t)stream;
+  float* lw = static_cast<float*>(d_workspace);
+  float* dwp = lw ? lw + (size_t)batch * p.heads_q * p.total_q : nullptr;
+  if (has_q) {
+    PreArgs pa = {};
+    pa.lse = lse;
+    pa.lw = lw;
+    pa.dw = dwp;
+    pa.l_sb = l_sb; pa.l_st = l_st; pa.l_sh = l_sh;
+    pa.total_q = p.total_q;
+    pa.heads_q = p.heads_q;
+    const int ppb = 256 / (p.head_dim / 8);
+    const int64_t pairs = (int64_t)p.total_q * p.heads_q;
+    const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
+    dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+      hipLaunchKernelGGL(ffa_bwd_pre<decltype(d_tag)::value>, grid, dim3(256), 0, s, pa);
+    });
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_pre");
+  }
+  if (p.num_kv_items == 0) return FFA_OK;
+  const int32_t* bw = static_cast<const int32_t*>(d_meta) + p.bwd_off + ffa::kBwdHdr;
+  const int32_t* kv_items = bw + (size_t)p.num_dq_items * kItemRec + (size_t)p.num_dq_runs * kRec;
+  BwdArgs ba = {};
+  ba.items = kv_items;
+  ba.runs = kv_items + (size_t)p.num_kv_items * kItemRec;
+  ba.q = static_cast<const __bf16*>(q);
+  ba.k = static_cast<const __bf16*>(k);
+  ba.q_sb = q_sb; ba.q_st = q_st; ba.q_sh = q_sh;
+  ba.k_sb = k_sb; ba.k_st = k_st; ba.k_sh = k_sh;
+  ba.lw = lw;
+  ba.dw = dwp;
+  ba.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  ba.scale = softmax_scale;
+  ba.total_q = p.total_q;
+  ba.total_k = p.total_k;
+  ba.heads_q = p.heads_q;
+  ba.batch = batch;
+  ba.heads_per_item = p.heads_per_item;
+  ba.kv_ratio = p.heads_q / p.heads_kv;
+  const bool cap = ex.softcap > 0.0f;
+  ba.cap_log2 = cap ? (float)((double)ex.softcap * 1.4426950408889634074) : 0.0f;
+  ba.cap_arg = cap ? (float)(2.0 * 1.4426950408889634074 * (double)softmax_scale / (double)ex.softcap) : 0.0f;
+  ba.tot = total;
+  ba.t_sb = t_sb; ba.t_st = t_st; ba.t_sh = t_sh;
+  const dim3 grid((unsigned)((int64_t)p.num_kv_items * batch));
+  dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true, true>), grid, dim3(64 * ffa::kWaves), 0, s, ba);
+    else hipLaunchKernelGGL((ffa_bwd_main<D, true, false, true>), grid, dim3(64 * ffa::kWaves), 0, s, ba);
+  });
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (total attention)");
+  return FFA_OK;
+}
 
 ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const void* q, int64_t q_sb, int64_t q_st,
                    int64_t q_sh, const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh, const void* v, int64_t v_sb,

@@ -29,6 +29,7 @@
  *                   combine when the plan has split rows)
  *   ffa_bwd         gradients dq, dk, dv from the forward's out and lse and the
  *                   upstream gradient dout (plan built with FFA_PLAN_BACKWARD)
+ *   ffa_total_attention  attention probabilities summed over the queries, per key
  *   ffa_plan_destroy, ffa_status_string, ffa_last_error, ffa_abi_version
  *
  * Ownership.  The library owns only the host plan.  All device memory (meta,
@@ -232,6 +233,24 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
                    void* dv, int64_t dv_sb, int64_t dv_st, int64_t dv_sh,
                    float softmax_scale, const ffa_attn_extras* extras,
                    void* d_workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FlagAttention's total attention (user guide, "FlashAttention": `total`
+ * [B, Hq, N], the attention probabilities summed over the query axis):
+ *   total[b, j, h] = sum_i P[i, h, j],  P = exp(s_ij - lse[i,h]) on visible pairs
+ * from q, k and the forward's lse (and the same extras: softcap changes s, sinks
+ * only enter through lse).  fp32, element (b, key j, head h) at
+ * total[b*t_sb + j*t_st + h*t_sh]; every element is written (0 for keys no
+ * query sees).  Needs a plan with FFA_PLAN_BACKWARD (it walks the key-major
+ * worklist) and the backward's workspace (>= batch * info.bwd_workspace_bytes).
+ */
+ffa_status ffa_total_attention(ffa_plan_t plan, const void* d_meta, int32_t batch,
+                               const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                               const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh,
+                               const float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                               float* total, int64_t t_sb, int64_t t_st, int64_t t_sh,
+                               float softmax_scale, const ffa_attn_extras* extras,
+                               void* d_workspace, size_t workspace_bytes, void* stream);
 
 void ffa_plan_destroy(ffa_plan_t plan);
 const char* ffa_status_string(ffa_status status);

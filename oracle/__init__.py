@@ -22,6 +22,7 @@ from .fwd import (  # noqa: F401
     count_visible_pairs,
     attend,
     attend_dense,
+    total_attention,
     capped_scores,
     sink_logits,
     merge_partials,

@@ -228,6 +228,46 @@ def attend(q, k, v, q_ranges, k_ranges, mask_types, softmax_scale: Optional[floa
     return out, lse
 
 
+def total_attention(q, k, q_ranges, k_ranges, mask_types, softmax_scale: Optional[float] = None,
+                    block_rows: int = 256, sink=None, sink_layout: str = "sh", softcap: float = 0.0):
+    """Attention probabilities summed over the query axis: [Tk, Hq] float64.
+
+    FlagAttention user guide, "FlashAttention": `total` [B, Hq, N] holds the
+    attention probabilities summed over the query axis.  total[j, h] =
+    sum_i P[i, h, j] with P[i, h, j] = exp(s_ij - lse[i, h]) on visible pairs
+    (the weights `attend` uses; sinks only enter through lse, soft-capping
+    through s).
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    grp = hq // hkv
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    tot = np.zeros((tk, hq))
+    for b0 in range(0, tq, block_rows):
+        rb = np.arange(b0, min(tq, b0 + block_rows))
+        sinks = sink_logits(sink, sink_layout, rb, hq)
+        mask = mask_rows(rb, q_ranges, k_ranges, mask_types, tk)
+        cols = np.nonzero(mask.any(axis=0))[0]
+        if cols.size == 0:
+            continue
+        mk = mask[:, cols]
+        for g in range(hkv):
+            kg = k[cols, g, :]
+            for hh in range(grp):
+                h = g * grp + hh
+                s = np.where(mk, capped_scores((q[rb, h, :] @ kg.T) * scale, softcap), -np.inf)
+                sk = sinks[:, :, h] if sinks is not None else np.zeros((rb.shape[0], 0))
+                mx = np.maximum(s.max(axis=1), sk.max(axis=1, initial=-np.inf))
+                safe = np.where(np.isfinite(mx), mx, 0.0)
+                e = np.exp(s - safe[:, None])
+                den = e.sum(axis=1) + np.exp(sk - safe[:, None]).sum(axis=1)
+                p = e / np.where(den > 0, den, 1.0)[:, None]
+                tot[cols, h] += p.sum(axis=0)
+    return tot
+
+
 def attend_dense(q, k, v, mask: np.ndarray, softmax_scale: Optional[float] = None):
     """Softmax attention under an explicit [Tq, Tk] boolean mask (fp64)."""
     q = _as_f64(q)

@@ -19,7 +19,8 @@ from tests import test_oracle_pins as pins
 MUTATIONS = {
     "causal_off_by_one": ("end = ke - (qe - 1 - rows)", "end = ke - (qe - rows)"),
     "causal_top_left": ("end = ke - (qe - 1 - rows)", "end = ks + (rows - qs) + 1"),
-    "gqa_interleaved": ("h = g * grp + hh", "h = hh * hkv + g"),
+    "gqa_interleaved": ("h = g * grp + hh\n                s = capped_scores(",
+                        "h = hh * hkv + g\n                s = capped_scores("),
     "scale_dropped": ("s = capped_scores((q[rb, h, :] @ kg.T) * scale, softcap)",
                       "s = capped_scores((q[rb, h, :] @ kg.T), softcap)"),
     "v_replaced_by_k": ("o = (p @ vg)", "o = (p @ kg)"),
