@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--softcap", type=float, default=0.0, help="soft-capping of the scores (0: off)")
     ap.add_argument("--total", action="store_true", help="also time the total-attention pass")
+    ap.add_argument("--fp16", action="store_true", help="float16 inputs and outputs instead of bfloat16")
     ap.add_argument("--sinks", type=int, default=0, help="sink logits per head (layout sh; 0: none)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward (for profiling its kernels)")
@@ -157,7 +158,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     p = W.workload(args.workload)
-    q, k, v = W.make_qkv(p)
+    q, k, v = W.make_qkv(p, dtype=torch.float16 if args.fp16 else None)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
 
     t0 = time.perf_counter()
@@ -175,7 +176,7 @@ def main():
     if args.sinks > 0:
         g = torch.Generator().manual_seed(17)
         sink = torch.randn((args.sinks, p.heads_q), generator=g, dtype=torch.float32).to(dev)
-    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q)
+    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q, dtype=qd.dtype)
 
     def step():
         ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale, extras)
@@ -224,7 +225,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16" if args.fp16 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": p.name,
@@ -278,7 +279,7 @@ def total_leg(args, p, qd, kd, lse, scale, sink=None):
     tot = torch.empty((p.total_k, p.heads_q), dtype=torch.float32, device=dev)
     st = {"q": (0, qd.stride(0), qd.stride(1)), "k": (0, kd.stride(0), kd.stride(1)),
           "lse": (0, lse.stride(0), lse.stride(1)), "total": (0, tot.stride(0), tot.stride(1))}
-    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q)
+    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q, dtype=qd.dtype)
 
     def step():
         ffa.run_total(plan, qd, kd, lse, tot, st, 1, scale, extras)
@@ -312,7 +313,7 @@ def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink=None):
     plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
                     p.head_dim, backward=True)
     plan.device_meta(dev)
-    dout = W.make_dout(p).to(dev)
+    dout = W.make_dout(p, dtype=qd.dtype).to(dev)
     dq = torch.empty_like(qd)
     dk = torch.empty_like(kd)
     dv = torch.empty_like(vd)
@@ -322,7 +323,8 @@ def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink=None):
         st[n] = (0, t[n].stride(0), t[n].stride(1))
 
     dsink = torch.empty_like(sink) if sink is not None else None
-    extras = ffa.make_extras(sink, "sh", args.softcap, dsink=dsink, total_q=p.total_q, heads_q=p.heads_q)
+    extras = ffa.make_extras(sink, "sh", args.softcap, dsink=dsink, total_q=p.total_q, heads_q=p.heads_q,
+                             dtype=qd.dtype)
 
     def step():
         ffa.run_bwd(plan, t, st, 1, scale, extras)

@@ -100,7 +100,7 @@ class PlanInfo(ctypes.Structure):
 class AttnExtras(ctypes.Structure):
     """ffa_attn_extras: optional sink logits (and their gradient) and softcap."""
     _fields_ = [("sink", _vp), ("dsink", _vp), ("sink_sb", _i64), ("sink_st", _i64), ("sink_ss", _i64),
-                ("sink_sh", _i64), ("n_sink", _i32), ("softcap", _f32)]
+                ("sink_sh", _i64), ("n_sink", _i32), ("softcap", _f32), ("dtype", _i32)]
 
 
 # (name, restype, argtypes) of every function in include/ffa.h
@@ -306,30 +306,37 @@ def _cached_plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles, backward: bool = F
     return p
 
 
-def _require_bf16_cuda(name, t, ndim):
+def _require_bf16_cuda(name, t, ndim, dtype=None):
+    """A device tensor of `ndim` dims, bfloat16 or float16 (the same as `dtype` when given)."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have the dtype of q ({dtype}), got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if t.shape[-1] > 1 and t.stride(-1) != 1:
         raise ValueError(f"{name} must have a contiguous head_dim")
 
 
-def make_extras(sink=None, sink_layout: str = "sh", softcap: float = 0.0, dsink=None, total_q=None, heads_q=None):
-    """ffa_attn_extras for a sink tensor (fp32 device; layout "sh" [S, Hq] or "ssh" [Tq, S, Hq])
-    and a softcap; None when neither is used."""
+def make_extras(sink=None, sink_layout: str = "sh", softcap: float = 0.0, dsink=None, total_q=None, heads_q=None,
+                dtype=None):
+    """ffa_attn_extras for a sink tensor (fp32 device; layout "sh" [S, Hq] or "ssh" [Tq, S, Hq]),
+    a softcap and the element dtype (torch.float16 selects the fp16 kernels); None for plain
+    bfloat16 attention."""
     import torch
 
-    if sink is None and not softcap:
+    f16 = dtype == torch.float16
+    if sink is None and not softcap and not f16:
         return None
     ex = AttnExtras()
     ex.softcap = float(softcap or 0.0)
+    ex.dtype = 1 if f16 else 0
     if sink is not None:
         if not isinstance(sink, torch.Tensor) or sink.dtype != torch.float32 or not sink.is_cuda:
             raise TypeError("sink must be a float32 device tensor")
@@ -392,8 +399,8 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
     import torch
 
     _require_bf16_cuda("q", q, 3)
-    _require_bf16_cuda("k", k, 3)
-    _require_bf16_cuda("v", v, 3)
+    _require_bf16_cuda("k", k, 3, q.dtype)
+    _require_bf16_cuda("v", v, 3, q.dtype)
     tq, hq, d = q.shape
     tk, hkv, dk = k.shape
     if v.shape != k.shape or dk != d:
@@ -406,7 +413,7 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
     elif (plan.total_q, plan.total_k, plan.heads_q, plan.heads_kv, plan.head_dim) != (tq, tk, hq, hkv, d):
         raise ValueError("plan was built for another shape")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
     lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
     strides = {
         "q": (0, q.stride(0), q.stride(1)),
@@ -415,7 +422,7 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
         "out": (0, out.stride(0), out.stride(1)),
         "lse": (0, lse.stride(0), lse.stride(1)),
     }
-    ex = make_extras(sink, sink_layout, softcap, total_q=tq, heads_q=hq)
+    ex = make_extras(sink, sink_layout, softcap, total_q=tq, heads_q=hq, dtype=q.dtype)
     run_fwd(plan, q, k, v, out, lse, strides, 1, scale, ex)
     return out, lse
 
@@ -473,7 +480,7 @@ def flex_total_attention(q, k, lse, q_ranges, k_ranges, attn_type_map, softmax_s
     import torch
 
     _require_bf16_cuda("q", q, 3)
-    _require_bf16_cuda("k", k, 3)
+    _require_bf16_cuda("k", k, 3, q.dtype)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
     if lse.dtype != torch.float32 or tuple(lse.shape) != (tq, hq):
@@ -484,7 +491,7 @@ def flex_total_attention(q, k, lse, q_ranges, k_ranges, attn_type_map, softmax_s
     total = torch.empty((tk, hq), dtype=torch.float32, device=q.device)
     strides = {"q": _thd_strides(q), "k": _thd_strides(k), "lse": _thd_strides(lse), "total": _thd_strides(total)}
     run_total(plan, q, k, lse, total, strides, 1, scale, make_extras(sink, sink_layout, softcap, total_q=tq,
-                                                                     heads_q=hq))
+                                                                     heads_q=hq, dtype=q.dtype))
     return total
 
 
@@ -501,7 +508,7 @@ def flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_m
     import torch
 
     for name, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        _require_bf16_cuda(name, x, 3)
+        _require_bf16_cuda(name, x, 3, q.dtype)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
     if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape or k.shape[2] != d:
@@ -514,13 +521,13 @@ def flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_m
     elif (plan.total_q, plan.total_k, plan.heads_q, plan.heads_kv, plan.head_dim) != (tq, tk, hq, hkv, d):
         raise ValueError("plan was built for another shape")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    dq = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
-    dk = torch.empty((tk, hkv, d), dtype=torch.bfloat16, device=q.device)
-    dv = torch.empty((tk, hkv, d), dtype=torch.bfloat16, device=q.device)
+    dq = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
+    dk = torch.empty((tk, hkv, d), dtype=q.dtype, device=q.device)
+    dv = torch.empty((tk, hkv, d), dtype=q.dtype, device=q.device)
     t = {"q": q, "k": k, "v": v, "out": out, "lse": lse, "dout": dout, "dq": dq, "dk": dk, "dv": dv}
     strides = {n: _thd_strides(x) for n, x in t.items()}
     dsink = torch.empty_like(sink) if sink is not None else None
-    ex = make_extras(sink, sink_layout, softcap, dsink=dsink, total_q=tq, heads_q=hq)
+    ex = make_extras(sink, sink_layout, softcap, dsink=dsink, total_q=tq, heads_q=hq, dtype=q.dtype)
     run_bwd(plan, t, strides, 1, scale, ex)
     if sink is not None:
         return dq, dk, dv, dsink
@@ -534,13 +541,13 @@ def _autograd_function():
         @staticmethod
         def forward(ctx, q, k, v, sink, plan, scale, sink_layout, softcap):
             tq, hq, d = q.shape
-            out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+            out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
             lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
             strides = {"q": _thd_strides(q), "k": _thd_strides(k), "v": _thd_strides(v),
                        "out": _thd_strides(out), "lse": _thd_strides(lse)}
             sk = sink.detach() if sink is not None else None
             run_fwd(plan, q, k, v, out, lse, strides, 1, scale, make_extras(sk, sink_layout, softcap,
-                                                                           total_q=tq, heads_q=hq))
+                                                                           total_q=tq, heads_q=hq, dtype=q.dtype))
             ctx.save_for_backward(q, k, v, out, lse, sk)
             ctx.plan, ctx.scale, ctx.sink_layout, ctx.softcap = plan, scale, sink_layout, softcap
             ctx.mark_non_differentiable(lse)
@@ -549,8 +556,8 @@ def _autograd_function():
         @staticmethod
         def backward(ctx, dout, _dlse):
             q, k, v, out, lse, sink = ctx.saved_tensors
-            if dout.stride(-1) != 1 or dout.dtype != torch.bfloat16:
-                dout = dout.to(torch.bfloat16).contiguous()
+            if dout.stride(-1) != 1 or dout.dtype != q.dtype:
+                dout = dout.to(q.dtype).contiguous()
             g = flex_flash_attn_bwd(dout, q, k, v, out, lse, None, None, None, ctx.scale, plan=ctx.plan,
                                     sink=sink, sink_layout=ctx.sink_layout, softcap=ctx.softcap)
             dsink = g[3] if sink is not None else None
@@ -600,10 +607,10 @@ def _flash_function():
         @staticmethod
         def forward(ctx, q, k, v, plan, scale):
             b, hq, m, d = q.shape
-            out = torch.empty((b, hq, m, d), dtype=torch.bfloat16, device=q.device)
+            out = torch.empty((b, hq, m, d), dtype=q.dtype, device=q.device)
             lse = torch.empty((b, hq, m), dtype=torch.float32, device=q.device)
             strides = {n: _bhmd_strides(x) for n, x in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))}
-            run_fwd(plan, q, k, v, out, lse, strides, b, scale)
+            run_fwd(plan, q, k, v, out, lse, strides, b, scale, make_extras(dtype=q.dtype))
             ctx.save_for_backward(q, k, v, out, lse)
             ctx.plan, ctx.scale = plan, scale
             ctx.mark_non_differentiable(lse)
@@ -612,13 +619,14 @@ def _flash_function():
         @staticmethod
         def backward(ctx, dout, _dlse):
             q, k, v, out, lse = ctx.saved_tensors
-            if dout.stride(-1) != 1 or dout.dtype != torch.bfloat16:
-                dout = dout.to(torch.bfloat16).contiguous()
-            dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-            dk = torch.empty(k.shape, dtype=torch.bfloat16, device=q.device)
-            dv = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device)
+            if dout.stride(-1) != 1 or dout.dtype != q.dtype:
+                dout = dout.to(q.dtype).contiguous()
+            dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+            dk = torch.empty(k.shape, dtype=q.dtype, device=q.device)
+            dv = torch.empty(v.shape, dtype=q.dtype, device=q.device)
             t = {"q": q, "k": k, "v": v, "out": out, "lse": lse, "dout": dout, "dq": dq, "dk": dk, "dv": dv}
-            run_bwd(ctx.plan, t, {n: _bhmd_strides(x) for n, x in t.items()}, q.shape[0], ctx.scale)
+            run_bwd(ctx.plan, t, {n: _bhmd_strides(x) for n, x in t.items()}, q.shape[0], ctx.scale,
+                    make_extras(dtype=q.dtype))
             return dq, dk, dv, None, None
 
     return _FlashAttn
@@ -644,8 +652,8 @@ def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = N
     if return_seed_offset:
         raise NotImplementedError("return_seed_offset needs dropout, which is not supported")
     _require_bf16_cuda("q", q, 4)
-    _require_bf16_cuda("k", k, 4)
-    _require_bf16_cuda("v", v, 4)
+    _require_bf16_cuda("k", k, 4, q.dtype)
+    _require_bf16_cuda("v", v, 4, q.dtype)
     b, hq, m, d = q.shape
     bk, hkv, n, dk = k.shape
     if v.shape != k.shape or bk != b or dk != d:
@@ -666,5 +674,5 @@ def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = N
         total = torch.empty((b, hq, n), dtype=torch.float32, device=q.device)
         strides = {"q": _bhmd_strides(q), "k": _bhmd_strides(k), "lse": _bhmd_strides(lse),
                    "total": _bhmd_strides(total)}
-        run_total(plan, q.detach(), k.detach(), lse, total, strides, b, scale)
+        run_total(plan, q.detach(), k.detach(), lse, total, strides, b, scale, make_extras(dtype=q.dtype))
     return out, (lse if return_log_normalizer else None), total, None, None

@@ -127,8 +127,12 @@ __global__ __launch_bounds__(256) void ffa_bwd_dsink(SinkArgs a) {
 
 // Dd[b,h,t] = sum_d dO[b,t,h,d] O[b,t,h,d] (fp32 from the bf16 values) and
 // L[b,h,t] = lse * log2 e, with +inf for rows that see no key (their P is 0).
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
+  using V8 = typename ElemT<T>::v8;
+  using V4 = typename ElemT<T>::v4;
+  using V2 = typename ElemT<T>::v2;
+  (void)sizeof(V2);
   constexpr int TPP = D / 8;      // lanes per (row, head), 8 values each
   constexpr int PPB = 256 / TPP;  // (row, head) pairs per workgroup
   const int b = blockIdx.y;
@@ -143,9 +147,9 @@ __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
     h = (int)(p - t * a.heads_q);
   }
   if (p < pairs && a.out) {  // no out (total attention): only L
-    const bf16x8_t o = *reinterpret_cast<const bf16x8_t*>(a.out + (int64_t)b * a.o_sb + t * a.o_st +
+    const V8 o = *reinterpret_cast<const V8*>(a.out + (int64_t)b * a.o_sb + t * a.o_st +
                                                           (int64_t)h * a.o_sh + c * 8);
-    const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(a.dout + (int64_t)b * a.d_sb + t * a.d_st +
+    const V8 g = *reinterpret_cast<const V8*>(a.dout + (int64_t)b * a.d_sb + t * a.d_st +
                                                           (int64_t)h * a.d_sh + c * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
@@ -181,8 +185,12 @@ constexpr int kBwdWaves = (KV && !TOT) ? 1 : 2;  // total attention keeps no acc
 
 // TOT (key-major only): FlagAttention's total attention, sum_i P[i,h,j] per key j and
 // query head h -- the same walk over the transposed worklist with only X1 and P.
-template <int D, bool KV, bool CAP, bool TOT = false>
+template <int D, bool KV, bool CAP, bool TOT, typename T>
 __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(kBwdWaves<D, KV, TOT>, kBwdWaves<D, KV, TOT>))) void ffa_bwd_main(BwdArgs a) {
+  using V8 = typename ElemT<T>::v8;
+  using V4 = typename ElemT<T>::v4;
+  using V2 = typename ElemT<T>::v2;
+  (void)sizeof(V2);
   static_assert(!TOT || KV, "total attention walks the key-major worklist");
   constexpr int BN = kBlockN;          // 64 rows per streamed tile
   constexpr int ROWB = D * 2;          // bytes of one row
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const int hq = h0 + g;                     // query head of the row (query-major)
 
   // ---- the row's fragments (B operands, head-dim half hh): q and dO, or k and v
-  bf16x8_t f1[KSTEPS], f2[KSTEPS];
+  V8 f1[KSTEPS], f2[KSTEPS];
   {
     const __bf16* p1 = KV ? a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh + (int64_t)row * a.k_st
                           : a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)row * a.q_st;
@@ -233,13 +241,13 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       if (load) {
-        f1[s] = reinterpret_cast<const bf16x8_t*>(p1 + hh * (D / 2))[s];
-        f2[s] = reinterpret_cast<const bf16x8_t*>(p2 + hh * (D / 2))[s];
+        f1[s] = reinterpret_cast<const V8*>(p1 + hh * (D / 2))[s];
+        f2[s] = reinterpret_cast<const V8*>(p2 + hh * (D / 2))[s];
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          f1[s][j] = (__bf16)0.0f;
-          f2[s][j] = (__bf16)0.0f;
+          f1[s][j] = (T)0.0f;
+          f2[s][j] = (T)0.0f;
         }
       }
     }
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 
   // ---- X = T F^T for the streamed tile T at LDS offset OFF: two 32-row blocks
   // (xa, xb); hook(m) runs after the m-th MFMA is issued
-  auto rowprod = [&](auto off_tag, const bf16x8_t(&f)[KSTEPS], f32x16_t& xa, f32x16_t& xb, auto&& hook) {
+  auto rowprod = [&](auto off_tag, const V8(&f)[KSTEPS], f32x16_t& xa, f32x16_t& xb, auto&& hook) {
     constexpr int OFF = decltype(off_tag)::value;
     constexpr int NQ = 2 * KSTEPS;
     constexpr int KIF = 4;
@@ -354,9 +362,9 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       lds_wait<later>();
       fence(rf[m % KIF]);
       if constexpr (m % 2 == 0)
-        xa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(rf[m % KIF]), f[m / 2], xa, 0, 0, 0);
+        xa = mfma32(as_v8<T>(rf[m % KIF]), f[m / 2], xa);
       else
-        xb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(rf[m % KIF]), f[m / 2], xb, 0, 0, 0);
+        xb = mfma32(as_v8<T>(rf[m % KIF]), f[m / 2], xb);
       if constexpr (m + KIF < NQ) {
         constexpr int r = m + KIF;
         rf[m % KIF] = lds_read_b128<OFF + (r % 2) * 32 * ROWB>(r_addr[r / 2]);
@@ -367,7 +375,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 
   // ---- acc^T += T^T X for the streamed tile T at LDS offset OFF (16 rows per
   // MFMA, the reads of step t+1 in flight during the MFMAs of step t)
-  auto trprod = [&](auto off_tag, const bf16x8_t(&xf)[4], f32x16_t(&acc)[DBLK], auto&& hook) {
+  auto trprod = [&](auto off_tag, const V8(&xf)[4], f32x16_t(&acc)[DBLK], auto&& hook) {
     constexpr int OFF = decltype(off_tag)::value;
     s16x4_t vlo[2][DBLK], vhi[2][DBLK];
 #pragma unroll
@@ -393,7 +401,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         fence(vhi[cur][d]);
         const s16x8_t vv = {vlo[cur][d][0], vlo[cur][d][1], vlo[cur][d][2], vlo[cur][d][3],
                             vhi[cur][d][0], vhi[cur][d][1], vhi[cur][d][2], vhi[cur][d][3]};
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), xf[t], acc[d], 0, 0, 0);
+        acc[d] = mfma32(__builtin_bit_cast(V8, vv), xf[t], acc[d]);
       });
       hook(std::integral_constant<int, t>{});
     });
@@ -513,7 +521,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     auto lval = [&](int e) -> float { return KV ? lv[e >> 2][e & 3] : l_row; };
     auto dval = [&](int e) -> float { return KV ? dv[e >> 2][e & 3] : d_row; };
     constexpr int EPQ = 32 / (2 * KSTEPS);  // score elements per MFMA of X2
-    bf16x8_t pf[4], sf[4];
+    V8 pf[4], sf[4];
     rowprod(std::integral_constant<int, OB>{}, f2, ya, yb, [&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
 #pragma unroll
@@ -523,7 +531,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           const float th = tanh_from_2ylog2e(x * a.cap_arg);
           const float arg = x == -INFINITY ? -INFINITY : __builtin_fmaf(a.cap_log2, th, -lval(e));
           const float pr = __builtin_amdgcn_exp2f(arg);
-          if constexpr (KV) pf[e >> 3][e & 7] = (__bf16)pr;
+          if constexpr (KV) pf[e >> 3][e & 7] = (T)pr;
           const float keep = pr * __builtin_fmaf(-th, th, 1.0f);
           if (e < 16) xa[e] = keep;
           else xb[e - 16] = keep;
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         const int e = 8 * t + u;
         const float p = e < 16 ? xa[e] : xb[e - 16];
         const float y = e < 16 ? ya[e] : yb[e - 16];
-        sf[t][u] = (__bf16)(p * (y - dval(e)));
+        sf[t][u] = (T)(p * (y - dval(e)));
       }
       fence(sf[t]);
     };
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int e = 8 * t + u;
-          pf[t][u] = (__bf16)(e < 16 ? xa[e] : xb[e - 16]);
+          pf[t][u] = (T)(e < 16 ? xa[e] : xb[e - 16]);
         }
     }
     if constexpr (KV) {
@@ -608,10 +616,10 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       for (int d = 0; d < DBLK; ++d)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          bf16x4_t w;
+          V4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * gq + e] * mul);
-          *reinterpret_cast<bf16x4_t*>(dst + 32 * d + 8 * gq + 4 * hh) = w;
+          for (int e = 0; e < 4; ++e) w[e] = (T)(acc[d][4 * gq + e] * mul);
+          *reinterpret_cast<V4*>(dst + 32 * d + 8 * gq + 4 * hh) = w;
         }
     };
     if constexpr (KV) {
@@ -684,7 +692,9 @@ ffa_status ffa_total_attention(ffa_plan_t plan, const void* d_meta, int32_t batc
     const int64_t pairs = (int64_t)p.total_q * p.heads_q;
     const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
     dispatch_head_dim(p.head_dim, [&](auto d_tag) {
-      hipLaunchKernelGGL(ffa_bwd_pre<decltype(d_tag)::value>, grid, dim3(256), 0, s, pa);
+      dispatch_dtype(ex.dtype, [&](auto t_tag) {
+        hipLaunchKernelGGL((ffa_bwd_pre<decltype(d_tag)::value, decltype(t_tag)>), grid, dim3(256), 0, s, pa);
+      });
     });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_pre");
@@ -717,8 +727,11 @@ ffa_status ffa_total_attention(ffa_plan_t plan, const void* d_meta, int32_t batc
   const dim3 grid((unsigned)((int64_t)p.num_kv_items * batch));
   dispatch_head_dim(p.head_dim, [&](auto d_tag) {
     constexpr int D = decltype(d_tag)::value;
-    if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true, true>), grid, dim3(64 * ffa::kWaves), 0, s, ba);
-    else hipLaunchKernelGGL((ffa_bwd_main<D, true, false, true>), grid, dim3(64 * ffa::kWaves), 0, s, ba);
+    dispatch_dtype(ex.dtype, [&](auto t_tag) {
+      using T = decltype(t_tag);
+      if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true, true, T>), grid, dim3(64 * ffa::kWaves), 0, s, ba);
+      else hipLaunchKernelGGL((ffa_bwd_main<D, true, false, true, T>), grid, dim3(64 * ffa::kWaves), 0, s, ba);
+    });
   });
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (total attention)");
@@ -789,7 +802,9 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     const int64_t pairs = (int64_t)p.total_q * p.heads_q;
     const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
     dispatch_head_dim(p.head_dim, [&](auto d_tag) {
-      hipLaunchKernelGGL(ffa_bwd_pre<decltype(d_tag)::value>, grid, dim3(256), 0, s, pa);
+      dispatch_dtype(ex.dtype, [&](auto t_tag) {
+        hipLaunchKernelGGL((ffa_bwd_pre<decltype(d_tag)::value, decltype(t_tag)>), grid, dim3(256), 0, s, pa);
+      });
     });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_pre");
@@ -838,8 +853,11 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     const dim3 grid((unsigned)((int64_t)p.num_dq_items * batch));
     dispatch_head_dim(p.head_dim, [&](auto d_tag) {
       constexpr int D = decltype(d_tag)::value;
-      if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, false, true>), grid, block, 0, s, ba);
-      else hipLaunchKernelGGL((ffa_bwd_main<D, false, false>), grid, block, 0, s, ba);
+      dispatch_dtype(ex.dtype, [&](auto t_tag) {
+        using T = decltype(t_tag);
+        if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, false, true, false, T>), grid, block, 0, s, ba);
+        else hipLaunchKernelGGL((ffa_bwd_main<D, false, false, false, T>), grid, block, 0, s, ba);
+      });
     });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dq)");
@@ -850,8 +868,11 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     const dim3 grid((unsigned)((int64_t)p.num_kv_items * batch));
     dispatch_head_dim(p.head_dim, [&](auto d_tag) {
       constexpr int D = decltype(d_tag)::value;
-      if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true>), grid, block, 0, s, ba);
-      else hipLaunchKernelGGL((ffa_bwd_main<D, true, false>), grid, block, 0, s, ba);
+      dispatch_dtype(ex.dtype, [&](auto t_tag) {
+        using T = decltype(t_tag);
+        if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true, false, T>), grid, block, 0, s, ba);
+        else hipLaunchKernelGGL((ffa_bwd_main<D, true, false, false, T>), grid, block, 0, s, ba);
+      });
     });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dk, dv)");

@@ -14,6 +14,8 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 #define FFA_LDS __attribute__((address_space(3)))
 // plan records are read-only for the kernels: reading them through the constant
@@ -92,6 +94,37 @@ __device__ __forceinline__ float partner_sum(float x) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(f32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
+// Element type of q, k, v, out and the gradients: bfloat16 or IEEE half.  The
+// kernels are templated on it; the two differ only in the MFMA opcode and in the
+// conversions (and, in the forward, in how large a probability may grow before
+// the exact rescale: fp16 tops out at 65504).
+template <typename T>
+struct ElemT;
+template <>
+struct ElemT<__bf16> {
+  typedef bf16x8_t v8;
+  typedef bf16x4_t v4;
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  static constexpr float kMaxP = 18446744073709551616.0f;  // 2^64
+};
+template <>
+struct ElemT<_Float16> {
+  typedef f16x8_t v8;
+  typedef f16x4_t v4;
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  static constexpr float kMaxP = 32768.0f;  // 2^15
+};
+template <typename T>
+__device__ __forceinline__ typename ElemT<T>::v8 as_v8(f32x4_t x) {
+  return __builtin_bit_cast(typename ElemT<T>::v8, x);
+}
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 // Tile iterator over an item's runs (wave-uniform): the tile's first key and the
 // mask parameters of its run.
 struct TileIt {
@@ -115,6 +148,11 @@ __device__ __forceinline__ void tile_next(TileIt& t, const FFA_CONST int32_t* rp
 
 // Host: calls f(std::integral_constant<int, D>{}) for the head dim d (32, 64 or 128;
 // the planner has validated it).
+template <typename F>
+inline void dispatch_dtype(int dtype, F&& f) {
+  if (dtype == FFA_DTYPE_F16) f(_Float16{});
+  else f(__bf16{});
+}
 template <typename F>
 inline void dispatch_head_dim(int d, F&& f) {
   if (d == 128) f(std::integral_constant<int, 128>{});

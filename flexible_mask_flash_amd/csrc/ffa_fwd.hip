@@ -102,10 +102,10 @@ __device__ __forceinline__ float tanh_from_2ylog2e(float z) {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 // A row keeps its reference point (log2 units) until one of its probabilities
-// would exceed 2^64: a lane's per-tile partial sum above kOverflow sends the
-// whole wave through the exact rescale path.  Values up to 2^64 are exact
-// enough in bf16 / fp32 (relative rounding) and cannot overflow the fp32 sums.
-constexpr float kOverflow = 18446744073709551616.0f;  // 2^64
+// would exceed ElemT<T>::kMaxP (2^64 for bf16, 2^15 for fp16, whose largest value
+// is 65504): a lane's per-tile partial sum above it sends the whole wave through
+// the exact rescale path.  Values up to that bound are exact enough in the
+// element type and fp32 (relative rounding) and cannot overflow the fp32 sums.
 
 // LDS row swizzles (16-byte chunk index XOR by key row).
 //  K rows are read as MFMA A operands: lanes 0-15 read one chunk of rows
@@ -124,8 +124,12 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? ((r & 3) << 2) : D == 64 ? (((r >> 1) & 1) << 2) : 0;
 }
 
-template <int D, bool CAP>
+template <int D, bool CAP, typename T>
 __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
+  using V8 = typename ElemT<T>::v8;
+  using V4 = typename ElemT<T>::v4;
+  using V2 = typename ElemT<T>::v2;
+  (void)sizeof(V2);
   constexpr int BN = kBlockN;          // 64 keys per tile
   constexpr int ROWB = D * 2;          // bytes of one K/V row
   constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -176,9 +180,9 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const char* vbase = (const char*)(a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh);
 
   // ---- Q^T operand: lane holds query `row`, head-dim half hh (D/2 contiguous values)
-  bf16x8_t qf[KSTEPS];
+  V8 qf[KSTEPS];
   if (row_ok && n_runs > 0) {
-    const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh +
+    const V8* qp = reinterpret_cast<const V8*>(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh +
                                                            (int64_t)row * a.q_st + hh * (D / 2));
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = qp[s];
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qf[s][j] = (__bf16)0.0f;
+      for (int j = 0; j < 8; ++j) qf[s][j] = (T)0.0f;
   }
 
   f32x16_t o[DBLK];
@@ -283,9 +287,9 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       lds_wait<later>();
       fence(kf[m % KIF]);
       if constexpr (m % 2 == 0)
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m / 2], sa, 0, 0, 0);
+        sa = mfma32(as_v8<T>(kf[m % KIF]), qf[m / 2], sa);
       else
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[m % KIF]), qf[m / 2], sb, 0, 0, 0);
+        sb = mfma32(as_v8<T>(kf[m % KIF]), qf[m / 2], sb);
       if constexpr (m + KIF < NQ) {
         constexpr int r = m + KIF;
         kf[m % KIF] = lds_read_b128<OK + (r % 2) * 32 * ROWB>(k_addr[r / 2]);
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 
   // ---- O^T += V^T P^T of one tile from V buffer BUF (16 keys per MFMA; the reads
   // of step t+1 are in flight during the MFMAs of step t); hook(slot) as above
-  auto pv = [&](auto buf_tag, const bf16x8_t (&pf)[4], auto&& hook) {
+  auto pv = [&](auto buf_tag, const V8 (&pf)[4], auto&& hook) {
     constexpr int OV = kOffV[decltype(buf_tag)::value];
     s16x4_t vlo[2][DBLK], vhi[2][DBLK];
 #pragma unroll
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         fence(vhi[cur][d]);
         const s16x8_t vv = {vlo[cur][d][0], vlo[cur][d][1], vlo[cur][d][2], vlo[cur][d][3],
                             vhi[cur][d][0], vhi[cur][d][1], vhi[cur][d][2], vhi[cur][d][3]};
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[t], o[d], 0, 0, 0);
+        o[d] = mfma32(__builtin_bit_cast(V8, vv), pf[t], o[d]);
         hook(std::integral_constant<int, t * DBLK + d>{});
       });
     });
@@ -444,8 +448,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           const float p0 = __builtin_amdgcn_exp2f(s0v);
           const float p1 = __builtin_amdgcn_exp2f(s1v);
           ps += p0 + p1;
-          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-          const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
+                    const V2 pr = {(T)p0, (T)p1};
           pu[e >> 1] = __builtin_bit_cast(uint32_t, pr);
           fence(pu[e >> 1]);
         }
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       } else {
         static_for<QSLOTS>(exp_hook);
       }
-      if (__builtin_amdgcn_ballot_w64(!(ps <= kOverflow))) {
+      if (__builtin_amdgcn_ballot_w64(!(ps <= ElemT<T>::kMaxP))) {
         // rare: some probability above 2^64 -- move the reference to the row max
         // of this tile, rescale what is accumulated, and redo the tile (the
         // arguments hold s * c2 - msub)
@@ -479,18 +482,17 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           const float p0 = __builtin_amdgcn_exp2f((e < 16 ? ca[e] : cb[e - 16]) - shift);
           const float p1 = __builtin_amdgcn_exp2f((e + 1 < 16 ? ca[e + 1] : cb[e + 1 - 16]) - shift);
           ps += p0 + p1;
-          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-          const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
+                    const V2 pr = {(T)p0, (T)p1};
           pu[e >> 1] = __builtin_bit_cast(uint32_t, pr);
         }
       }
       l_run += ps;
-      bf16x8_t pf[4];
+      V8 pf[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
         const u32x4_t w = {pu[4 * t], pu[4 * t + 1], pu[4 * t + 2], pu[4 * t + 3]};
-        pf[t] = __builtin_bit_cast(bf16x8_t, w);
+        pf[t] = __builtin_bit_cast(V8, w);
       }
 
       // O += P_j V_j; the edge mask and reference point of tile j+1 go first, its
@@ -574,11 +576,11 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       for (int d = 0; d < DBLK; ++d)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          bf16x4_t w;
+          V4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[d][4 * gq + e] * inv);
+          for (int e = 0; e < 4; ++e) w[e] = (T)(o[d][4 * gq + e] * inv);
           const int c = 4 * d + gq;  // 16-byte chunk of the row
-          *reinterpret_cast<bf16x4_t*>(st + q * ROWB + ((c ^ swz_k<D>(q)) << 4) + hh * 8) = w;
+          *reinterpret_cast<V4*>(st + q * ROWB + ((c ^ swz_k<D>(q)) << 4) + hh * 8) = w;
         }
     }
     __bf16* ob = out_p + (int64_t)b * o_sb + (int64_t)h * o_sh;
@@ -617,8 +619,12 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 
 // Merge split partials: lse = ln sum_c exp(lse_c); out = sum_c exp(lse_c - lse) out_c.
 // One workgroup per combine entry (up to 128 (row, head) pairs); D/4 lanes per pair.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
+  using V8 = typename ElemT<T>::v8;
+  using V4 = typename ElemT<T>::v4;
+  using V2 = typename ElemT<T>::v2;
+  (void)sizeof(V2);
   constexpr int TPP = D / 4;          // threads per (row, head) pair
   constexpr int PPP = 256 / TPP;      // pairs per pass
   const int bid = blockIdx.x;
@@ -676,10 +682,10 @@ __global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
     // sink logits: denominator terms without a value
     for (int s = 0; s < a.n_sink; ++s) den += __expf(sp[s * a.sk_ss] - msafe);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    bf16x4_t w4;
+    V4 w4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x4_t*>(a.out + (int64_t)b * a.o_sb + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + dq) = w4;
+    for (int e = 0; e < 4; ++e) w4[e] = (T)(acc[e] * inv);
+    *reinterpret_cast<V4*>(a.out + (int64_t)b * a.o_sb + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + dq) = w4;
     if (dq == 0)
       a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)h * a.l_sh] =
           den > 0.0f ? msafe + __logf(den) : -INFINITY;
@@ -870,9 +876,12 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   const dim3 grid((unsigned)((int64_t)p.num_items * batch));
   const dim3 blk(64 * ffa::kWaves);
   dispatch_head_dim(p.head_dim, [&](auto d_tag) {
-    constexpr int D = decltype(d_tag)::value;
-    if (cap) hipLaunchKernelGGL((ffa_fwd_main<D, true>), grid, blk, 0, s, fa);
-    else hipLaunchKernelGGL((ffa_fwd_main<D, false>), grid, blk, 0, s, fa);
+    dispatch_dtype(ex.dtype, [&](auto t_tag) {
+      constexpr int D = decltype(d_tag)::value;
+      using T = decltype(t_tag);
+      if (cap) hipLaunchKernelGGL((ffa_fwd_main<D, true, T>), grid, blk, 0, s, fa);
+      else hipLaunchKernelGGL((ffa_fwd_main<D, false, T>), grid, blk, 0, s, fa);
+    });
   });
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch ffa_fwd_main");
@@ -894,7 +903,9 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     ca.n_sink = fa.n_sink;
     const dim3 cgrid((unsigned)((int64_t)p.num_combine * batch));
     dispatch_head_dim(p.head_dim, [&](auto d_tag) {
-      hipLaunchKernelGGL(ffa_combine<decltype(d_tag)::value>, cgrid, dim3(256), 0, s, ca);
+      dispatch_dtype(ex.dtype, [&](auto t_tag) {
+        hipLaunchKernelGGL((ffa_combine<decltype(d_tag)::value, decltype(t_tag)>), cgrid, dim3(256), 0, s, ca);
+      });
     });
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch ffa_combine");

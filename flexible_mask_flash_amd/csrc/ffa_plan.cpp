@@ -240,6 +240,8 @@ ffa_status check_extras(const ffa_attn_extras* ex, bool has_rows) {
   if (!(ex->softcap >= 0.0f) || !std::isfinite(ex->softcap))
     return set_error(FFA_ERR_ARG, "softcap must be finite and >= 0 (0: off)");
   if (ex->n_sink < 0) return set_error(FFA_ERR_ARG, "n_sink must be >= 0");
+  if (ex->dtype != FFA_DTYPE_BF16 && ex->dtype != FFA_DTYPE_F16)
+    return set_error(FFA_ERR_ARG, "dtype must be FFA_DTYPE_BF16 or FFA_DTYPE_F16");
   if (ex->n_sink > 0 && has_rows && !ex->sink) return set_error(FFA_ERR_NULL, "n_sink > 0 but sink is NULL");
   return FFA_OK;
 }

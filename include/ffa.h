@@ -59,6 +59,9 @@ extern "C" {
 #define FFA_MASK_INVCAUSAL 2
 #define FFA_MASK_BICAUSAL 3
 
+#define FFA_DTYPE_BF16 0
+#define FFA_DTYPE_F16 1
+
 #define FFA_PLAN_NATURAL_ORDER 1u
 #define FFA_PLAN_BACKWARD 2u
 
@@ -98,6 +101,8 @@ typedef struct {
   int64_t sink_sb, sink_st, sink_ss, sink_sh;
   int32_t n_sink;   /* sink logits per (row, head); 0: no sink */
   float softcap;    /* 0: off; must be finite and >= 0 */
+  int32_t dtype;    /* element type of q, k, v, out, dout and the gradients:
+                       FFA_DTYPE_BF16 (0, also when extras is NULL) or FFA_DTYPE_F16 */
 } ffa_attn_extras;
 
 /* Opaque host plan; immutable after ffa_plan, safe to share between threads. */

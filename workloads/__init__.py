@@ -195,12 +195,14 @@ def random_problem(seed: int, total_q: int, total_k: int, hq: int, hkv: int, d: 
     return make_problem(f"random_{seed}", total_q, total_k, hq, hkv, d, slices, seed=seed)
 
 
-def make_qkv(p: Problem, seed: Optional[int] = None, q_zero: bool = False):
-    """Draw q, k, v (CPU, bfloat16) for problem `p`.
+def make_qkv(p: Problem, seed: Optional[int] = None, q_zero: bool = False, dtype=None):
+    """Draw q, k, v (CPU, bfloat16 unless `dtype` says otherwise) for problem `p`.
 
     Returns torch tensors q [Tq,Hq,D], k [Tk,Hkv,D], v [Tk,Hkv,D].
     """
     import torch
+
+    dtype = torch.bfloat16 if dtype is None else dtype
 
     g = torch.Generator().manual_seed(p.seed if seed is None else seed)
     q = torch.randn(p.total_q, p.heads_q, p.head_dim, generator=g, dtype=torch.float32)
@@ -208,7 +210,7 @@ def make_qkv(p: Problem, seed: Optional[int] = None, q_zero: bool = False):
     v = torch.randn(p.total_k, p.heads_kv, p.head_dim, generator=g, dtype=torch.float32)
     if q_zero:
         q.zero_()
-    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
 def sliding_window_problem(T, w, docs, hq, hkv, d, seed):
@@ -275,12 +277,13 @@ def workload(name: str) -> Problem:
     raise ValueError(f"unknown workload {name!r}")
 
 
-def make_dout(p: Problem, seed: Optional[int] = None):
-    """Draw an upstream gradient dout [Tq,Hq,D] (CPU, bfloat16) for problem `p`."""
+def make_dout(p: Problem, seed: Optional[int] = None, dtype=None):
+    """Draw an upstream gradient dout [Tq,Hq,D] (CPU, bfloat16 unless `dtype`) for problem `p`."""
     import torch
 
     g = torch.Generator().manual_seed((p.seed if seed is None else seed) + 7919)
-    return torch.randn(p.total_q, p.heads_q, p.head_dim, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return torch.randn(p.total_q, p.heads_q, p.head_dim, generator=g, dtype=torch.float32).to(
+        torch.bfloat16 if dtype is None else dtype)
 
 
 def sample_rows(p: Problem, n: int, seed: int = 0) -> np.ndarray:
