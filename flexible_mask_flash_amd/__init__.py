@@ -1,4 +1,4 @@
-"""Flexible-mask flash-attention forward for MI355X (gfx950).
+"""Flexible-mask flash attention (forward and backward) for MI355X (gfx950).
 
 A thin ctypes binding over ``libffa.so`` (C ABI declared in ``include/ffa.h``).
 Python marshals arguments only: validation of the slices, planning and every
@@ -7,17 +7,21 @@ for device memory and streams.  There is no fallback: if the library is missing
 or cannot be loaded, every entry point raises.
 
 API (names follow the pages):
-  flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, softmax_scale=None)
-      MagiAttention's single-GPU FFA interface, forward; packed THD
-      tensors q [Tq,Hq,D], k/v [Tk,Hkv,D] (bf16) -> (out [Tq,Hq,D] bf16,
-      lse [Tq,Hq] fp32).
-  flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map)
-      its gradients (dq, dk, dv).
+  flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
+                      softmax_scale=None, softcap=0.0, sink_layout="sh")
+      MagiAttention's single-GPU FFA interface on packed THD tensors
+      q [Tq,Hq,D], k/v [Tk,Hkv,D] (bf16 or fp16; D 32, 64 or 128) ->
+      (out [Tq,Hq,D], lse [Tq,Hq] fp32); mask types 0-3, optional sink
+      logits and soft-capping.
+  flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, ...)
+      its gradients (dq, dk, dv[, dsink]).
   flex_flash_attn_func(...)  the same forward as a torch.autograd.Function.
+  flex_total_attention(q, k, lse, q_ranges, k_ranges, attn_type_map, ...)
+      attention probabilities summed over the queries, [Tk, Hq].
   flash_attention(q, k, v, causal=False, sm_scale=None, ...)
       FlagAttention's dense contract on [B,H,M,D] tensors (GQA, bottom-right
-      causal); returns out, or the 5-tuple (out, lse [B,Hq,M], None, None,
-      None) when an auxiliary flag is set.
+      causal), differentiable; returns out, or the 5-tuple (out, lse [B,Hq,M],
+      total [B,Hq,N], None, None) when an auxiliary flag is set.
   Plan(...)  a reusable host plan (ffa_plan) with its device metadata.
 """
 from __future__ import annotations
@@ -387,7 +391,7 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
                         plan: Optional[Plan] = None, split_tiles: int = 0, sink_layout: str = "sh"):
     """Forward of flexible-mask attention on packed THD tensors -> (out, lse).
 
-    q [Tq,Hq,D], k/v [Tk,Hkv,D] bf16 device tensors (head_dim contiguous);
+    q [Tq,Hq,D], k/v [Tk,Hkv,D] bf16 or fp16 device tensors (head_dim contiguous);
     q_ranges / k_ranges int32 [S,2], attn_type_map int32 [S] (0 full, 1 causal,
     2 inverse causal, 3 bi-causal), host or device (device ranges are copied to
     the host, which synchronises).  Optional: sink, fp32 logits [S_sink, Hq]

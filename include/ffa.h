@@ -1,11 +1,11 @@
 /*
- * ffa.h -- C ABI of the MI355X (gfx950) flexible-mask flash-attention forward.
+ * ffa.h -- C ABI of the MI355X (gfx950) flexible-mask flash attention (forward,
+ *          backward and total attention).
  *
  * The operation (MagiAttention quickstart, section "Single-GPU
  * Flex-Flash-Attention"; FlagAttention user guide, section "FlashAttention"):
  *
- *   q [total_q, Hq, D], k and v [total_k, Hkv, D], bfloat16, head_dim D
- *   contiguous.  A mask is a list of S slices (q_range, k_range, type) with
+ *   q [total_q, Hq, D], k and v [total_k, Hkv, D], head_dim D contiguous.  A mask is a list of S slices (q_range, k_range, type) with
  *   half-open ranges.  Query row i of slice s (qs <= i < qe) sees
  *     FULL      (type 0): keys [ks, ke)
  *     CAUSAL    (type 1): keys [ks, ke - (qe - 1 - i))             -- bottom-right aligned
@@ -17,8 +17,9 @@
  *   With s_ij = softmax_scale * q_i . k_j over the visible keys V(i):
  *     lse[i,h] = ln sum_{j in V(i)} exp(s_ij)           (-inf if V(i) is empty)
  *     out[i,h] = sum_{j in V(i)} exp(s_ij - lse[i,h]) v_j  (0 if V(i) is empty)
- *   out is bfloat16 (round to nearest even), lse float32; the kernels
- *   accumulate in float32 (the quickstart states fp32 reduction).
+ *   q, k, v and out are bfloat16 (or IEEE half with ffa_attn_extras.dtype),
+ *   rounded to nearest even; lse is float32; the kernels accumulate in float32
+ *   (the quickstart states fp32 reduction).  head_dim is 32, 64 or 128.
  *
  * Calls:
  *   ffa_plan        validate the slices and build the work plan on the host

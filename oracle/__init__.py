@@ -1,4 +1,4 @@
-"""CPU oracle for flexible-mask attention forward (fp64).
+"""CPU oracle for flexible-mask attention: forward, gradients and total attention (fp64).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
