@@ -5,8 +5,9 @@
  * The operation (MagiAttention quickstart, section "Single-GPU
  * Flex-Flash-Attention"; FlagAttention user guide, section "FlashAttention"):
  *
- *   q [total_q, Hq, D], k and v [total_k, Hkv, D], head_dim D contiguous.  A mask is a list of S slices (q_range, k_range, type) with
- *   half-open ranges.  Query row i of slice s (qs <= i < qe) sees
+ *   q [total_q, Hq, D], k and v [total_k, Hkv, D], head_dim D contiguous.
+ *   A mask is a list of S slices (q_range, k_range, type) with half-open
+ *   ranges.  Query row i of slice s (qs <= i < qe) sees
  *     FULL      (type 0): keys [ks, ke)
  *     CAUSAL    (type 1): keys [ks, ke - (qe - 1 - i))             -- bottom-right aligned
  *     INVCAUSAL (type 2): keys [ks + (i - qs), ke)                 -- top-left aligned
