@@ -193,16 +193,21 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   (void)sizeof(V2);
   static_assert(!TOT || KV, "total attention walks the key-major worklist");
   constexpr int BN = kBlockN;          // 64 rows per streamed tile
-  constexpr int ROWB = D * 2;          // bytes of one row
-  constexpr int CH = D / 8;            // 16-byte chunks per row
+  // D = 16 keeps its tiles in the 32-wide layout (as the forward): the row products
+  // read only the 16 real head dims, the transposed reads of the unused half only
+  // feed accumulator rows 16-31, which are never stored.
+  constexpr int DL = D < 32 ? 32 : D;  // head dims of an LDS row and of the accumulators
+  constexpr int GC = D / 8;            // 16-byte chunks of a global row
+  constexpr int ROWB = DL * 2;         // bytes of one row in LDS
+  constexpr int CH = DL / 8;           // 16-byte chunks per LDS row
   constexpr int KSTEPS = D / 16;       // MFMA k-steps over the head dim
-  constexpr int DBLK = D / 32;         // 32-wide head-dim blocks of the accumulators
+  constexpr int DBLK = DL / 32;        // 32-wide head-dim blocks of the accumulators
   constexpr int TILE = BN * ROWB;      // bytes of one streamed tile
   constexpr int W = ffa::kWaves;
   constexpr int NLD = TILE / (1024 * W);  // DMA instructions per thread per tile
   constexpr int RPL = 1024 * W / ROWB;    // rows between consecutive DMA instructions
   static_assert(NLD * 1024 * W == TILE, "DMA split");
-  static_assert(BN == 64 && (D == 32 || D == 64 || D == 128), "tile shape");
+  static_assert(BN == 64 && (D == 16 || D == 32 || D == 64 || D == 128), "tile shape");
   // LDS: A0 | B0 | A1 | B1 (double-buffered tiles), then (key-major) L and Dd of
   // the 64 streamed rows per buffer, 1 KiB each (one DMA instruction writes
   // 64 x 16 bytes; the first 256 count).  The L / Dd block has its own base
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   uint32_t r_addr[KSTEPS];
   {
     const int r = lane & 31;
-    const uint32_t a0 = lds + r * ROWB + ((((D / 16) * hh) ^ swz_b<D>(r)) << 4);
+    const uint32_t a0 = lds + r * ROWB + ((((D / 16) * hh) ^ swz_b<DL>(r)) << 4);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) r_addr[s] = a0 ^ (s << 4);
   }
@@ -287,8 +292,8 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     const int grp = lane >> 4, jl = lane & 15;
     const int vr = 4 * hh + (jl >> 2);
     const int cl = 2 * (grp & 1) + ((jl & 3) >> 1);
-    const uint32_t lo = lds + vr * ROWB + ((cl ^ swz_b<D>(vr)) << 4) + (jl & 1) * 8;
-    const uint32_t hi = lds + (vr + 8) * ROWB + ((cl ^ swz_b<D>(vr + 8)) << 4) + (jl & 1) * 8;
+    const uint32_t lo = lds + vr * ROWB + ((cl ^ swz_b<DL>(vr)) << 4) + (jl & 1) * 8;
+    const uint32_t hi = lds + (vr + 8) * ROWB + ((cl ^ swz_b<DL>(vr + 8)) << 4) + (jl & 1) * 8;
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
       t_lo[d] = lo ^ (d << 6);
@@ -304,12 +309,15 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   // row (their scores are masked).
   const int lin0 = wave * 64 + lane;
   const int dr0 = lin0 / CH, dp = lin0 % CH;
-  const int sw0 = swz_b<D>(dr0);
+  const int sw0 = swz_b<DL>(dr0);
+  // D = 16: lanes whose chunk is padding load zeros (an offset past the buffer's end,
+  // no memory access) or, on the last tile, chunk 0 of their row again
+  const bool pad_lane = GC < CH && (dp ^ sw0) >= GC;
   auto dma = [&](const char* base, int64_t st_b, int dst_off, int kstart, int total) {
     if (kstart + BN <= total) {
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kstart * st_b), (short)0, 0x7fffffff, kBufferFlags);
-      const uint32_t goff = (uint32_t)(dr0 * st_b) + ((dp ^ sw0) << 4);
+      const uint32_t goff = pad_lane ? 0x80000000u : (uint32_t)(dr0 * st_b) + ((dp ^ sw0) << 4);
       uint32_t ldst = (uint32_t)(uintptr_t)(FFA_LDS char*)smem + dst_off + wave * 1024;
       int32_t rstep = (int32_t)(RPL * st_b);
       asm volatile("" : "+s"(ldst), "+s"(rstep));
@@ -321,7 +329,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int r = min(kstart + dr0 + i * RPL, total - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)r * st_b + ((dp ^ sw0) << 4)),
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)r * st_b + (pad_lane ? 0 : (dp ^ sw0) << 4)),
                                          (FFA_LDS void*)(smem + dst_off + (i * W + wave) * 1024), 16, 0, 0);
       }
     }
@@ -348,7 +356,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   auto rowprod = [&](auto off_tag, const V8(&f)[KSTEPS], f32x16_t& xa, f32x16_t& xb, auto&& hook) {
     constexpr int OFF = decltype(off_tag)::value;
     constexpr int NQ = 2 * KSTEPS;
-    constexpr int KIF = 4;
+    constexpr int KIF = NQ < 4 ? NQ : 4;  // reads in flight; no more than the tile has (D = 16: 2)
 #pragma unroll
     for (int i = 0; i < 16; ++i) { xa[i] = 0.0f; xb[i] = 0.0f; }
     f32x4_t rf[KIF];
@@ -616,6 +624,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       for (int d = 0; d < DBLK; ++d)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
+          if (32 * d + 8 * gq >= D) continue;  // D = 16: accumulator rows past the head dim
           V4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = (T)(acc[d][4 * gq + e] * mul);

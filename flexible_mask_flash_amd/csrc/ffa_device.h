@@ -146,8 +146,8 @@ __device__ __forceinline__ void tile_next(TileIt& t, const FFA_CONST int32_t* rp
   }
 }
 
-// Host: calls f(std::integral_constant<int, D>{}) for the head dim d (32, 64 or 128;
-// the planner has validated it).
+// Host: calls f(std::integral_constant<int, D>{}) for the head dim d (16, 32, 64 or
+// 128; the planner has validated it).
 template <typename F>
 inline void dispatch_dtype(int dtype, F&& f) {
   if (dtype == FFA_DTYPE_F16) f(_Float16{});
@@ -157,7 +157,8 @@ template <typename F>
 inline void dispatch_head_dim(int d, F&& f) {
   if (d == 128) f(std::integral_constant<int, 128>{});
   else if (d == 64) f(std::integral_constant<int, 64>{});
-  else f(std::integral_constant<int, 32>{});
+  else if (d == 32) f(std::integral_constant<int, 32>{});
+  else f(std::integral_constant<int, 16>{});
 }
 
 }  // namespace dev

@@ -131,10 +131,16 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   using V2 = typename ElemT<T>::v2;
   (void)sizeof(V2);
   constexpr int BN = kBlockN;          // 64 keys per tile
-  constexpr int ROWB = D * 2;          // bytes of one K/V row
-  constexpr int CH = D / 8;            // 16-byte chunks per row
+  // D = 16 keeps its K and V tiles in the 32-wide layout: one MFMA k-step covers
+  // the 16 head dims of a score, and the unused half of a V row only feeds rows
+  // 16-31 of the O accumulator, which are never stored (so the DMA may leave
+  // anything there, as long as it reads nothing outside the tensors).
+  constexpr int DL = D < 32 ? 32 : D;  // head dims of an LDS row and of O
+  constexpr int GC = D / 8;            // 16-byte chunks of a global row
+  constexpr int ROWB = DL * 2;         // bytes of one K/V row in LDS
+  constexpr int CH = DL / 8;           // 16-byte chunks per LDS row
   constexpr int KSTEPS = D / 16;       // MFMA k-steps of K Q^T per 32-key block
-  constexpr int DBLK = D / 32;         // 32-wide head-dim blocks of O
+  constexpr int DBLK = DL / 32;        // 32-wide head-dim blocks of O
   constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
   constexpr int W = ffa::kWaves;       // wavefronts sharing the DMA of a tile
   constexpr int NLD = TILE / (1024 * W);  // DMA instructions per thread per K (or V) tile
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   static_assert(NLD * 1024 * W == TILE, "DMA split");
   constexpr int QSLOTS = 2 * KSTEPS;   // MFMAs of one K Q^T tile
   constexpr int EPQ = 32 / QSLOTS;     // score elements exponentiated per K Q^T MFMA
-  static_assert(BN == 64 && (D == 32 || D == 64 || D == 128), "tile shape");
+  static_assert(BN == 64 && (D == 16 || D == 32 || D == 64 || D == 128), "tile shape");
   // one LDS array: K0 | V0 | K1 | V1; every read offset is a compile-time immediate
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   constexpr int kOffK[2] = {0, 2 * TILE};
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   uint32_t k_addr[KSTEPS];
   {
     const int r = lane & 31;
-    const uint32_t a0 = lds + r * ROWB + ((((D / 16) * hh) ^ swz_k<D>(r)) << 4);
+    const uint32_t a0 = lds + r * ROWB + ((((D / 16) * hh) ^ swz_k<DL>(r)) << 4);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) k_addr[s] = a0 ^ (s << 4);
   }
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     const int grp = lane >> 4, jl = lane & 15;
     const int vr = 4 * hh + (jl >> 2);
     const int cl = 2 * (grp & 1) + ((jl & 3) >> 1);
-    const uint32_t a0 = lds + vr * ROWB + ((cl ^ swz_v<D>(vr)) << 4) + (jl & 1) * 8;
+    const uint32_t a0 = lds + vr * ROWB + ((cl ^ swz_v<DL>(vr)) << 4) + (jl & 1) * 8;
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) v_addr[d] = a0 ^ (d << 6);
   }
@@ -230,8 +236,14 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const int lin0 = wave * 64 + lane;
   const int dr0 = lin0 / CH, dp = lin0 % CH;
   const int64_t kst_b = a.k_st * 2, vst_b = a.v_st * 2;
-  const uint32_t k_goff = (uint32_t)(dr0 * kst_b) + ((dp ^ swz_k<D>(dr0)) << 4);
-  const uint32_t v_goff = (uint32_t)(dr0 * vst_b) + ((dp ^ swz_v<D>(dr0)) << 4);
+  uint32_t k_goff = (uint32_t)(dr0 * kst_b) + ((dp ^ swz_k<DL>(dr0)) << 4);
+  uint32_t v_goff = (uint32_t)(dr0 * vst_b) + ((dp ^ swz_v<DL>(dr0)) << 4);
+  if constexpr (GC < CH) {
+    // padding lanes of a D = 16 row: an offset past the buffer's end loads zeros
+    // without touching memory
+    if ((dp ^ swz_k<DL>(dr0)) >= GC) k_goff = 0x80000000u;
+    if ((dp ^ swz_v<DL>(dr0)) >= GC) v_goff = 0x80000000u;
+  }
   auto dma = [&](const char* base, int64_t st_b, uint32_t goff, int swzc, char* dst, int kstart) {
     if (kstart + BN <= a.total_k) {
       const __amdgpu_buffer_rsrc_t rs =
@@ -251,18 +263,20 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int key = min(kstart + dr0 + i * RPL, a.total_k - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)key * st_b + ((dp ^ swzc) << 4)),
+        int lc = dp ^ swzc;
+        if constexpr (GC < CH) lc = lc < GC ? lc : 0;  // padding lanes re-read chunk 0 of the row
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)key * st_b + (lc << 4)),
                                          (FFA_LDS void*)(dst + (i * W + wave) * 1024), 16, 0, 0);
       }
     }
   };
   auto dma_k = [&](auto buf_tag, int kstart) {
     constexpr int BUF = decltype(buf_tag)::value;
-    dma(kbase, kst_b, k_goff, swz_k<D>(dr0), smem + kOffK[BUF], kstart);
+    dma(kbase, kst_b, k_goff, swz_k<DL>(dr0), smem + kOffK[BUF], kstart);
   };
   auto dma_v = [&](auto buf_tag, int kstart) {
     constexpr int BUF = decltype(buf_tag)::value;
-    dma(vbase, vst_b, v_goff, swz_v<D>(dr0), smem + kOffV[BUF], kstart);
+    dma(vbase, vst_b, v_goff, swz_v<DL>(dr0), smem + kOffV[BUF], kstart);
   };
 
   // ---- K Q^T of one tile from K buffer BUF into (sa, sb); hook(slot) runs after
@@ -270,7 +284,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   auto qk = [&](auto buf_tag, f32x16_t& sa, f32x16_t& sb, auto&& hook) {
     constexpr int OK = kOffK[decltype(buf_tag)::value];
     constexpr int NQ = 2 * KSTEPS;   // fragments of the tile, in MFMA order
-    constexpr int KIF = 4;           // fragment reads in flight (a ring of KIF registers)
+    constexpr int KIF = NQ < 4 ? NQ : 4;  // fragment reads in flight (a ring of KIF registers)
     // MFMA m uses k-step m/2 of key block m%2: the two accumulator chains
     // alternate, so consecutive MFMAs never depend on each other
 #pragma unroll
@@ -580,7 +594,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = (T)(o[d][4 * gq + e] * inv);
           const int c = 4 * d + gq;  // 16-byte chunk of the row
-          *reinterpret_cast<V4*>(st + q * ROWB + ((c ^ swz_k<D>(q)) << 4) + hh * 8) = w;
+          *reinterpret_cast<V4*>(st + q * ROWB + ((c ^ swz_k<DL>(q)) << 4) + hh * 8) = w;
         }
     }
     __bf16* ob = out_p + (int64_t)b * o_sb + (int64_t)h * o_sh;
@@ -592,13 +606,13 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     for (int i = 0; i < NST; ++i) {  // every read issued before the first store
       const int lin = i * 64 + lane;
       const int r = lin / CH, c = lin % CH;
-      val[i] = *reinterpret_cast<const f32x4_t*>(st + r * ROWB + ((c ^ swz_k<D>(r)) << 4));
+      val[i] = *reinterpret_cast<const f32x4_t*>(st + r * ROWB + ((c ^ swz_k<DL>(r)) << 4));
     }
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const int lin = i * 64 + lane;
       const int r = lin / CH, c = lin % CH;
-      if (r < nvalid) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * o_st + c * 8) = val[i];
+      if (r < nvalid && c < GC) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * o_st + c * 8) = val[i];
     }
     if (row_ok && hh == 0) lse_p[(int64_t)b * l_sb + (int64_t)row * l_st + (int64_t)h * l_sh] = lse_v;
   } else if (row_ok) {
@@ -608,6 +622,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
+        if (32 * d + 8 * gq >= D) continue;  // D = 16: the O rows past the head dim
         f32x4_t w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = o[d][4 * gq + e] * inv;

@@ -259,8 +259,8 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   if (total_q < 0 || total_k < 0 || total_q > kMaxTokens || total_k > kMaxTokens)
     return set_error(FFA_ERR_SHAPE, "total_q and total_k must be in [0, 2^30]");
   if (heads_q <= 0 || heads_kv <= 0) return set_error(FFA_ERR_SHAPE, "head counts must be positive");
-  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
-    return set_error(FFA_ERR_SHAPE, "head_dim must be 32, 64 or 128, got " + std::to_string(head_dim));
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return set_error(FFA_ERR_SHAPE, "head_dim must be 16, 32, 64 or 128, got " + std::to_string(head_dim));
   if (heads_q % heads_kv != 0)
     return set_error(FFA_ERR_GQA, "heads_q (" + std::to_string(heads_q) + ") must be a multiple of heads_kv (" +
                                       std::to_string(heads_kv) + ")");

@@ -20,7 +20,7 @@
  *     out[i,h] = sum_{j in V(i)} exp(s_ij - lse[i,h]) v_j  (0 if V(i) is empty)
  *   q, k, v and out are bfloat16 (or IEEE half with ffa_attn_extras.dtype),
  *   rounded to nearest even; lse is float32; the kernels accumulate in float32
- *   (the quickstart states fp32 reduction).  head_dim is 32, 64 or 128.
+ *   (the quickstart states fp32 reduction).  head_dim is 16, 32, 64 or 128.
  *
  * Calls:
  *   ffa_plan        validate the slices and build the work plan on the host
@@ -70,7 +70,7 @@ extern "C" {
 typedef enum {
   FFA_OK = 0,
   FFA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
-  FFA_ERR_SHAPE = 2,       /* total_q/total_k < 0, heads <= 0, head_dim not in {32,64,128} */
+  FFA_ERR_SHAPE = 2,       /* total_q/total_k < 0, heads <= 0, head_dim not 16/32/64/128  */
   FFA_ERR_GQA = 3,         /* heads_q % heads_kv != 0                                      */
   FFA_ERR_RANGE = 4,       /* a range leaves [0, total] or has start > end                 */
   FFA_ERR_MASK_TYPE = 5,   /* a type outside 0..3 (FULL, CAUSAL, INVCAUSAL, BICAUSAL)      */
@@ -157,8 +157,7 @@ typedef struct {
  * mask_types: HOST int32 [num_slices].  num_slices may be 0 (every row empty).
  * The slices must be pairwise disjoint in the (q, k) plane (FFA_ERR_OVERLAP
  * otherwise); empty ranges (start == end) are valid no-ops.  head_dim must be
- * 32, 64 or 128 (the FlagAttention user guide, "FlashAttention", lists 16 to
- * 128).  On success *plan_out receives a plan the caller must destroy.
+ * 16, 32, 64 or 128 (the FlagAttention user guide, "FlashAttention").  On success *plan_out receives a plan the caller must destroy.
  */
 ffa_status ffa_plan(const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* mask_types,
                     int32_t num_slices, int32_t total_q, int32_t total_k, int32_t heads_q,

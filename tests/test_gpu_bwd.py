@@ -272,3 +272,13 @@ def test_bwd_head_dim_32(gpu_lib, seed):
     hq = hkv * int(rng.choice([1, 2, 4]))
     p = W.random_problem(1800 + seed, tq, tk, hq, hkv, 32, n_types=4)
     case(gpu_lib, p, f"D 32 random {seed}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_bwd_head_dim_16(gpu_lib, seed):
+    rng = np.random.default_rng(3000 + seed)
+    tq, tk = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    p = W.random_problem(3000 + seed, tq, tk, hq, hkv, 16, n_types=4)
+    case(gpu_lib, p, f"D 16 random {seed}")

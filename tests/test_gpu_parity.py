@@ -401,3 +401,32 @@ def test_head_dim_32_packed_docs_scaled(gpu_lib):
     q, k, v = W.make_qkv(p)
     out, lse = run(gpu_lib, p, q, k, v)
     compare(out, lse, *oracle_ref(p, q, k, v), what="D 32 config 3 / 8")
+
+
+# ---------------------------------------------------------------- head_dim 16
+
+@pytest.mark.parametrize("seed", range(4))
+def test_head_dim_16_random_slices(gpu_lib, seed):
+    rng = np.random.default_rng(2800 + seed)
+    tq, tk = int(rng.integers(1, 600)), int(rng.integers(1, 600))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    p = W.random_problem(2800 + seed, tq, tk, hq, hkv, 16, n_types=4)
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v, split_tiles=3 if seed == 3 else 0)
+    compare(out, lse, *oracle_ref(p, q, k, v), what=f"D 16 random {seed}")
+
+
+def test_head_dim_16_strided_rows_do_not_leak(gpu_lib):
+    # q, k, v as views of wider rows whose other columns are huge: a padding lane
+    # that read them would corrupt scores or outputs
+    p = W.random_problem(2900, 300, 300, 4, 2, 16, n_types=4)
+    q, k, v = W.make_qkv(p)
+    dev = torch.device("cuda", 0)
+    def wide(x):
+        w = torch.full(x.shape[:2] + (64,), 3.0e4, dtype=x.dtype)
+        w[:, :, :16] = x
+        return w.to(dev)[:, :, :16]
+    out, lse = gpu_lib.flex_flash_attn_fwd(wide(q), wide(k), wide(v), p.q_ranges, p.k_ranges, p.mask_types)
+    torch.cuda.synchronize()
+    compare(out, lse, *oracle_ref(p, q, k, v), what="D 16 wide rows")

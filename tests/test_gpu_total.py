@@ -33,7 +33,7 @@ def test_total_attention_random_slices(gpu_lib, seed):
     tq, tk = int(rng.integers(1, 500)), int(rng.integers(1, 500))
     hkv = int(rng.choice([1, 2]))
     hq = hkv * int(rng.choice([1, 2, 4]))
-    d = [32, 64, 128][seed % 3]
+    d = [16, 32, 64, 128][seed % 4]
     p = W.random_problem(2400 + seed, tq, tk, hq, hkv, d, n_types=4)
     q, k, v = W.make_qkv(p)
     sink = torch.randn((2, hq), generator=torch.Generator().manual_seed(seed)) if seed % 2 else None

@@ -67,7 +67,8 @@ def test_validation_errors():
     ok = ([[0, 8]], [[0, 8]], [1])
     assert plan_status(*ok, 8, 8, 2, 2, 128) == 0
     assert plan_status(*ok, 8, 8, 2, 2, 96) == 2            # head_dim
-    assert plan_status(*ok, 8, 8, 2, 2, 16) == 2
+    assert plan_status(*ok, 8, 8, 2, 2, 8) == 2
+    assert plan_status(*ok, 8, 8, 2, 2, 16) == 0
     assert plan_status(*ok, 8, 8, 2, 2, 32) == 0
     assert plan_status(*ok, 8, 8, 0, 2, 128) == 2           # heads
     assert plan_status(*ok, -1, 8, 2, 2, 128) == 2          # total_q

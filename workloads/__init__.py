@@ -257,6 +257,7 @@ EXTRA_WORKLOADS = {
     "block_sparse_k16": lambda: block_sparse_problem(16384, 64, 16, 0.25, 32, 8, 128, 32, "block_sparse_k16"),
     "block_sparse_q16": lambda: block_sparse_problem(16384, 16, 64, 0.25, 32, 8, 128, 33, "block_sparse_q16"),
     "packed_docs_d32": lambda: _with_head_dim(config(3), 32, "packed_docs_d32"),
+    "packed_docs_d16": lambda: _with_head_dim(config(3), 16, "packed_docs_d16"),
 }
 
 
