@@ -256,9 +256,17 @@ EXTRA_WORKLOADS = {
     "block_sparse": lambda: block_sparse_problem(16384, 64, 64, 0.25, 32, 8, 128, 31, "block_sparse"),
     "block_sparse_k16": lambda: block_sparse_problem(16384, 64, 16, 0.25, 32, 8, 128, 32, "block_sparse_k16"),
     "block_sparse_q16": lambda: block_sparse_problem(16384, 16, 64, 0.25, 32, 8, 128, 33, "block_sparse_q16"),
+    # sliding windows of 1024 keys over the packed documents (bi-causal bands)
+    "sliding_window": lambda: _named(sliding_window_problem(16384, 1024, [0] + list(np.cumsum(config(3).docs)),
+                                                            32, 8, 128, 3), "sliding_window"),
     "packed_docs_d32": lambda: _with_head_dim(config(3), 32, "packed_docs_d32"),
     "packed_docs_d16": lambda: _with_head_dim(config(3), 16, "packed_docs_d16"),
 }
+
+
+def _named(p: Problem, name: str) -> Problem:
+    p.name = name
+    return p
 
 
 def _with_head_dim(p: Problem, d: int, name: str) -> Problem:
