@@ -215,3 +215,35 @@ def test_block_sparse_full_size_plans_quickly():
         assert plan.info["visible_pairs"] == int(oracle.count_visible_pairs(
             p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k)) if p.num_slices < 3000 else True
         assert dt < 5.0, f"{name}: planning took {dt:.2f} s for {p.num_slices} slices"
+
+
+def test_total_attention_rejects_bad_arguments_without_launching():
+    lib = ffa.load_library()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    pb = make_plan(W.make_problem("c", 64, 64, 2, 2, 128, [((0, 64), (0, 64), W.CAUSAL)]))
+    pf = ffa.Plan([[0, 64]], [[0, 64]], [1], 64, 64, 2, 2, 128, num_cus=NCU)
+    wsb = pb.info["bwd_workspace_bytes"]
+
+    def call(plan=pb, **kw):
+        a = dict(meta=fake, batch=1, q=fake, k=fake, lse=fake, tot=fake, st=2 * 128, sh=128, scale=0.1,
+                 ws=fake, wsb=wsb, ex=None)
+        a.update(kw)
+        return lib.ffa_total_attention(plan.handle if plan is not None else None, a["meta"], a["batch"],
+                                       a["q"], 0, a["st"], a["sh"], a["k"], 0, a["st"], a["sh"],
+                                       a["lse"], 0, 2, 1, a["tot"], 0, 1, 64, a["scale"], a["ex"],
+                                       a["ws"], a["wsb"], None)
+
+    assert call(plan=pf) == 11          # no key-major worklist
+    assert call(plan=None) == 1
+    assert call(batch=0) == 11
+    assert call(scale=0.0) == 11
+    assert call(meta=None) == 1
+    assert call(q=None) == 1
+    assert call(tot=None) == 1
+    assert call(ws=None) == 7
+    assert call(wsb=wsb - 4) == 7
+    assert call(k=fake + 2) == 10
+    assert call(st=2 * 128 + 4) == 10
+    ex = ffa.AttnExtras()
+    ex.softcap = -2.0
+    assert call(ex=ctypes.byref(ex)) == 11
