@@ -887,6 +887,7 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dk, dv)");
   }
   if (ex.n_sink > 0 && ex.dsink && has_q) {
+    if ((int64_t)ex.n_sink * p.heads_q > INT32_MAX) return ffa::set_error(FFA_ERR_ARG, "n_sink * heads_q too large");
     SinkArgs sa;
     sa.sink = ex.sink;
     sa.dsink = ex.dsink;

@@ -242,6 +242,7 @@ ffa_status check_extras(const ffa_attn_extras* ex, bool has_rows) {
   if (ex->n_sink < 0) return set_error(FFA_ERR_ARG, "n_sink must be >= 0");
   if (ex->dtype != FFA_DTYPE_BF16 && ex->dtype != FFA_DTYPE_F16)
     return set_error(FFA_ERR_ARG, "dtype must be FFA_DTYPE_BF16 or FFA_DTYPE_F16");
+  if (ex->n_sink > 65536) return set_error(FFA_ERR_ARG, "n_sink must be at most 65536");
   if (ex->n_sink > 0 && has_rows && !ex->sink) return set_error(FFA_ERR_NULL, "n_sink > 0 but sink is NULL");
   return FFA_OK;
 }
@@ -468,6 +469,9 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
     for (const Slice& s : slices) tr.push_back(transpose(s));
     emit(make_tiles(tr, total_k, kKvRowsPerItem), heads_kv, 1, kv_items, kv_runs, kv_tiles);
     kv_tiles *= ratio;
+    // a key-major item walks its tiles once per query head of its kv head (int32 step count)
+    for (const ItemRec& it : kv_items)
+      if ((int64_t)it.tiles * ratio > INT32_MAX) return set_error(FFA_ERR_ARG, "plan too large (key-major item)");
   }
 
   if (items.size() > (size_t)INT32_MAX / kItemRec || runs.size() > (size_t)INT32_MAX ||

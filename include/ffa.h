@@ -101,7 +101,7 @@ typedef struct {
   const float* sink;
   float* dsink;
   int64_t sink_sb, sink_st, sink_ss, sink_sh;
-  int32_t n_sink;   /* sink logits per (row, head); 0: no sink */
+  int32_t n_sink;   /* sink logits per (row, head); 0: no sink; at most 65536 */
   float softcap;    /* 0: off; must be finite and >= 0 */
   int32_t dtype;    /* element type of q, k, v, out, dout and the gradients:
                        FFA_DTYPE_BF16 (0, also when extras is NULL) or FFA_DTYPE_F16 */

@@ -347,6 +347,8 @@ def test_fwd_rejects_bad_arguments_without_launching(lib):
     assert call(ex=ctypes.byref(ex)) == 1
     ex.n_sink, ex.dtype = 0, 7  # unknown element type
     assert call(ex=ctypes.byref(ex)) == 11
+    ex.n_sink, ex.dtype, ex.sink = 70000, 0, fake  # too many sink logits
+    assert call(ex=ctypes.byref(ex)) == 11
     # a split plan without workspace
     ps = ffa.Plan([[0, 32]], [[0, 8192]], [0], 32, 8192, 4, 1, 128, num_cus=NCU, split_tiles=16)
     assert ps.info["workspace_bytes"] > 0
