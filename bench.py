@@ -244,7 +244,7 @@ def main():
         "ms_max": round(max(per), 4),
         "wall_s_timed": round(wall, 3),
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "gcn_arch": getattr(props, "gcnArchName", "")},
+                   "gcn_arch": getattr(props, "gcnArchName", ""), "hip": getattr(torch.version, "hip", None)},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
