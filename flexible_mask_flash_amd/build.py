@@ -22,6 +22,11 @@ SOURCES = ["ffa_plan.cpp", "ffa_fwd.hip", "ffa_bwd.hip"]
 
 # Packed fp32 VALU ops are disabled: the compiler must not form v_pk_{add,mul,fma}_f32.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans"]
+# Per-source device flags.  The backward's score products feed VALU work (exp2,
+# dS) directly, so their MFMAs must write arch VGPRs: left to its heuristic, the
+# compiler gives every MFMA of a one-wave-per-SIMD kernel an AGPR destination and
+# then copies each score out and back (v_accvgpr_read / write around every exp2).
+SOURCE_FLAGS = {"ffa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -44,7 +49,7 @@ def build(verbose: bool = False, asm: bool = False) -> str:
         obj = os.path.join(bdir, src + ".o")
         cmd = [cc, *common]
         if src.endswith(".hip"):
-            cmd += DEVICE_FLAGS
+            cmd += DEVICE_FLAGS + SOURCE_FLAGS.get(src, [])
         else:
             cmd += ["-x", "c++"]
         cmd += ["-c", path, "-o", obj]
@@ -52,7 +57,8 @@ def build(verbose: bool = False, asm: bool = False) -> str:
         objs.append(obj)
         if asm and src.endswith(".hip"):
             s_out = os.path.join(bdir, src + f".{ARCH}.s")
-            jobs.append([cc, *common, *DEVICE_FLAGS, "--cuda-device-only", "-S", path, "-o", s_out])
+            jobs.append([cc, *common, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-S", path, "-o",
+                         s_out])
     # the sources compile independently
     with ThreadPoolExecutor(max_workers=min(len(jobs), 4)) as ex:
         for f in [ex.submit(_run, cmd, verbose) for cmd in jobs]:

@@ -11,7 +11,7 @@
 //
 // Three kernels, all on the caller's stream, no atomics (results are bitwise
 // reproducible):
-//   ffa_bwd_pre          Dd and lse * log2 e per (head, row) into the workspace
+//   ffa_bwd_pre          -Dd and L per (head, row) into the workspace
 //   ffa_bwd_main<D, 0>   dQ, query-major: a workgroup owns the rows of one
 //                        forward item (unsplit) and walks its key tiles
 //   ffa_bwd_main<D, 1>   dK and dV, key-major: a workgroup owns 128 keys of one
@@ -23,6 +23,10 @@
 // and dO), double-buffered and filled by global_load_lds.  Per tile:
 //   X1 = A F1^T, X2 = B F2^T       (v_mfma_f32_32x32x16_bf16, A/B rows from LDS)
 //   P = exp2(X1 c2 - L), dS = P (X2 - Dd)   (fp32)
+// Key-major, the lane's 32 scores belong to 32 different queries, each with its own
+// L and Dd: rather than holding those in registers, the MFMAs start their
+// accumulators from them (X1 from -lse / scale, X2 from -Dd, read from LDS), so that
+// P = exp2(c2 X1) and dS = P X2 directly.
 //   acc1 += A^T dS  (dQ^T or dK^T),  acc2 += B^T P  (dV^T, key-major only)
 // with A^T / B^T read from LDS by ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
@@ -49,12 +53,14 @@ struct PreArgs {
   const __bf16* out;
   const __bf16* dout;
   const float* lse;
-  float* lw;  // [batch][heads_q][total_q]
-  float* dw;  // [batch][heads_q][total_q]
+  float* lw;  // [batch][heads_q][total_q]: L (see ffa_bwd_pre)
+  float* dw;  // [batch][heads_q][total_q]: -Dd
   int64_t o_sb, o_st, o_sh;
   int64_t d_sb, d_st, d_sh;
   int64_t l_sb, l_st, l_sh;
   int32_t total_q, heads_q;
+  float scale;  // softmax_scale
+  int32_t fold;  // L = -lse / scale (uncapped) instead of lse * log2 e (soft-capped)
 };
 
 struct BwdArgs {
@@ -94,6 +100,7 @@ struct SinkArgs {
   const float* dw;
   int64_t sk_sb, sk_st, sk_ss, sk_sh;
   int32_t total_q, heads_q, n_sink;
+  float l_mul;  // lse * log2 e = l_mul * L
 };
 
 // tanh(y) from z = 2 y log2(e): 1 - 2 / (1 + 2^z); exact limits +-1 for +-inf
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(256) void ffa_bwd_dsink(SinkArgs a) {
   float acc = 0.0f;
   for (int t = threadIdx.x; t < a.total_q; t += 256) {
     const float x = sp[(int64_t)t * a.sk_st] * kLog2e;
-    const float c = -__builtin_amdgcn_exp2f(x - a.lw[row0 + t]) * a.dw[row0 + t];
+    const float c = __builtin_amdgcn_exp2f(x - a.l_mul * a.lw[row0 + t]) * a.dw[row0 + t];
     if (a.sk_st != 0) dp[(int64_t)t * a.sk_st] = c;
     else acc += c;
   }
@@ -125,14 +132,12 @@ __global__ __launch_bounds__(256) void ffa_bwd_dsink(SinkArgs a) {
   if (threadIdx.x == 0) *dp = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// Dd[b,h,t] = sum_d dO[b,t,h,d] O[b,t,h,d] (fp32 from the bf16 values) and
-// L[b,h,t] = lse * log2 e, with +inf for rows that see no key (their P is 0).
+// -Dd[b,h,t] with Dd = sum_d dO[b,t,h,d] O[b,t,h,d] (fp32 from the bf16 values), and
+// L[b,h,t] = -lse / scale (fold) or lse * log2 e: either way a row that sees no key
+// (lse = -inf) gets the value that makes its P zero.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
   using V8 = typename ElemT<T>::v8;
-  using V4 = typename ElemT<T>::v4;
-  using V2 = typename ElemT<T>::v2;
-  (void)sizeof(V2);
   constexpr int TPP = D / 8;      // lanes per (row, head), 8 values each
   constexpr int PPB = 256 / TPP;  // (row, head) pairs per workgroup
   const int b = blockIdx.y;
@@ -158,9 +163,10 @@ __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
   for (int m = TPP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (p < pairs && c == 0) {
     const int64_t idx = ((int64_t)b * a.heads_q + h) * a.total_q + t;
-    a.dw[idx] = acc;
+    a.dw[idx] = -acc;
     const float l = a.lse[(int64_t)b * a.l_sb + t * a.l_st + (int64_t)h * a.l_sh];
-    a.lw[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
+    if (a.fold) a.lw[idx] = l == -INFINITY ? -INFINITY : -l / a.scale;
+    else a.lw[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -176,12 +182,13 @@ __device__ __forceinline__ int swz_b(int r) {
                    : ((r >> 2) & 3);  // 64-byte rows: four rows per bank window already
 }
 
-// Occupancy: the query-major kernel fits 256 registers (two waves per SIMD, so one
-// wave's VALU work hides behind the other's MFMAs); the key-major kernel holds
-// two fp32 accumulators and the k, v fragments (~480 registers at D = 128; at
-// D = 64 it would spill under 256), one wave per SIMD.
+// Occupancy: two waves per SIMD wherever the kernel fits 256 registers, so that one
+// wave's VALU work hides behind the other's MFMAs: the query-major kernel, total
+// attention (no accumulators) and the key-major kernel up to D = 64 (~240
+// registers).  At D = 128 the key-major kernel holds two fp32 accumulators of 64
+// registers each and the k, v fragments (~330 registers): one wave per SIMD.
 template <int D, bool KV, bool TOT>
-constexpr int kBwdWaves = (KV && !TOT) ? 1 : 2;  // total attention keeps no accumulators: two waves
+constexpr int kBwdWaves = (KV && !TOT && D > 64) ? 1 : 2;
 
 // TOT (key-major only): FlagAttention's total attention, sum_i P[i,h,j] per key j and
 // query head h -- the same walk over the transposed worklist with only X1 and P.
@@ -257,11 +264,11 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       }
     }
   }
-  // query-major: the row's L and Dd are per lane
+  // query-major: the row's lse * log2 e and -Dd are per lane
   float l_row = 0.0f, d_row = 0.0f;
   if (!KV && row_ok && n_runs > 0) {
     const int64_t idx = ((int64_t)b * a.heads_q + hq) * a.total_q + row;
-    l_row = a.lw[idx];
+    l_row = CAP ? a.lw[idx] : -(a.lw[idx] * a.scale_log2);
     d_row = a.dw[idx];
   }
 
@@ -351,14 +358,13 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     }
   };
 
-  // ---- X = T F^T for the streamed tile T at LDS offset OFF: two 32-row blocks
-  // (xa, xb); hook(m) runs after the m-th MFMA is issued
-  auto rowprod = [&](auto off_tag, const V8(&f)[KSTEPS], f32x16_t& xa, f32x16_t& xb, auto&& hook) {
+  // ---- X = C + T F^T for the streamed tile T at LDS offset OFF: two 32-row blocks
+  // (xa, xb); init() sets C once the LDS reads issued before the call have
+  // landed, hook(m) runs after the m-th MFMA is issued
+  auto rowprod = [&](auto off_tag, const V8(&f)[KSTEPS], f32x16_t& xa, f32x16_t& xb, auto&& hook, auto&& init) {
     constexpr int OFF = decltype(off_tag)::value;
     constexpr int NQ = 2 * KSTEPS;
     constexpr int KIF = NQ < 4 ? NQ : 4;  // reads in flight; no more than the tile has (D = 16: 2)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { xa[i] = 0.0f; xb[i] = 0.0f; }
     f32x4_t rf[KIF];
     static_for<KIF>([&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
@@ -368,6 +374,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       constexpr int m = decltype(m_tag)::value;
       constexpr int later = (m + KIF - 1 < NQ - 1) ? KIF - 1 : NQ - 1 - m;
       lds_wait<later>();
+      if constexpr (m == 0) init(xa, xb);
       fence(rf[m % KIF]);
       if constexpr (m % 2 == 0)
         xa = mfma32(as_v8<T>(rf[m % KIF]), f[m / 2], xa);
@@ -485,23 +492,41 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     constexpr int OB = OA + TILE;
     constexpr int OL = decltype(buf_tag)::value * LDB;  // relative to ld_addr
     f32x16_t xa, xb, ya, yb;
-    // key-major: this tile's L and Dd for the lane's 32 elements
-    f32x4_t lv[8], dv[8];
-    if constexpr (KV) {
+    // key-major: the tile's L (OL) or -Dd (OL + 1024) for the lane's 32 scores,
+    // element e of the pair (xa, xb) in word e % 4 of read e / 4
+    auto read_ld = [&](auto at_tag, f32x4_t(&w)[8]) {
       static_for<8>([&](auto i_tag) {
         constexpr int i = decltype(i_tag)::value;  // block i / 4, group i % 4
-        lv[i] = lds_read_b128<OL + ((i >> 2) * 32 + (i & 3) * 8) * 4>(ld_addr);
-        dv[i] = lds_read_b128<OL + 1024 + ((i >> 2) * 32 + (i & 3) * 8) * 4>(ld_addr);
+        w[i] = lds_read_b128<decltype(at_tag)::value + ((i >> 2) * 32 + (i & 3) * 8) * 4>(ld_addr);
       });
-    }
-    rowprod(std::integral_constant<int, OA>{}, f1, xa, xb, [](auto) {});
-    if constexpr (KV) {
+    };
+    auto zero = [](f32x16_t& u, f32x16_t& w) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { u[i] = 0.0f; w[i] = 0.0f; }
+    };
+    auto from = [](f32x4_t(&r)[8]) {
+      return [&r](f32x16_t& u, f32x16_t& w) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fence(r[i]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          u[e] = r[e >> 2][e & 3];
+          w[e] = r[4 + (e >> 2)][e & 3];
+        }
+      };
+    };
+    // key-major uncapped, X1 starts at -lse / scale; soft-capped, the lane keeps
+    // lse * log2 e of its 32 queries (lv) for the tanh path
+    f32x4_t lv[8];
+    if constexpr (KV) read_ld(std::integral_constant<int, OL>{}, lv);
+    if constexpr (KV && !CAP)
+      rowprod(std::integral_constant<int, OA>{}, f1, xa, xb, [](auto) {}, from(lv));
+    else
+      rowprod(std::integral_constant<int, OA>{}, f1, xa, xb, [](auto) {}, zero);
+    if constexpr (KV && CAP) {
       lds_wait<0>();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        fence(lv[i]);
-        fence(dv[i]);
-      }
+      for (int i = 0; i < 8; ++i) fence(lv[i]);
     }
     if (s.t.edge()) mask(s.t, xa, xb);
     if constexpr (TOT) {
@@ -513,7 +538,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           const float th = tanh_from_2ylog2e(x * a.cap_arg);
           arg = x == -INFINITY ? -INFINITY : __builtin_fmaf(a.cap_log2, th, -lv[e >> 2][e & 3]);
         } else {
-          arg = __builtin_fmaf(x, c2, -lv[e >> 2][e & 3]);
+          arg = x * c2;
         }
         tsum += __builtin_amdgcn_exp2f(arg);
       }
@@ -523,13 +548,19 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
       }
       return;
     }
-    // P = exp2(X1 c2 - L) in place, between the MFMAs of X2.  Soft-capped:
-    // P = exp2(cap_log2 tanh - L) (masked scores stay at P = 0), and what stays in
-    // place is P (1 - tanh^2), the factor of dS; P itself goes to bf16 at once.
+    // P = exp2(X1 c2 - L) in place, between the MFMAs of X2 (key-major uncapped,
+    // L is already in X1).  Soft-capped: P = exp2(cap_log2 tanh - L) (masked scores
+    // stay at P = 0), and what stays in place is P (1 - tanh^2), the factor of dS;
+    // P itself goes to bf16 at once.  Key-major, X2 starts at -Dd.
     auto lval = [&](int e) -> float { return KV ? lv[e >> 2][e & 3] : l_row; };
-    auto dval = [&](int e) -> float { return KV ? dv[e >> 2][e & 3] : d_row; };
     constexpr int EPQ = 32 / (2 * KSTEPS);  // score elements per MFMA of X2
     V8 pf[4], sf[4];
+    f32x4_t dv[8];
+    if constexpr (KV) read_ld(std::integral_constant<int, OL + 1024>{}, dv);
+    auto x2_init = [&](f32x16_t& u, f32x16_t& w) {
+      if constexpr (KV) from(dv)(u, w);
+      else zero(u, w);
+    };
     rowprod(std::integral_constant<int, OB>{}, f2, ya, yb, [&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
 #pragma unroll
@@ -543,14 +574,17 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           const float keep = pr * __builtin_fmaf(-th, th, 1.0f);
           if (e < 16) xa[e] = keep;
           else xb[e - 16] = keep;
+        } else if constexpr (KV) {
+          if (e < 16) xa[e] = __builtin_amdgcn_exp2f(xa[e] * c2);
+          else xb[e - 16] = __builtin_amdgcn_exp2f(xb[e - 16] * c2);
         } else {
-          if (e < 16) xa[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xa[e], c2, -lval(e)));
-          else xb[e - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(xb[e - 16], c2, -lval(e)));
+          if (e < 16) xa[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xa[e], c2, -l_row));
+          else xb[e - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(xb[e - 16], c2, -l_row));
         }
       }
       fence(xa);
       fence(xb);
-    });
+    }, x2_init);
     // dS = P (X2 - Dd) and the bf16 operands of the transposed products, one
     // 16-row step t at a time, so that the VALU work of a step runs behind MFMAs:
     // key-major, all of dS behind the dV product (which needs only P); query-
@@ -561,7 +595,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         const int e = 8 * t + u;
         const float p = e < 16 ? xa[e] : xb[e - 16];
         const float y = e < 16 ? ya[e] : yb[e - 16];
-        sf[t][u] = (T)(p * (y - dval(e)));
+        sf[t][u] = (T)(KV ? p * y : p * (y + d_row));
       }
       fence(sf[t]);
     };
@@ -697,6 +731,8 @@ ffa_status ffa_total_attention(ffa_plan_t plan, const void* d_meta, int32_t batc
     pa.l_sb = l_sb; pa.l_st = l_st; pa.l_sh = l_sh;
     pa.total_q = p.total_q;
     pa.heads_q = p.heads_q;
+    pa.scale = softmax_scale;
+    pa.fold = ex.softcap > 0.0f ? 0 : 1;
     const int ppb = 256 / (p.head_dim / 8);
     const int64_t pairs = (int64_t)p.total_q * p.heads_q;
     const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
@@ -807,6 +843,8 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     pa.l_sb = l_sb; pa.l_st = l_st; pa.l_sh = l_sh;
     pa.total_q = p.total_q;
     pa.heads_q = p.heads_q;
+    pa.scale = softmax_scale;
+    pa.fold = ex.softcap > 0.0f ? 0 : 1;
     const int ppb = 256 / (p.head_dim / 8);
     const int64_t pairs = (int64_t)p.total_q * p.heads_q;
     const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
@@ -897,6 +935,7 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     sa.total_q = p.total_q;
     sa.heads_q = p.heads_q;
     sa.n_sink = ex.n_sink;
+    sa.l_mul = ex.softcap > 0.0f ? 1.0f : -ba.scale_log2;
     const dim3 grid((unsigned)((int64_t)ex.n_sink * p.heads_q), (unsigned)batch);
     hipLaunchKernelGGL(ffa_bwd_dsink, grid, dim3(256), 0, s, sa);
     hipError_t e = hipGetLastError();

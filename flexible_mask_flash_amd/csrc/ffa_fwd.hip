@@ -636,10 +636,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
 // One workgroup per combine entry (up to 128 (row, head) pairs); D/4 lanes per pair.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
-  using V8 = typename ElemT<T>::v8;
   using V4 = typename ElemT<T>::v4;
-  using V2 = typename ElemT<T>::v2;
-  (void)sizeof(V2);
   constexpr int TPP = D / 4;          // threads per (row, head) pair
   constexpr int PPP = 256 / TPP;      // pairs per pass
   const int bid = blockIdx.x;
