@@ -221,7 +221,8 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
  * Every element of dq, dk and dv is written (zero where nothing is visible).
  * Accumulation is fp32; results are bitwise reproducible (no atomics).
  * d_workspace: >= batch * info.bwd_workspace_bytes bytes of device memory
- * (fp32 lse * log2 e and rowsum(dout * out) per head and row).  The plan must
+ * (fp32 per head and row: the lse in the kernels' own scaling and -rowsum(dout * out);
+ * its contents are scratch between the call's kernels, not a result).  The plan must
  * have been built with FFA_PLAN_BACKWARD (FFA_ERR_ARG otherwise); token
  * strides of q, k, v and dout must be below 2^24 elements.  extras: the same
  * sink / softcap as the forward call (dS is multiplied by 1 - tanh^2 under a
