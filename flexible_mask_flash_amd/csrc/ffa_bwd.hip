@@ -477,7 +477,10 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     if (++s.jt >= total_tiles) {
       s.jt = 0;
       ++s.head;
-      tile_first(s.t, itp + 8);
+      // re-read the item's first run rather than keep its seven words live in SGPRs
+      const FFA_CONST int32_t* fr = itp + 8;
+      asm volatile("" : "+s"(fr));
+      tile_first(s.t, fr);
     } else {
       tile_next(s.t, rp, n_runs);
     }
