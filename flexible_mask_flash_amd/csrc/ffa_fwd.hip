@@ -259,7 +259,10 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(uintptr_t)(ldst + i * W * 1024), 16, goff,
                                                  i * rstep, 0, 0);
     } else {
-      // last tile of the key axis: rows past total_k re-read the last row (they are masked)
+      // last tile of the key axis: rows past total_k re-read the last row (they are masked).
+      // The empty asm keeps this path's per-lane address arithmetic inside the branch
+      // (hoisted above it, it would run on every tile).
+      asm volatile("" : "+s"(kstart));
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int key = min(kstart + dr0 + i * RPL, a.total_k - 1);
@@ -461,8 +464,8 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           const float s1v = e + 1 < 16 ? ca[e + 1] : cb[e + 1 - 16];
           const float p0 = __builtin_amdgcn_exp2f(s0v);
           const float p1 = __builtin_amdgcn_exp2f(s1v);
-          ps += p0 + p1;
-                    const V2 pr = {(T)p0, (T)p1};
+          ps = e == 0 ? p0 + p1 : ps + (p0 + p1);  // no 0 + x add for the first pair
+          const V2 pr = {(T)p0, (T)p1};
           pu[e >> 1] = __builtin_bit_cast(uint32_t, pr);
           fence(pu[e >> 1]);
         }
