@@ -319,6 +319,17 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   }
   const int32_t rows_per_item = kSlotsPerItem / G;
   const int32_t n_groups = heads_q / G;
+  // The groups of a q tile are emitted kv head by kv head within each round j of the
+  // ratio / G groups that share a kv head: group g reads kv head g / (ratio / G), and
+  // the hardware hands consecutive workgroups to the 8 XCDs in turn, so with 8 kv heads
+  // every group of a kv head lands on the same XCD (and its L2) instead of two or more.
+  std::vector<int32_t> group_order;
+  group_order.reserve(n_groups);
+  {
+    const int32_t per_kv = ratio / G;
+    for (int32_t j = 0; j < per_kv; ++j)
+      for (int32_t kv = 0; kv < heads_kv; ++kv) group_order.push_back(kv * per_kv + j);
+  }
 
   // ---------------------------------------------------------------- segments and q tiles
   const std::vector<QTile> tiles = make_tiles(slices, total_q, rows_per_item);
@@ -390,7 +401,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
     if (n_chunks <= 1) {
       const int32_t off = (int32_t)(runs.size() / kRec);
       for (const TileRun& r : t.runs) push_run(r.k0, r.n_tiles, r.n_lead, r.n_full, r);
-      for (int32_t g = 0; g < n_groups; ++g)
+      for (const int32_t g : group_order)
         items.push_back({t.q0, t.nrows, g * G, off, (int32_t)t.runs.size(), -1, (int32_t)t.tiles});
       continue;
     }
@@ -418,7 +429,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
       }
       chunk_nruns[c] = nr;
     }
-    for (int32_t g = 0; g < n_groups; ++g) {
+    for (const int32_t g : group_order) {
       const int32_t slot0 = n_slots;
       n_slots += (int32_t)n_chunks * kSlotsPerItem;
       for (int64_t c = 0; c < n_chunks; ++c) {

@@ -354,3 +354,19 @@ def test_fwd_rejects_bad_arguments_without_launching(lib):
     assert ps.info["workspace_bytes"] > 0
     assert lib.ffa_fwd(ps.handle, fake, 1, fake, 0, 512, 128, fake, 0, 128, 128, fake, 0, 128, 128, fake, 0, 512,
                        128, fake, 0, 4, 1, 0.1, None, None, 0, None) == 7
+
+
+def test_head_groups_of_a_kv_head_share_a_dispatch_lane():
+    """Hq 64 / Hkv 8 (two head groups of 4 per kv head): within every block of 8
+    consecutive items (the XCDs the dispatcher cycles through) each item's kv head
+    equals its position, so both groups of a kv head run on the same L2."""
+    qr, kr = [[0, 4096]], [[0, 4096]]
+    plan = ffa.Plan(qr, kr, [1], 4096, 4096, 64, 8, 128, num_cus=NCU)
+    m = parse(plan.meta_host())
+    assert m["G"] == 4
+    kv = m["items"][:, 2] // 8  # h0 / (Hq / Hkv)
+    assert len(kv) % 8 == 0
+    assert (kv == np.arange(len(kv)) % 8).all()
+    # every (q tile, head group) pair appears exactly once
+    pairs = {(int(a), int(b)) for a, b in zip(m["items"][:, 0], m["items"][:, 2])}
+    assert len(pairs) == len(kv) == (4096 // 32) * 16
