@@ -12,7 +12,9 @@ HIP events recorded on the stream the kernels are launched on.
 Prints one JSON line.  `roofline` refers to the dominant kernel (ffa_fwd_main,
 bound by bf16 MFMA); `cpu_baseline` times the fp64 CPU oracle on a bounded
 sample of the same workload; `backward` times ffa_bwd (dq, dk, dv from the
-forward's out and lse) on the same workload, outside the forward's step.
+forward's out and lse) on the same workload, outside the forward's step; `also`
+times the forward of further workloads (default: the heterogeneous-mask mix, the other
+configuration the >= 50% target names) the same way, outside the step.
 """
 from __future__ import annotations
 
@@ -43,6 +45,9 @@ def parse():
     ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--also", default="hetero_mask_mix",
+                    help="comma-separated workloads whose forward is also timed, reported under `also` "
+                         "(the bench line's value stays the --workload one); '' for none")
     ap.add_argument("--softcap", type=float, default=0.0, help="soft-capping of the scores (0: off)")
     ap.add_argument("--total", action="store_true", help="also time the total-attention pass")
     ap.add_argument("--fp16", action="store_true", help="float16 inputs and outputs instead of bfloat16")
@@ -258,11 +263,68 @@ def main():
     }
     if not args.no_backward:
         res["backward"] = backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink)
+    also = [w for w in args.also.split(",") if w and w != p.name]
+    if also and not args.backward_only and args.sinks == 0:  # (sink logits are drawn for the main workload only)
+        res["also"] = [also_leg(args, w) for w in also]
     if args.total:
         res["total_attention"] = total_leg(args, p, qd, kd, lse, scale, sink)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, q, k, v, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def also_leg(args, name: str):
+    """The forward of another workload, timed like the main step (HIP events on the launch
+    stream after at least the same warm-up), with the same options; FLOPs as for the main line."""
+    import torch
+
+    import flexible_mask_flash_amd as ffa
+    import workloads as W
+
+    if name not in WORKLOADS:
+        raise SystemExit(f"--also: unknown workload {name!r}")
+    dev = torch.device("cuda", 0)
+    p = W.workload(name)
+    q, k, v = W.make_qkv(p, dtype=torch.float16 if args.fp16 else None)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, split_tiles=args.split_tiles)
+    plan.device_meta(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((p.total_q, p.heads_q), dtype=torch.float32, device=dev)
+    strides = {"q": (0, qd.stride(0), qd.stride(1)), "k": (0, kd.stride(0), kd.stride(1)),
+               "v": (0, vd.stride(0), vd.stride(1)), "out": (0, out.stride(0), out.stride(1)),
+               "lse": (0, lse.stride(0), lse.stride(1))}
+    extras = ffa.make_extras(None, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q, dtype=qd.dtype)
+    scale = 1.0 / math.sqrt(p.head_dim)
+
+    def step():
+        ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale, extras)
+
+    warm = 0
+    t_w = time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_seconds:
+        step()
+        warm += 1
+        if warm % 5 == 0:
+            torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 4.0 * p.head_dim * p.heads_q * plan.info["visible_pairs"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": p.name, "value": round(tflops, 2), "unit": "TFLOPS", "ms_per_step": round(ms, 4),
+            "steps": args.steps, "warmup": warm, "flops_per_step": flops,
+            "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(p.name),
+            "num_items": int(plan.info["num_items"]), "num_split_items": int(plan.info["num_split_items"])}
 
 
 def total_leg(args, p, qd, kd, lse, scale, sink=None):
