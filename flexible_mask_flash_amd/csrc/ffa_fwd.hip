@@ -585,6 +585,9 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     // rows with 16-byte stores: in the MFMA layout a lane holds 4 consecutive
     // values of each of 16 head-dim groups, which would otherwise become 8-byte
     // stores spread over 32 rows.  Every wave is past its last LDS read first.
+    // out and lse are written once and not read again by this launch: stored
+    // non-temporal (measured: the workgroup's end, which waits for its stores,
+    // comes earlier).
     wg_barrier();
     char* st = smem + wave * (32 * ROWB);
     {
@@ -615,9 +618,11 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     for (int i = 0; i < NST; ++i) {
       const int lin = i * 64 + lane;
       const int r = lin / CH, c = lin % CH;
-      if (r < nvalid && c < GC) *reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * o_st + c * 8) = val[i];
+      if (r < nvalid && c < GC)
+        __builtin_nontemporal_store(val[i], reinterpret_cast<f32x4_t*>(ob + (int64_t)(r0 + r) * o_st + c * 8));
     }
-    if (row_ok && hh == 0) lse_p[(int64_t)b * l_sb + (int64_t)row * l_st + (int64_t)h * l_sh] = lse_v;
+    if (row_ok && hh == 0)
+      __builtin_nontemporal_store(lse_v, lse_p + (int64_t)b * l_sb + (int64_t)row * l_st + (int64_t)h * l_sh);
   } else if (row_ok) {
     const int64_t sidx = (int64_t)b * ea->ws_slots + slot + lrow * G + g;
     float* op = ea->ws_o + sidx * D;
