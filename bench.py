@@ -90,6 +90,9 @@ def measured_traffic(workload: str):
 
 
 def copy_calibration():
+    """A plain 1 GiB device copy: the reference kernel for scaling FETCH_SIZE / WRITE_SIZE
+    (profile this command), and the HBM rate a streaming kernel reaches on this part
+    (timed with HIP events over 20 copies after the first three)."""
     import torch
 
     n = 1 << 30  # bytes
@@ -98,7 +101,16 @@ def copy_calibration():
     for _ in range(3):
         y.copy_(x)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copy_ms": round(ms, 4),
+                      "copy_read_plus_write_TB_s": round(2 * n / (ms * 1e-3) / 1e12, 3)}), flush=True)
 
 
 def cpu_baseline(p, q, k, v, budget_s: float):

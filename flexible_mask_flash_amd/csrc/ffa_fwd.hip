@@ -656,59 +656,84 @@ __global__ __launch_bounds__(256) void ffa_combine(CombineArgs a) {
   const int npairs = nrows * G;
   const int t = threadIdx.x;
   const int dq = (t % TPP) * 4;
-  for (int p = t / TPP; p < npairs; p += PPP) {
-    const int64_t base = (int64_t)b * a.ws_slots + slot0 + p;
+  // Each lane merges two (row, head) pairs per pass, p and p + PPP: the loads of
+  // both are issued before either is consumed, so that twice as many partials are
+  // in flight per lane.  Chunks come in groups of four (four independent loads).
+  constexpr int NG = 4;
+  struct Grp {
+    float l[NG];
+    f32x4_t x[NG];
+  };
+  auto load_grp = [&](int64_t base, int c, Grp& g) {
     const float* lsep = a.ws_lse + base;
     const float* op = a.ws_o + base * D + dq;
-    // chunks in groups of four: the loads of a group are independent, so four
-    // are in flight at a time instead of one dependent load per chunk
-    float mx = -INFINITY;
-    int c = 0;
-    for (; c + 4 <= nch; c += 4) {
-      const float l0 = lsep[(int64_t)c * kSlotsPerItem], l1 = lsep[(int64_t)(c + 1) * kSlotsPerItem];
-      const float l2 = lsep[(int64_t)(c + 2) * kSlotsPerItem], l3 = lsep[(int64_t)(c + 3) * kSlotsPerItem];
-      mx = fmaxf(fmaxf(mx, fmaxf(l0, l1)), fmaxf(l2, l3));
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      if (c + u < nch) {
+        g.l[u] = lsep[(int64_t)(c + u) * kSlotsPerItem];
+        g.x[u] = *reinterpret_cast<const f32x4_t*>(op + (int64_t)(c + u) * kSlotsPerItem * D);
+      } else {
+        g.l[u] = -INFINITY;
+        g.x[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
     }
-    for (; c < nch; ++c) mx = fmaxf(mx, lsep[(int64_t)c * kSlotsPerItem]);
-    const int row = q0 + p / G, h = h0 + p % G;
-    const float* sp = a.n_sink > 0 ? a.sink + (int64_t)b * a.sk_sb + (int64_t)row * a.sk_st + (int64_t)h * a.sk_sh
-                                    : nullptr;
-    for (int s = 0; s < a.n_sink; ++s) mx = fmaxf(mx, sp[s * a.sk_ss]);
-    const float msafe = mx == -INFINITY ? 0.0f : mx;
-    float den = 0.0f;
+  };
+  // running (max, denominator, weighted sum) of one pair, rescaled when the max grows
+  struct Acc {
+    float m = -INFINITY, den = 0.0f;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    c = 0;
-    for (; c + 4 <= nch; c += 4) {
-      f32x4_t x[4];
-      float l[4];
+  };
+  auto merge = [&](Acc& r, const float (&l)[NG], const f32x4_t (&x)[NG]) {
+    const float gm = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
+    const float mn = fmaxf(r.m, gm);
+    if (mn == -INFINITY) return;  // nothing visible yet
+    const float sc = __expf(r.m - mn);  // 0 while r.m is -inf (den and acc are still 0)
+    r.den *= sc;
+    r.acc *= sc;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        l[u] = lsep[(int64_t)(c + u) * kSlotsPerItem];
-        x[u] = *reinterpret_cast<const f32x4_t*>(op + (int64_t)(c + u) * kSlotsPerItem * D);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = __expf(l[u] - msafe);
-        den += w;
-        acc += w * x[u];
-      }
+    for (int u = 0; u < NG; ++u) {
+      const float w = __expf(l[u] - mn);  // 0 for an empty chunk (lse -inf)
+      r.den += w;
+      r.acc += w * x[u];
     }
-    for (; c < nch; ++c) {
-      const float w = __expf(lsep[(int64_t)c * kSlotsPerItem] - msafe);
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(op + (int64_t)c * kSlotsPerItem * D);
-      den += w;
-      acc += w * x;
-    }
+    r.m = mn;
+  };
+  auto finish = [&](int p, Acc& r) {
+    const int row = q0 + p / G, h = h0 + p % G;
     // sink logits: denominator terms without a value
-    for (int s = 0; s < a.n_sink; ++s) den += __expf(sp[s * a.sk_ss] - msafe);
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    if (a.n_sink > 0) {
+      const float* sp = a.sink + (int64_t)b * a.sk_sb + (int64_t)row * a.sk_st + (int64_t)h * a.sk_sh;
+      const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4_t x0[NG] = {z, z, z, z};
+      for (int s0 = 0; s0 < a.n_sink; s0 += NG) {
+        float l[NG];
+#pragma unroll
+        for (int u = 0; u < NG; ++u) l[u] = s0 + u < a.n_sink ? sp[(int64_t)(s0 + u) * a.sk_ss] : -INFINITY;
+        merge(r, l, x0);
+      }
+    }
+    const float inv = r.den > 0.0f ? 1.0f / r.den : 0.0f;
     V4 w4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w4[e] = (T)(acc[e] * inv);
+    for (int e = 0; e < 4; ++e) w4[e] = (T)(r.acc[e] * inv);
     *reinterpret_cast<V4*>(a.out + (int64_t)b * a.o_sb + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + dq) = w4;
     if (dq == 0)
       a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)h * a.l_sh] =
-          den > 0.0f ? msafe + __logf(den) : -INFINITY;
+          r.den > 0.0f ? r.m + __logf(r.den) : -INFINITY;
+  };
+  for (int p = t / TPP; p < npairs; p += 2 * PPP) {
+    const bool two = p + PPP < npairs;  // the second pair exists
+    const int64_t base0 = (int64_t)b * a.ws_slots + slot0 + p;
+    Acc r0, r1;
+    for (int c = 0; c < nch; c += NG) {
+      Grp g0, g1;
+      load_grp(base0, c, g0);
+      if (two) load_grp(base0 + PPP, c, g1);
+      merge(r0, g0.l, g0.x);
+      if (two) merge(r1, g1.l, g1.x);
+    }
+    finish(p, r0);
+    if (two) finish(p + PPP, r1);
   }
 }
 
