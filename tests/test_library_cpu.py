@@ -271,7 +271,14 @@ def test_plan_meta_layout_and_order():
     m = parse(plan.meta_host())
     assert m["G"] == 4 and m["rows"] == 32 and m["bn"] == 64
     cost = m["items"][:, 6] + 2 * (m["items"][:, 4] > 0)
-    assert (np.diff(cost) <= 0).all(), "items are not longest-first"
+    # longest first, except that the second half of the first wave (items NCU .. 2 NCU - 1,
+    # in q-tile blocks of Hq / G items) runs shortest first, pairing long and short items
+    nb = p.heads_q // m["G"]
+    assert (np.diff(cost[:NCU]) <= 0).all() and (np.diff(cost[2 * NCU:]) <= 0).all(), "not longest-first"
+    blocks = cost[NCU:2 * NCU].reshape(-1, nb)
+    assert (blocks == blocks[:, :1]).all(), "a q-tile block was split"
+    assert (np.diff(blocks[:, 0]) >= 0).all(), "second half of the first wave is not shortest-first"
+    assert cost[2 * NCU - 1] >= cost[2 * NCU], "the reversed wave must not reach into the tail"
     # per-document causal: one run per item, every row of the problem in some item
     assert (m["items"][:, 4] == 1).all()
 
