@@ -248,6 +248,24 @@ def test_bitwise_deterministic(gpu_lib):
     assert torch.equal(o3, o4) and torch.equal(l3, l4)
 
 
+@pytest.mark.parametrize("shape", ["hetero", "gqa8"])
+def test_item_order_does_not_change_results(gpu_lib, shape):
+    """The planner only reorders independent items (longest first, the head groups of a kv
+    head on one XCD, the first wave paired long/short per CU): the output must be bitwise
+    that of the plan in natural order."""
+    if shape == "hetero":
+        p = W.scaled(4, 2)
+    else:  # two head groups per kv head: the XCD order permutes the groups of each q tile
+        p = W.make_problem("gqa8", 2048, 2048, 16, 2, 128, [((0, 2048), (0, 2048), W.CAUSAL)], seed=11)
+    q, k, v = W.make_qkv(p)
+    plans = [gpu_lib.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                          p.head_dim, natural_order=nat) for nat in (False, True)]
+    items = [pl.meta_host()[16:16 + 16 * pl.info["num_items"]].reshape(-1, 16)[:, :3].tolist() for pl in plans]
+    assert items[0] != items[1] and sorted(items[0]) == sorted(items[1]), "the orders should differ, items not"
+    (o1, l1), (o2, l2) = [run(gpu_lib, p, q, k, v, plan=pl) for pl in plans]
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_slices(gpu_lib, seed):
     rng = np.random.default_rng(700 + seed)
