@@ -384,6 +384,25 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   struct ItemRec {
     int32_t q0, nrows, h0, run_off, n_runs, slot, tiles;
   };
+  // The first wave fills two slots per CU, and the dispatcher puts workgroup i and
+  // workgroup i + (number of CUs) on the same CU.  Reversing the second half of the
+  // first wave of a longest-first list (in whole q-tile blocks of n_groups items, which
+  // keeps each block's kv heads on their XCDs) pairs the k-th longest item with the k-th
+  // shortest of the wave, so the CUs start with about equal work.  This matters when the
+  // items about fill the slots once (rect_causal_gqa: 512 items of 33-64 tiles, +1.8%
+  // measured on the forward); with many more items the longest-first dispatch after the
+  // first wave balances by itself.  Used for the lists of kernels that run two
+  // workgroups per CU (the forward and the query-major backward).
+  auto pair_first_wave = [&](std::vector<ItemRec>& its) {
+    if (flags & 1u) return;
+    const size_t half = (size_t)num_cus, nb = (size_t)n_groups;
+    if (half % nb != 0 || its.size() <= half) return;
+    const size_t end = std::min(its.size(), 2 * half) / nb * nb;
+    std::vector<ItemRec> seg(its.begin() + half, its.begin() + end);
+    const size_t nblk = seg.size() / nb;
+    for (size_t k = 0; k < nblk; ++k)
+      std::copy(seg.begin() + (nblk - 1 - k) * nb, seg.begin() + (nblk - k) * nb, its.begin() + half + k * nb);
+  };
   std::vector<ItemRec> items;
   std::vector<int32_t> runs;      // flattened run records (kRec each)
   std::vector<int32_t> combine;   // flattened combine records
@@ -447,21 +466,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
       const int32_t cx = x.tiles + (x.n_runs ? kItemOverhead : 1), cy = y.tiles + (y.n_runs ? kItemOverhead : 1);
       return cx > cy;
     });
-    // The first wave fills two slots per CU, and the dispatcher puts workgroup i and
-    // workgroup i + (number of CUs) on the same CU.  Reversing the second half of the
-    // first wave (in whole q-tile blocks, which keeps each block's kv heads on their
-    // XCDs) pairs the k-th longest item with the k-th shortest of the wave, so the CUs
-    // start with about equal work.  This matters when the items about fill the slots
-    // once (rect_causal_gqa: 512 items of 33-64 tiles, +1.8% measured); with many more
-    // items the longest-first dispatch after the first wave balances by itself.
-    const size_t half = (size_t)num_cus, nb = (size_t)n_groups;
-    if (n_split_items == 0 && half % nb == 0 && items.size() > half) {
-      const size_t end = std::min(items.size(), 2 * half) / nb * nb;
-      std::vector<ItemRec> seg(items.begin() + half, items.begin() + end);
-      const size_t nblk = seg.size() / nb;
-      for (size_t k = 0; k < nblk; ++k)
-        std::copy(seg.begin() + (nblk - 1 - k) * nb, seg.begin() + (nblk - k) * nb, items.begin() + half + k * nb);
-    }
+    if (n_split_items == 0) pair_first_wave(items);
   }
 
   // ---------------------------------------------------------------- backward worklists
@@ -490,6 +495,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
         std::stable_sort(its.begin(), its.end(), [](const ItemRec& x, const ItemRec& y) { return x.tiles > y.tiles; });
     };
     emit(tiles, n_groups, G, dq_items, dq_runs, dq_tiles);
+    pair_first_wave(dq_items);
     std::vector<Slice> tr;
     tr.reserve(slices.size());
     for (const Slice& s : slices) tr.push_back(transpose(s));
