@@ -10,7 +10,7 @@ API (names follow the pages):
   flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
                       softmax_scale=None, softcap=0.0, sink_layout="sh")
       MagiAttention's single-GPU FFA interface on packed THD tensors
-      q [Tq,Hq,D], k/v [Tk,Hkv,D] (bf16 or fp16; D 32, 64 or 128) ->
+      q [Tq,Hq,D], k/v [Tk,Hkv,D] (bf16 or fp16; D 16, 32, 64 or 128) ->
       (out [Tq,Hq,D], lse [Tq,Hq] fp32); mask types 0-3, optional sink
       logits and soft-capping.
   flex_flash_attn_bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, ...)
@@ -23,6 +23,11 @@ API (names follow the pages):
       causal), differentiable; returns out, or the 5-tuple (out, lse [B,Hq,M],
       total [B,Hq,N], None, None) when an auxiliary flag is set.
   Plan(...)  a reusable host plan (ffa_plan) with its device metadata.
+
+Streams.  A plan may be used on several streams: its metadata is uploaded once
+per device and other streams wait for that upload; each (device, stream) pair
+gets its own workspace, so calls on different streams never share scratch.
+Calls on one stream are ordered by the stream.
 """
 from __future__ import annotations
 
@@ -115,6 +120,7 @@ _SIGNATURES = [
     ("ffa_plan", _i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PlanOpts),
                         ctypes.POINTER(_vp)]),
     ("ffa_plan_info_get", _i32, [_vp, ctypes.POINTER(PlanInfo)]),
+    ("ffa_plan_sizes", _i32, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     ("ffa_plan_upload", _i32, [_vp, _vp, _sz, _vp]),
     ("ffa_plan_export", _i32, [_vp, _vp, _sz]),
     ("ffa_fwd", _i32, [_vp, _vp, _i32,
@@ -124,6 +130,10 @@ _SIGNATURES = [
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
                        _f32, ctypes.POINTER(AttnExtras), _vp, _sz, _vp]),
+    ("ffa_combine", _i32, [_vp, _vp, _i32,
+                           _vp, _i64, _i64, _i64,
+                           _vp, _i64, _i64, _i64,
+                           ctypes.POINTER(AttnExtras), _vp, _sz, _vp]),
     ("ffa_bwd", _i32, [_vp, _vp, _i32,
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
@@ -226,9 +236,13 @@ class Plan:
         inf = PlanInfo()
         _check(lib.ffa_plan_info_get(self._h, ctypes.byref(inf)), "ffa_plan_info_get")
         self.info = {name: getattr(inf, name) for name, _ in PlanInfo._fields_}
-        self._meta = {}  # device index -> torch int32 tensor
-        self._ws = {}    # device index -> torch uint8 tensor
-        self._bws = {}   # device index -> torch uint8 tensor (backward)
+        # Device state.  The metadata is uploaded once per device; a stream other than
+        # the one that uploaded it waits on the upload's event before its first use.
+        # Workspaces hold per-call scratch (split partials, backward row terms), so each
+        # (device, stream) pair gets its own: calls on different streams never share one.
+        self._meta = {}  # device index -> (torch int32 tensor, upload stream, event)
+        self._ws = {}    # (device index, stream handle) -> torch uint8 tensor
+        self._bws = {}   # (device index, stream handle) -> torch uint8 tensor (backward)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -248,49 +262,56 @@ class Plan:
         _check(lib.ffa_plan_export(self._h, buf.ctypes.data, n), "ffa_plan_export")
         return buf
 
+    def sizes(self):
+        """(meta_bytes, workspace_bytes) from ffa_plan_sizes."""
+        mb, wb = _sz(), _sz()
+        _check(load_library().ffa_plan_sizes(self._h, ctypes.byref(mb), ctypes.byref(wb)), "ffa_plan_sizes")
+        return int(mb.value), int(wb.value)
+
     def device_meta(self, device, stream=None):
-        """Device copy of the metadata (ffa_plan_upload), cached per device."""
+        """Device copy of the metadata (ffa_plan_upload), uploaded once per device; a
+        later use on another stream is ordered after the upload."""
         import torch
 
         dev = torch.device(device)
         key = dev.index if dev.index is not None else torch.cuda.current_device()
-        t = self._meta.get(key)
-        if t is None:
+        s = torch.cuda.current_stream(key) if stream is None else stream
+        ent = self._meta.get(key)
+        if ent is None:
             n = int(self.info["meta_bytes"])
             t = torch.empty(max(1, n // 4), dtype=torch.int32, device=torch.device("cuda", key))
-            s = torch.cuda.current_stream(key) if stream is None else stream
             _check(load_library().ffa_plan_upload(self._h, t.data_ptr(), n, s.cuda_stream), "ffa_plan_upload")
-            self._meta[key] = t
-        return t
+            ev = torch.cuda.Event()
+            ev.record(s)
+            ent = (t, s.cuda_stream, ev)
+            self._meta[key] = ent
+        elif ent[1] != s.cuda_stream:
+            s.wait_event(ent[2])
+            ent[0].record_stream(s)
+        return ent[0]
+
+    def _scratch(self, cache, need: int, device):
+        import torch
+
+        if need == 0:
+            return None, 0
+        dev = torch.device(device)
+        idx = dev.index if dev.index is not None else torch.cuda.current_device()
+        key = (idx, torch.cuda.current_stream(idx).cuda_stream)
+        t = cache.get(key)
+        if t is None or t.numel() < need:
+            with torch.cuda.device(idx):
+                t = torch.empty(need, dtype=torch.uint8, device=torch.device("cuda", idx))
+            cache[key] = t
+        return t, need
 
     def workspace(self, device, batch: int = 1):
-        import torch
-
-        need = int(self.info["workspace_bytes"]) * int(batch)
-        if need == 0:
-            return None, 0
-        dev = torch.device(device)
-        key = dev.index if dev.index is not None else torch.cuda.current_device()
-        t = self._ws.get(key)
-        if t is None or t.numel() < need:
-            t = torch.empty(need, dtype=torch.uint8, device=torch.device("cuda", key))
-            self._ws[key] = t
-        return t, need
-
+        """Split-K workspace of this plan for the current stream of `device`."""
+        return self._scratch(self._ws, int(self.info["workspace_bytes"]) * int(batch), device)
 
     def bwd_workspace(self, device, batch: int = 1):
-        import torch
-
-        need = int(self.info["bwd_workspace_bytes"]) * int(batch)
-        if need == 0:
-            return None, 0
-        dev = torch.device(device)
-        key = dev.index if dev.index is not None else torch.cuda.current_device()
-        t = self._bws.get(key)
-        if t is None or t.numel() < need:
-            t = torch.empty(need, dtype=torch.uint8, device=torch.device("cuda", key))
-            self._bws[key] = t
-        return t, need
+        """Backward workspace of this plan for the current stream of `device`."""
+        return self._scratch(self._bws, int(self.info["bwd_workspace_bytes"]) * int(batch), device)
 
 
 _plan_cache: "OrderedDict[tuple, Plan]" = OrderedDict()
@@ -384,6 +405,22 @@ def run_fwd(plan: Plan, q, k, v, out, lse, strides, batch: int, softmax_scale: f
                      float(softmax_scale), ctypes.byref(extras) if extras is not None else None,
                      ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
     _check(st, "ffa_fwd")
+
+
+def run_combine(plan: Plan, out, lse, strides, batch: int, extras=None):
+    """Call ffa_combine: merge the split partials the last ffa_fwd with this plan left in
+    its workspace (on the current stream).  strides: (sb, st, sh) for "out" and "lse"."""
+    import torch
+
+    dev = out.device
+    s = torch.cuda.current_stream(dev)
+    meta = plan.device_meta(dev, s)
+    ws, ws_bytes = plan.workspace(dev, batch)
+    st = load_library().ffa_combine(plan.handle, meta.data_ptr(), int(batch), out.data_ptr(), *strides["out"],
+                                    lse.data_ptr(), *strides["lse"],
+                                    ctypes.byref(extras) if extras is not None else None,
+                                    ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
+    _check(st, "ffa_combine")
 
 
 def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,

@@ -718,8 +718,8 @@ ffa_status ffa_total_attention(ffa_plan_t plan, const void* d_meta, int32_t batc
   for (int64_t x : {q_sb, q_st, q_sh, k_sb, k_st, k_sh})
     if (!st8(x)) return ffa::set_error(FFA_ERR_ALIGN, "q and k strides must be multiples of 8 elements");
   const int64_t lim = ((int64_t)1 << 31) / (2 * ffa::kBlockN);
-  if (std::llabs(k_st) >= lim || std::llabs(q_st) >= lim)
-    return ffa::set_error(FFA_ERR_ARG, "q / k token strides must be below 2^24 elements");
+  for (int64_t x : {k_st, q_st})
+    if (x < 0 || x >= lim) return ffa::set_error(FFA_ERR_ARG, "q / k token strides must be in [0, 2^24) elements");
   if ((int64_t)p.num_kv_items * batch > INT32_MAX) return ffa::set_error(FFA_ERR_ARG, "grid too large");
   if ((int64_t)p.total_q * p.heads_q > ((int64_t)INT32_MAX) * 16) return ffa::set_error(FFA_ERR_ARG, "grid too large");
 
@@ -826,10 +826,14 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     if (!st8(x)) return ffa::set_error(FFA_ERR_ALIGN, "bf16 tensor strides must be multiples of 8 elements");
   // the kernels address one 64-row tile with 32-bit offsets
   const int64_t lim = ((int64_t)1 << 31) / (2 * ffa::kBlockN);
-  if (std::llabs(k_st) >= lim || std::llabs(v_st) >= lim || std::llabs(q_st) >= lim || std::llabs(d_st) >= lim)
-    return ffa::set_error(FFA_ERR_ARG, "q / k / v / dout token strides must be below 2^24 elements");
+  // (unsigned 32-bit offsets from the tile's first row: token strides must be >= 0)
+  for (int64_t x : {k_st, v_st, q_st, d_st})
+    if (x < 0 || x >= lim)
+      return ffa::set_error(FFA_ERR_ARG, "q / k / v / dout token strides must be in [0, 2^24) elements");
   if (((int64_t)p.num_dq_items + p.num_kv_items) * batch > INT32_MAX) return ffa::set_error(FFA_ERR_ARG, "grid too large");
   if ((int64_t)p.total_q * p.heads_q > ((int64_t)INT32_MAX) * 16) return ffa::set_error(FFA_ERR_ARG, "grid too large");
+  if (ex.n_sink > 0 && ex.dsink && has_q && (int64_t)ex.n_sink * p.heads_q > INT32_MAX)
+    return ffa::set_error(FFA_ERR_ARG, "n_sink * heads_q too large");
 
   hipStream_t s = (hipStream_t)stream;
   float* lw = static_cast<float*>(d_workspace);
@@ -928,7 +932,6 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_main (dk, dv)");
   }
   if (ex.n_sink > 0 && ex.dsink && has_q) {
-    if ((int64_t)ex.n_sink * p.heads_q > INT32_MAX) return ffa::set_error(FFA_ERR_ARG, "n_sink * heads_q too large");
     SinkArgs sa;
     sa.sink = ex.sink;
     sa.dsink = ex.dsink;

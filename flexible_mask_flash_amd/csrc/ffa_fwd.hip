@@ -744,6 +744,58 @@ static ffa_status hip_fail(hipError_t e, const char* what) {
   return ffa::set_error(FFA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+namespace {
+
+// Enqueues the split combine of plan p over the partials at ws (fp32 out
+// [batch][slots][D], then fp32 lse [batch][slots]).  Arguments already validated.
+ffa_status launch_combine(const ffa::Plan& p, const int32_t* meta, int32_t batch, void* out, int64_t o_sb,
+                          int64_t o_st, int64_t o_sh, float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                          const ffa_attn_extras& ex, const float* ws, hipStream_t s) {
+  if (p.num_combine == 0) return FFA_OK;
+  CombineArgs ca;
+  ca.combine = meta + ffa::kHdr + (size_t)p.num_items * kItemRec + (size_t)p.num_runs * kRec;
+  ca.ws_o = ws;
+  ca.ws_lse = ws + (size_t)batch * p.num_slots * p.head_dim;
+  ca.ws_slots = p.num_slots;
+  ca.out = static_cast<__bf16*>(out);
+  ca.lse = lse;
+  ca.o_sb = o_sb; ca.o_st = o_st; ca.o_sh = o_sh;
+  ca.l_sb = l_sb; ca.l_st = l_st; ca.l_sh = l_sh;
+  ca.batch = batch;
+  ca.heads_per_item = p.heads_per_item;
+  ca.sink = ex.n_sink > 0 ? ex.sink : nullptr;
+  ca.sk_sb = ex.sink_sb; ca.sk_st = ex.sink_st; ca.sk_ss = ex.sink_ss; ca.sk_sh = ex.sink_sh;
+  ca.n_sink = ex.n_sink;
+  const dim3 cgrid((unsigned)((int64_t)p.num_combine * batch));
+  dispatch_head_dim(p.head_dim, [&](auto d_tag) {
+    dispatch_dtype(ex.dtype, [&](auto t_tag) {
+      hipLaunchKernelGGL((ffa_combine<decltype(d_tag)::value, decltype(t_tag)>), cgrid, dim3(256), 0, s, ca);
+    });
+  });
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch ffa_combine");
+  return FFA_OK;
+}
+
+// Checks shared by ffa_fwd and ffa_combine: the output tensors and the workspace.
+ffa_status check_outputs(const ffa::Plan& p, int32_t batch, const void* d_meta, const void* out, int64_t o_sb,
+                         int64_t o_st, int64_t o_sh, const float* lse, const void* d_workspace,
+                         size_t workspace_bytes) {
+  if (batch < 1) return ffa::set_error(FFA_ERR_ARG, "batch must be >= 1");
+  if (!d_meta) return ffa::set_error(FFA_ERR_NULL, "d_meta is NULL");
+  if (p.total_q > 0 && (!out || !lse)) return ffa::set_error(FFA_ERR_NULL, "out and lse must be non-NULL");
+  const int64_t ws_need = (int64_t)batch * p.workspace_bytes();
+  if (ws_need > 0 && (!d_workspace || (int64_t)workspace_bytes < ws_need))
+    return ffa::set_error(FFA_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                                 " bytes, plan needs " + std::to_string(ws_need));
+  if (((uintptr_t)out & 15u) != 0) return ffa::set_error(FFA_ERR_ALIGN, "out must be 16-byte aligned");
+  if ((o_sb & 7) || (o_st & 7) || (o_sh & 7))
+    return ffa::set_error(FFA_ERR_ALIGN, "out strides must be multiples of 8 elements");
+  return FFA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t ffa_abi_version(void) { return FFA_ABI_VERSION; }
@@ -827,6 +879,14 @@ ffa_status ffa_plan_info_get(ffa_plan_t plan, ffa_plan_info* info) {
   return FFA_OK;
 }
 
+ffa_status ffa_plan_sizes(ffa_plan_t plan, size_t* meta_bytes, size_t* workspace_bytes) {
+  ffa::clear_error();
+  if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
+  if (meta_bytes) *meta_bytes = (size_t)plan->plan.meta_bytes();
+  if (workspace_bytes) *workspace_bytes = (size_t)plan->plan.workspace_bytes();
+  return FFA_OK;
+}
+
 ffa_status ffa_plan_upload(ffa_plan_t plan, void* d_meta, size_t meta_bytes, void* stream) {
   ffa::clear_error();
   if (!plan || !d_meta) return ffa::set_error(FFA_ERR_NULL, "plan or d_meta is NULL");
@@ -858,32 +918,28 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   ffa::clear_error();
   if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
   const ffa::Plan& p = plan->plan;
-  if (batch < 1) return ffa::set_error(FFA_ERR_ARG, "batch must be >= 1");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return ffa::set_error(FFA_ERR_ARG, "softmax_scale must be finite and > 0");
   const ffa_status xs = ffa::check_extras(extras, p.total_q > 0);
   if (xs != FFA_OK) return xs;
   ffa_attn_extras ex = {};
   if (extras) ex = *extras;
-  if (!d_meta) return ffa::set_error(FFA_ERR_NULL, "d_meta is NULL");
-  if (p.total_q > 0 && (!q || !out || !lse)) return ffa::set_error(FFA_ERR_NULL, "q, out and lse must be non-NULL");
+  const ffa_status os = check_outputs(p, batch, d_meta, out, o_sb, o_st, o_sh, lse, d_workspace, workspace_bytes);
+  if (os != FFA_OK) return os;
+  if (p.total_q > 0 && !q) return ffa::set_error(FFA_ERR_NULL, "q must be non-NULL");
   const bool need_kv = p.total_tiles > 0;
   if (need_kv && (!k || !v)) return ffa::set_error(FFA_ERR_NULL, "k and v must be non-NULL");
-  const int64_t ws_need = (int64_t)batch * p.workspace_bytes();
-  if (ws_need > 0 && (!d_workspace || (int64_t)workspace_bytes < ws_need))
-    return ffa::set_error(FFA_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
-                                                 " bytes, plan needs " + std::to_string(ws_need));
   auto al16 = [](const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; };
   auto st8 = [](int64_t s) { return (s & 7) == 0; };
-  if (!al16(q) || !al16(out) || (need_kv && (!al16(k) || !al16(v))))
-    return ffa::set_error(FFA_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (!al16(q) || (need_kv && (!al16(k) || !al16(v))))
+    return ffa::set_error(FFA_ERR_ALIGN, "q, k and v must be 16-byte aligned");
   if (!st8(q_sb) || !st8(q_st) || !st8(q_sh) || !st8(k_sb) || !st8(k_st) || !st8(k_sh) || !st8(v_sb) ||
-      !st8(v_st) || !st8(v_sh) || !st8(o_sb) || !st8(o_st) || !st8(o_sh))
-    return ffa::set_error(FFA_ERR_ALIGN, "q, k, v and out strides must be multiples of 8 elements");
-  // the kernels address one 64-key tile with 32-bit offsets
+      !st8(v_st) || !st8(v_sh))
+    return ffa::set_error(FFA_ERR_ALIGN, "q, k and v strides must be multiples of 8 elements");
+  // the kernels address one 64-key tile with unsigned 32-bit offsets from its first key
   const int64_t kv_lim = ((int64_t)1 << 31) / (2 * ffa::kBlockN);
-  if (need_kv && (std::llabs(k_st) >= kv_lim || std::llabs(v_st) >= kv_lim))
-    return ffa::set_error(FFA_ERR_ARG, "k / v token strides must be below 2^24 elements");
+  if (need_kv && (k_st < 0 || v_st < 0 || k_st >= kv_lim || v_st >= kv_lim))
+    return ffa::set_error(FFA_ERR_ARG, "k / v token strides must be in [0, 2^24) elements");
   if (p.num_items == 0) return FFA_OK;
   if ((int64_t)p.num_items * batch > INT32_MAX || (int64_t)p.num_combine * batch > INT32_MAX)
     return ffa::set_error(FFA_ERR_ARG, "grid too large");
@@ -930,32 +986,24 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   });
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch ffa_fwd_main");
+  return launch_combine(p, meta, batch, out, o_sb, o_st, o_sh, lse, l_sb, l_st, l_sh, ex, fa.ws_o, s);
+}
 
-  if (p.num_combine > 0) {
-    CombineArgs ca;
-    ca.combine = fa.runs + (size_t)p.num_runs * kRec;
-    ca.ws_o = fa.ws_o;
-    ca.ws_lse = fa.ws_lse;
-    ca.ws_slots = p.num_slots;
-    ca.out = fa.out;
-    ca.lse = lse;
-    ca.o_sb = o_sb; ca.o_st = o_st; ca.o_sh = o_sh;
-    ca.l_sb = l_sb; ca.l_st = l_st; ca.l_sh = l_sh;
-    ca.batch = batch;
-    ca.heads_per_item = p.heads_per_item;
-    ca.sink = fa.sink;
-    ca.sk_sb = fa.sk_sb; ca.sk_st = fa.sk_st; ca.sk_ss = fa.sk_ss; ca.sk_sh = fa.sk_sh;
-    ca.n_sink = fa.n_sink;
-    const dim3 cgrid((unsigned)((int64_t)p.num_combine * batch));
-    dispatch_head_dim(p.head_dim, [&](auto d_tag) {
-      dispatch_dtype(ex.dtype, [&](auto t_tag) {
-        hipLaunchKernelGGL((ffa_combine<decltype(d_tag)::value, decltype(t_tag)>), cgrid, dim3(256), 0, s, ca);
-      });
-    });
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "launch ffa_combine");
-  }
-  return FFA_OK;
+ffa_status ffa_combine(ffa_plan_t plan, const void* d_meta, int32_t batch, void* out, int64_t o_sb, int64_t o_st,
+                       int64_t o_sh, float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                       const ffa_attn_extras* extras, const void* d_workspace, size_t workspace_bytes, void* stream) {
+  ffa::clear_error();
+  if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
+  const ffa::Plan& p = plan->plan;
+  const ffa_status xs = ffa::check_extras(extras, p.total_q > 0);
+  if (xs != FFA_OK) return xs;
+  ffa_attn_extras ex = {};
+  if (extras) ex = *extras;
+  const ffa_status os = check_outputs(p, batch, d_meta, out, o_sb, o_st, o_sh, lse, d_workspace, workspace_bytes);
+  if (os != FFA_OK) return os;
+  if ((int64_t)p.num_combine * batch > INT32_MAX) return ffa::set_error(FFA_ERR_ARG, "grid too large");
+  return launch_combine(p, static_cast<const int32_t*>(d_meta), batch, out, o_sb, o_st, o_sh, lse, l_sb, l_st, l_sh,
+                        ex, static_cast<const float*>(d_workspace), (hipStream_t)stream);
 }
 
 }  // extern "C"

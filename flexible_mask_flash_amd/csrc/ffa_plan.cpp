@@ -170,7 +170,11 @@ double lpt_makespan(std::vector<int64_t>& costs, int64_t slots) {
   }
   return (double)*std::max_element(heap.begin(), heap.end());
 }
-constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+// Largest token count of either axis.  It keeps every bound a slice can produce
+// (edge_base = ke - qe + 1 <= kMaxTokens, lo_base = ks - qs >= 1 - kMaxTokens, and
+// the same for the transposed slices) strictly inside (-kNoEdge, kNoEdge), so a real
+// bound never reads as "no bound", and row + bound stays inside int32 on the device.
+constexpr int64_t kMaxTokens = ((int64_t)1 << 30) - 2;
 
 // Steps 1-3: q segments, q tiles of rows_per_item rows and their key runs.
 std::vector<QTile> make_tiles(const std::vector<Slice>& slices, int32_t total_rows, int32_t rows_per_item) {
@@ -258,7 +262,7 @@ ffa_status build_plan(const int32_t* q_ranges, const int32_t* k_ranges, const in
   if (num_slices > 0 && (!q_ranges || !k_ranges || !mask_types))
     return set_error(FFA_ERR_NULL, "q_ranges, k_ranges and mask_types must be non-NULL when num_slices > 0");
   if (total_q < 0 || total_k < 0 || total_q > kMaxTokens || total_k > kMaxTokens)
-    return set_error(FFA_ERR_SHAPE, "total_q and total_k must be in [0, 2^30]");
+    return set_error(FFA_ERR_SHAPE, "total_q and total_k must be in [0, 2^30 - 2]");
   if (heads_q <= 0 || heads_kv <= 0) return set_error(FFA_ERR_SHAPE, "head counts must be positive");
   if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
     return set_error(FFA_ERR_SHAPE, "head_dim must be 16, 32, 64 or 128, got " + std::to_string(head_dim));

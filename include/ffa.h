@@ -24,11 +24,13 @@
  *
  * Calls:
  *   ffa_plan        validate the slices and build the work plan on the host
- *   ffa_plan_info   sizes and statistics of a plan
+ *   ffa_plan_info_get  sizes and statistics of a plan
+ *   ffa_plan_sizes  the metadata and workspace sizes alone
  *   ffa_plan_upload copy the plan's metadata to a caller-owned device buffer
  *   ffa_plan_export copy the same metadata to host memory (inspection, tests)
  *   ffa_fwd         run the forward on a stream (main kernel, then the split
  *                   combine when the plan has split rows)
+ *   ffa_combine     the split combine alone, over partials ffa_fwd left
  *   ffa_bwd         gradients dq, dk, dv from the forward's out and lse and the
  *                   upstream gradient dout (plan built with FFA_PLAN_BACKWARD)
  *   ffa_total_attention  attention probabilities summed over the queries, per key
@@ -70,7 +72,8 @@ extern "C" {
 typedef enum {
   FFA_OK = 0,
   FFA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
-  FFA_ERR_SHAPE = 2,       /* total_q/total_k < 0, heads <= 0, head_dim not 16/32/64/128  */
+  FFA_ERR_SHAPE = 2,       /* total_q/total_k outside [0, 2^30 - 2], heads <= 0,
+                              head_dim not 16/32/64/128                                    */
   FFA_ERR_GQA = 3,         /* heads_q % heads_kv != 0                                      */
   FFA_ERR_RANGE = 4,       /* a range leaves [0, total] or has start > end                 */
   FFA_ERR_MASK_TYPE = 5,   /* a type outside 0..3 (FULL, CAUSAL, INVCAUSAL, BICAUSAL)      */
@@ -164,7 +167,15 @@ ffa_status ffa_plan(const int32_t* q_ranges, const int32_t* k_ranges, const int3
                     int32_t heads_kv, int32_t head_dim, const ffa_plan_opts* opts,
                     ffa_plan_t* plan_out);
 
+/* All statistics of a plan (sizes, the visible-pair count behind the FLOP
+ * metric, item counts).  FFA_ERR_NULL when plan or info is NULL. */
 ffa_status ffa_plan_info_get(ffa_plan_t plan, ffa_plan_info* info);
+
+/* The two buffer sizes a caller must provide, without the rest of the
+ * statistics: *meta_bytes for ffa_plan_upload, *workspace_bytes for ffa_fwd
+ * per batch element (0 when the plan splits no row).  Either output pointer
+ * may be NULL (that size is not returned); FFA_ERR_NULL when plan is NULL. */
+ffa_status ffa_plan_sizes(ffa_plan_t plan, size_t* meta_bytes, size_t* workspace_bytes);
 
 /* Copy the plan metadata (info.meta_bytes) into d_meta, a device buffer of
  * meta_bytes >= info.meta_bytes, with hipMemcpyAsync on `stream` (a hipStream_t;
@@ -181,14 +192,21 @@ ffa_status ffa_plan_upload(ffa_plan_t plan, void* d_meta, size_t meta_bytes, voi
 ffa_status ffa_plan_export(ffa_plan_t plan, void* h_meta, size_t meta_bytes);
 
 /*
- * Forward.  All tensor pointers are DEVICE pointers; strides are in elements.
+ * Forward: out and lse of the operation at the top of this header for every
+ * query row and head (MagiAttention quickstart, "Single-GPU
+ * Flex-Flash-Attention": flex_flash_attn_func returns out and meta.lse;
+ * FlagAttention user guide, "FlashAttention": the log-normalizer lse).  Plans
+ * that split long rows run a second kernel that merges float32 partial (out,
+ * lse) pairs with a global logsumexp (FlagAttention user guide, "Split-KV and
+ * paged attention").  All tensor pointers are DEVICE pointers; strides are in elements.
  *   batch >= 1 independent problems share the plan; element b of every tensor
  *   starts at base + b * stride_b.
  *   q:   bf16, element (b, t, h, d) at q[b*q_sb + t*q_st + h*q_sh + d]
  *   k,v: bf16, (b, t, hkv, d) likewise with their own strides
  *   out: bf16, like q (written for every row and head)
  *   lse: fp32, (b, t, h) at lse[b*l_sb + t*l_st + h*l_sh]
- * q, k, v, out bases and their strides must be multiples of 8 elements (16 B).
+ * q, k, v, out bases and their strides must be multiples of 8 elements (16 B);
+ * the token strides of k and v must be in [0, 2^24) elements (FFA_ERR_ARG).
  * softmax_scale must be finite and > 0 (callers resolve "None" to 1/sqrt(D)).
  * extras: sink / softcap (see ffa_attn_extras), NULL for plain attention.
  * d_meta: the buffer filled by ffa_plan_upload.  d_workspace: workspace_bytes
@@ -204,6 +222,26 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
                    float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
                    float softmax_scale, const ffa_attn_extras* extras,
                    void* d_workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The merge step of a split plan on its own (FlagAttention user guide,
+ * "Split-KV and paged attention": a second kernel merges the partial results
+ * with a global logsumexp): for every split (row, head),
+ *   lse = ln sum_c exp(lse_c),  out = sum_c exp(lse_c - lse) out_c
+ * over the float32 partials (out_c, lse_c) that the main kernel of ffa_fwd left
+ * in d_workspace, in a fixed chunk order; sink logits in extras join the sum as
+ * terms without a value.  ffa_fwd already runs this step; calling ffa_combine
+ * after it on the same workspace rewrites the split rows' out and lse with the
+ * same values (this is how the merge is timed alone).  Only split rows are
+ * written; a plan without split rows enqueues nothing.  Arguments, strides and
+ * error rules are those of ffa_fwd (d_workspace must hold the partials of an
+ * ffa_fwd call with the same plan, batch and sink logits).
+ */
+ffa_status ffa_combine(ffa_plan_t plan, const void* d_meta, int32_t batch,
+                       void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                       float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                       const ffa_attn_extras* extras, const void* d_workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * Backward.  The derivative of the operation above for a loss L with

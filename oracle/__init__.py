@@ -16,12 +16,10 @@ from .fwd import (  # noqa: F401
     INVCAUSAL,
     BICAUSAL,
     slice_row_interval,
-    row_intervals,
     mask_rows,
     dense_mask,
     count_visible_pairs,
     attend,
-    attend_dense,
     total_attention,
     capped_scores,
     sink_logits,

@@ -62,17 +62,6 @@ def slice_row_interval(i: int, qs: int, qe: int, ks: int, ke: int, mask_type: in
     return (a, b)
 
 
-def row_intervals(i: int, q_ranges, k_ranges, mask_types) -> List[Tuple[int, int]]:
-    """Non-empty key intervals row i sees, one per slice covering the row."""
-    out = []
-    for (qs, qe), (ks, ke), t in zip(np.asarray(q_ranges).tolist(), np.asarray(k_ranges).tolist(),
-                                     np.asarray(mask_types).tolist()):
-        a, b = slice_row_interval(i, qs, qe, ks, ke, t)
-        if b > a:
-            out.append((a, b))
-    return out
-
-
 def mask_rows(rows: Sequence[int], q_ranges, k_ranges, mask_types, total_k: int) -> np.ndarray:
     """Explicit boolean mask [len(rows), total_k]; True = key visible."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -266,31 +255,6 @@ def total_attention(q, k, q_ranges, k_ranges, mask_types, softmax_scale: Optiona
                 p = e / np.where(den > 0, den, 1.0)[:, None]
                 tot[cols, h] += p.sum(axis=0)
     return tot
-
-
-def attend_dense(q, k, v, mask: np.ndarray, softmax_scale: Optional[float] = None):
-    """Softmax attention under an explicit [Tq, Tk] boolean mask (fp64)."""
-    q = _as_f64(q)
-    k = _as_f64(k)
-    v = _as_f64(v)
-    tq, hq, d = q.shape
-    hkv = k.shape[1]
-    grp = hq // hkv
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    out = np.zeros((tq, hq, d))
-    lse = np.full((tq, hq), -np.inf)
-    for h in range(hq):
-        g = h // grp
-        s = (q[:, h, :] @ k[:, g, :].T) * scale
-        s = np.where(mask, s, -np.inf)
-        mx = s.max(axis=1)
-        safe = np.where(np.isfinite(mx), mx, 0.0)
-        p = np.exp(s - safe[:, None])
-        den = p.sum(axis=1)
-        ne = den > 0
-        lse[:, h] = np.where(ne, safe + np.log(np.where(ne, den, 1.0)), -np.inf)
-        out[:, h, :] = np.where(ne[:, None], (p @ v[:, g, :]) / np.where(ne, den, 1.0)[:, None], 0.0)
-    return out, lse
 
 
 def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):

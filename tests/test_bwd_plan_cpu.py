@@ -189,11 +189,19 @@ def test_bwd_rejects_bad_arguments_without_launching():
     assert call(dq=fake + 4) == 10
     assert call(st=2 * 128 + 2) == 10
     assert call(st=(1 << 24) * 8) == 11  # token stride beyond the 32-bit tile addressing
+    assert call(st=-256) == 11            # negative token strides (unsigned tile offsets)
     ex = ffa.AttnExtras()
     ex.n_sink = 1  # no sink pointer
     assert call(ex=ctypes.byref(ex)) == 1
     ex.n_sink, ex.softcap = 0, float("inf")
     assert call(ex=ctypes.byref(ex)) == 11
+    # n_sink * heads_q beyond the d sink grid: refused before the first kernel is enqueued
+    hq = 40000
+    pbig = make_plan(W.make_problem("h", 32, 32, hq, 1, 16, [((0, 32), (0, 32), W.FULL)]))
+    ex = ffa.AttnExtras()
+    ex.n_sink, ex.sink, ex.dsink, ex.sink_ss, ex.sink_sh = 65536, fake, fake, hq, 1
+    assert call(plan=pbig, st=hq * 16, sh=16, wsb=pbig.info["bwd_workspace_bytes"], ex=ctypes.byref(ex)) == 11
+    assert "n_sink" in lib.ffa_last_error().decode()
 
 
 @pytest.mark.parametrize("qb,kb", [(64, 64), (16, 64), (64, 16), (64, 1), (8, 64)])
@@ -205,16 +213,26 @@ def test_block_sparse_worklists_cover_mask_exactly_once(qb, kb):
     check_plan(p)
 
 
-def test_block_sparse_full_size_plans_quickly():
+@pytest.mark.parametrize("name,qb,kb", [("block_sparse", 64, 64), ("block_sparse_k16", 64, 16),
+                                         ("block_sparse_q16", 16, 64)])
+def test_block_sparse_full_size_plans_quickly(name, qb, kb):
+    # The visible-pair count (the FLOP count of the bench lines) against the closed form of
+    # the construction: every kept (query block, key block) cell is a disjoint FULL slice of
+    # qb x kb pairs (16384 is a multiple of both block sizes), and every query block keeps
+    # round(nk / 4) of the nk key blocks.
     import time
-    for name in ("block_sparse", "block_sparse_k16", "block_sparse_q16"):
-        p = W.workload(name)
-        t0 = time.perf_counter()
-        plan = make_plan(p)
-        dt = time.perf_counter() - t0
-        assert plan.info["visible_pairs"] == int(oracle.count_visible_pairs(
-            p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k)) if p.num_slices < 3000 else True
-        assert dt < 5.0, f"{name}: planning took {dt:.2f} s for {p.num_slices} slices"
+    p = W.workload(name)
+    nq, nk = 16384 // qb, 16384 // kb
+    n_keep = round(0.25 * nk)
+    assert p.num_slices == nq * n_keep
+    cells = np.stack([p.q_ranges[:, 0] // qb, p.k_ranges[:, 0] // kb], axis=1)
+    assert len({tuple(c) for c in cells.tolist()}) == p.num_slices  # no cell twice
+    assert ((p.q_ranges[:, 1] - p.q_ranges[:, 0]) == qb).all() and ((p.k_ranges[:, 1] - p.k_ranges[:, 0]) == kb).all()
+    t0 = time.perf_counter()
+    plan = make_plan(p)
+    dt = time.perf_counter() - t0
+    assert plan.info["visible_pairs"] == nq * n_keep * qb * kb
+    assert dt < 5.0, f"{name}: planning took {dt:.2f} s for {p.num_slices} slices"
 
 
 def test_total_attention_rejects_bad_arguments_without_launching():
@@ -244,6 +262,7 @@ def test_total_attention_rejects_bad_arguments_without_launching():
     assert call(wsb=wsb - 4) == 7
     assert call(k=fake + 2) == 10
     assert call(st=2 * 128 + 4) == 10
+    assert call(st=-256) == 11            # negative token strides (unsigned tile offsets)
     ex = ffa.AttnExtras()
     ex.softcap = -2.0
     assert call(ex=ctypes.byref(ex)) == 11

@@ -361,6 +361,68 @@ def test_fwd_rejects_bad_arguments_without_launching(lib):
     assert ps.info["workspace_bytes"] > 0
     assert lib.ffa_fwd(ps.handle, fake, 1, fake, 0, 512, 128, fake, 0, 128, 128, fake, 0, 128, 128, fake, 0, 512,
                        128, fake, 0, 4, 1, 0.1, None, None, 0, None) == 7
+    # negative k / v token strides: the kernels address a tile with unsigned offsets
+    for ks_, vs_ in ((-256, 256), (256, -256)):
+        assert lib.ffa_fwd(p.handle, fake, 1, fake, 0, 256, 128, fake, 0, ks_, 128, fake, 0, vs_, 128, fake, 0,
+                           256, 128, fake, 0, 2, 1, 0.1, None, None, 0, None) == 11
+
+
+def test_plan_sizes_match_plan_info(lib):
+    for split in (-1, 16):
+        p = ffa.Plan([[0, 32]], [[0, 8192]], [0], 32, 8192, 4, 1, 128, num_cus=NCU, split_tiles=split)
+        assert p.sizes() == (p.info["meta_bytes"], p.info["workspace_bytes"])
+        assert (p.info["workspace_bytes"] > 0) == (split > 0)
+        mb = ctypes.c_size_t(0)
+        assert lib.ffa_plan_sizes(p.handle, ctypes.byref(mb), None) == 0 and mb.value == p.info["meta_bytes"]
+        assert lib.ffa_plan_sizes(p.handle, None, None) == 0
+    assert lib.ffa_plan_sizes(None, None, None) == 1
+
+
+def test_combine_rejects_bad_arguments_without_launching(lib):
+    fake = 1 << 20  # never dereferenced: validation fails first
+    ps = ffa.Plan([[0, 32]], [[0, 8192]], [0], 32, 8192, 4, 1, 128, num_cus=NCU, split_tiles=16)
+    wsb = ps.info["workspace_bytes"]
+    assert ps.info["num_combine"] > 0
+
+    def call(plan=ps, **kw):
+        a = dict(meta=fake, batch=1, out=fake, lse=fake, st=512, sh=128, ws=fake, wsb=wsb, ex=None)
+        a.update(kw)
+        return lib.ffa_combine(plan.handle if plan is not None else None, a["meta"], a["batch"], a["out"], 0,
+                               a["st"], a["sh"], a["lse"], 0, 4, 1, a["ex"], a["ws"], a["wsb"], None)
+
+    assert call(plan=None) == 1
+    assert call(batch=0) == 11
+    assert call(meta=None) == 1
+    assert call(out=None) == 1
+    assert call(lse=None) == 1
+    assert call(ws=None) == 7
+    assert call(wsb=wsb - 4) == 7
+    assert call(batch=2) == 7            # the workspace holds one batch element
+    assert call(out=fake + 2) == 10
+    assert call(st=512 + 4) == 10
+    ex = ffa.AttnExtras()
+    ex.softcap = -1.0
+    assert call(ex=ctypes.byref(ex)) == 11
+    # a plan that splits nothing: nothing to merge, nothing enqueued
+    pn = ffa.Plan([[0, 64]], [[0, 64]], [1], 64, 64, 2, 2, 128, num_cus=NCU)
+    assert pn.info["num_combine"] == 0
+    assert call(plan=pn, ws=None, wsb=0) == 0
+
+
+def test_largest_key_axis_keeps_its_causal_edge():
+    # With a key axis of 2^30 - 2 tokens a causal bound ke - qe + 1 stays below the
+    # "no bound" sentinel, so the run keeps its masked trailing tile; one more token is
+    # rejected (a bound could then equal the sentinel and read as "no bound").
+    nk = (1 << 30) - 2
+    p = ffa.Plan([[0, 2]], [[0, nk]], [1], 2, nk, 1, 1, 128, num_cus=NCU, split_tiles=-1)
+    meta = p.meta_host()
+    assert p.info["num_items"] == 1
+    run = meta[HDR + IREC * 1: HDR + IREC * 1 + REC]
+    k0, n_tiles, n_full, k_hi, edge_base = (int(x) for x in run[:5])
+    assert (k0, k_hi, edge_base) == (0, nk, nk - 2 + 1)
+    assert n_tiles == -(-nk // 64) and n_full == (nk - 1) // 64 < n_tiles
+    assert plan_status([[0, 2]], [[0, 2]], [1], 2, nk + 1, 1, 1, 128) == 2
+    assert plan_status([[0, 2]], [[0, 2]], [1], nk + 1, 2, 1, 1, 128) == 2
 
 
 def test_head_groups_of_a_kv_head_share_a_dispatch_lane():

@@ -30,6 +30,14 @@ MUTATIONS = {
     "invcausal_from_the_end": ("start = ks + (rows - qs) if", "start = ks + (qe - 1 - rows) if"),
     "bicausal_loses_start": ("start = ks + (rows - qs) if t in (INVCAUSAL, BICAUSAL)",
                              "start = ks + (rows - qs) if t in (INVCAUSAL,)"),
+    # the per-row interval of one slice (used by the visible-pair count)
+    "row_interval_causal_off_by_one": ("b = ke - (qe - 1 - i) if mask_type in (CAUSAL, BICAUSAL) else ke",
+                                       "b = ke - (qe - i) if mask_type in (CAUSAL, BICAUSAL) else ke"),
+    "row_interval_full_is_causal": ("b = ke - (qe - 1 - i) if mask_type in (CAUSAL, BICAUSAL) else ke",
+                                    "b = ke - (qe - 1 - i)"),
+    # the union of a row's intervals in the visible-pair count
+    "count_union_drops_overlap_merge": ("cur_b = max(cur_b, b)", "cur_b = b"),
+    "count_union_double_counts": ("if a > cur_b:", "if True:"),
 }
 
 PINS = [
@@ -48,6 +56,7 @@ PINS = [
     pins.test_square_inverse_causal_is_causal_on_reversed_sequences,
     pins.test_square_bicausal_sees_only_its_diagonal_key,
     pins.test_bicausal_band_splits_into_inverse_causal_and_causal,
+    pins.test_visible_pair_counts_closed_forms,
 ]
 
 
@@ -62,8 +71,8 @@ def load_mutant(old, new):
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_mutation(name, monkeypatch):
     mod = load_mutant(*MUTATIONS[name])
-    for attr in ("mask_rows", "dense_mask", "count_visible_pairs", "attend", "attend_dense",
-                 "merge_partials", "slice_row_interval", "row_intervals"):
+    for attr in ("mask_rows", "dense_mask", "count_visible_pairs", "attend", "merge_partials",
+                 "slice_row_interval"):
         monkeypatch.setattr(oracle, attr, getattr(mod, attr))
     failed = 0
     for pin in PINS:

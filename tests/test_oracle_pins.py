@@ -396,6 +396,17 @@ def test_visible_pair_count_matches_mask_sum():
         p = W.random_problem(500 + seed, 37, 29, 1, 1, 4)
         m = oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, 37, 29)
         assert oracle.count_visible_pairs(p.q_ranges, p.k_ranges, p.mask_types, 37, 29) == int(m.sum())
+    # overlapping slices (the oracle's mask is their union): two 10 x 10 FULL squares that
+    # share a 5 x 5 corner cover 175 pairs; a causal square under a FULL one covers the square
+    assert oracle.count_visible_pairs([[0, 10], [5, 15]], [[0, 10], [5, 15]], [0, 0], 15, 15) == 175
+    assert oracle.count_visible_pairs([[0, 8], [0, 8]], [[0, 8], [0, 8]], [1, 0], 8, 8) == 64
+    rng = np.random.default_rng(77)
+    for _ in range(20):
+        qr = np.sort(rng.integers(0, 30, size=(4, 2)), axis=1)
+        kr = np.sort(rng.integers(0, 25, size=(4, 2)), axis=1)
+        ty = rng.integers(0, 4, size=4)
+        m = oracle.dense_mask(qr, kr, ty, 30, 25)
+        assert oracle.count_visible_pairs(qr, kr, ty, 30, 25) == int(m.sum())
 
 
 def test_config_doc_lists():
