@@ -10,11 +10,14 @@ only unmasked FLOPs: 4 * D * Hq * (visible (q, k) pairs per head).  Timing uses
 HIP events recorded on the stream the kernels are launched on.
 
 Prints one JSON line.  `roofline` refers to the dominant kernel (ffa_fwd_main,
-bound by bf16 MFMA); `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the same workload; `backward` times ffa_bwd (dq, dk, dv from the
-forward's out and lse) on the same workload, outside the forward's step; `also`
-times the forward of further workloads (default: the heterogeneous-mask mix, the other
-configuration the >= 50% target names) the same way, outside the step.
+bound by bf16 MFMA at D >= 64, by the per-score VALU work below); `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload; `backward`
+times ffa_bwd (dq, dk, dv from the forward's out and lse) on the same workload,
+outside the forward's step; `also` times the forward of further workloads
+(default: the heterogeneous-mask mix, the other configuration the >= 50% target
+names, the rectangular causal GQA case and the long-context case) the same way,
+outside the step; `combine` times the split-K combine kernel alone on the
+long-context case planned with forced chunks of 512 key tiles, against HBM.
 """
 from __future__ import annotations
 
@@ -24,6 +27,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -45,9 +50,12 @@ def parse():
     ap.add_argument("--split-tiles", type=int, default=0, help="planner split control (0 auto, <0 never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
-    ap.add_argument("--also", default="hetero_mask_mix",
+    ap.add_argument("--also", default="hetero_mask_mix,rect_causal_gqa,long_context",
                     help="comma-separated workloads whose forward is also timed, reported under `also` "
                          "(the bench line's value stays the --workload one); '' for none")
+    ap.add_argument("--combine", default="long_context:512",
+                    help="workload:split_tiles of the split-K combine leg (forced split, the combine kernel "
+                         "timed alone over the partials); '' for none")
     ap.add_argument("--softcap", type=float, default=0.0, help="soft-capping of the scores (0: off)")
     ap.add_argument("--total", action="store_true", help="also time the total-attention pass")
     ap.add_argument("--fp16", action="store_true", help="float16 inputs and outputs instead of bfloat16")
@@ -61,6 +69,56 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock.json")
+HBM_PEAK_TBS = 8.0  # MI355X HBM3E
+
+
+def alu_peak_tflops(head_dim: int) -> float:
+    """Peak of the metric's FLOP count when the per-score VALU work bounds the kernel.
+
+    Per wave64 instruction group of 64 scores the softmax needs about 18 VALU issue
+    cycles on a SIMD (v_exp_f32 8, the exponent-argument FMA 4, the row-sum add 4, half
+    a bf16 pack 2; measured with probe kernels), so a SIMD turns at most 64 / 18 scores
+    into probabilities per cycle: 1024 SIMDs (256 CUs x 4) x 2.4 GHz x 64 / 18 scores/s,
+    each worth 4 * D FLOPs of the metric.  Below D = 64 this is lower than the bf16 MFMA
+    peak (the MFMA work per score shrinks with D, the softmax work does not)."""
+    return 1024 * 2.4e9 * (64.0 / 18.0) * 4.0 * head_dim / 1e12
+
+
+def roofline_bound(head_dim: int):
+    """(bound, peak TFLOP/s) of the forward main kernel at this head dim."""
+    alu = alu_peak_tflops(head_dim)
+    return ("alu", round(alu, 1)) if alu < PEAK_BF16_TFLOPS else ("mfma", PEAK_BF16_TFLOPS)
+
+
+def measured_clock(workload: str):
+    """Shader clock under the main kernel, derived from a GRBM_GUI_ACTIVE counter pass
+    (profiles/clock.json), or None when missing or taken on another kernel source."""
+    try:
+        with open(CLOCK_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    w = c.get("workloads", {}).get(workload)
+    return None if w is None else {"mhz": w.get("mhz"), "source": "GRBM_GUI_ACTIVE / 8 XCDs / kernel duration "
+                                                              "(rocprofv3 counter pass, profiles/clock.json)"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 KERNEL_SOURCES = [os.path.join(ROOT, "flexible_mask_flash_amd", "csrc", f)
                   for f in ("ffa_fwd.hip", "ffa_device.h", "ffa_internal.h", "ffa_plan.cpp")]
 
@@ -146,6 +204,7 @@ def cpu_baseline(p, q, k, v, budget_s: float):
         "value": flops / t_used / 1e12,
         "unit": "TFLOPS",
         "cores": int(cores),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{done_rows} of {p.total_q} query rows ({done_rows // 256} seeded random 256-row blocks), "
                   f"all heads, fp64 numpy BLAS; {t_used:.1f} s",
@@ -163,7 +222,6 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import flexible_mask_flash_amd as ffa
@@ -238,6 +296,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": warm,
+        "warmup_requested": args.warmup,
+        "warmup_note": f"untimed warm-up runs until both {args.warmup} steps and "
+                       f"{args.min_warmup_seconds} s have passed (the clock ramps under sustained load)",
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -263,14 +324,15 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", ""), "hip": getattr(torch.version, "hip", None)},
         "roofline": {
-            "bound": "mfma",
+            "bound": roofline_bound(p.head_dim)[0],
             "achieved": round(tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": roofline_bound(p.head_dim)[1],
             "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(tflops / roofline_bound(p.head_dim)[1], 4),
             "traffic": measured_traffic(p.name),
             "kernel": "ffa_fwd_main",
             "algorithmic_flops_per_launch": flops,
+            "clock": measured_clock(p.name),
         },
     }
     if not args.no_backward:
@@ -278,6 +340,9 @@ def main():
     also = [w for w in args.also.split(",") if w and w != p.name]
     if also and not args.backward_only and args.sinks == 0:  # (sink logits are drawn for the main workload only)
         res["also"] = [also_leg(args, w) for w in also]
+    if args.combine and not args.backward_only and args.sinks == 0:
+        wl, _, st = args.combine.partition(":")
+        res["combine"] = combine_leg(args, wl, int(st or 512))
     if args.total:
         res["total_attention"] = total_leg(args, p, qd, kd, lse, scale, sink)
     if not args.no_cpu_baseline:
@@ -297,9 +362,8 @@ def also_leg(args, name: str):
         raise SystemExit(f"--also: unknown workload {name!r}")
     dev = torch.device("cuda", 0)
     p = W.workload(name)
-    q, k, v = W.make_qkv(p, dtype=torch.float16 if args.fp16 else None)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    del q, k, v
+    # drawn on the device (same distribution as the CPU draws; long-context inputs are 2.5 GB)
+    qd, kd, vd = W.make_qkv_device(p, dev, dtype=torch.float16 if args.fp16 else None)
     plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
                     p.head_dim, split_tiles=args.split_tiles)
     plan.device_meta(dev)
@@ -332,11 +396,81 @@ def also_leg(args, name: str):
     ms = e0.elapsed_time(e1) / args.steps
     flops = 4.0 * p.head_dim * p.heads_q * plan.info["visible_pairs"]
     tflops = flops / (ms * 1e-3) / 1e12
+    bound, peak = roofline_bound(p.head_dim)
     return {"workload": p.name, "value": round(tflops, 2), "unit": "TFLOPS", "ms_per_step": round(ms, 4),
             "steps": args.steps, "warmup": warm, "flops_per_step": flops,
             "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(p.name),
+            "bound": bound, "peak": peak, "frac": round(tflops / peak, 4), "traffic": measured_traffic(p.name),
+            "clock": measured_clock(p.name), "data": "synthetic, drawn on the device",
             "num_items": int(plan.info["num_items"]), "num_split_items": int(plan.info["num_split_items"])}
+
+
+def combine_leg(args, name: str, split_tiles: int):
+    """The split-K combine on its own: `name` planned with forced chunks of `split_tiles` key
+    tiles, one ffa_fwd call to leave the partials in the workspace, then ffa_combine timed
+    with HIP events.  Algorithmic bytes per launch: every split (row, head) reads its
+    n_chunks partials (4 D + 4 bytes each) and writes out and lse (2 D + 4 bytes)."""
+    import torch
+
+    import flexible_mask_flash_amd as ffa
+    import workloads as W
+
+    dev = torch.device("cuda", 0)
+    p = W.workload(name)
+    qd, kd, vd = W.make_qkv_device(p, dev)
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k, p.heads_q, p.heads_kv,
+                    p.head_dim, split_tiles=split_tiles)
+    plan.device_meta(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((p.total_q, p.heads_q), dtype=torch.float32, device=dev)
+    strides = {"q": (0, qd.stride(0), qd.stride(1)), "k": (0, kd.stride(0), kd.stride(1)),
+               "v": (0, vd.stride(0), vd.stride(1)), "out": (0, out.stride(0), out.stride(1)),
+               "lse": (0, lse.stride(0), lse.stride(1))}
+    scale = 1.0 / math.sqrt(p.head_dim)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the forced-split forward (main kernel + combine), a few steps
+    ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale)
+    torch.cuda.synchronize()
+    n_fwd = 3
+    e0.record(stream)
+    for _ in range(n_fwd):
+        ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / n_fwd
+    # the combine alone over the partials the last forward left
+    comb = lambda: ffa.run_combine(plan, out, lse, strides, 1)
+    warm = 0
+    t_w = time.perf_counter()
+    while warm < max(3, args.warmup) or time.perf_counter() - t_w < args.min_warmup_seconds:
+        comb()
+        warm += 1
+        if warm % 5 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        comb()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    meta = plan.meta_host()
+    ni, nr, nc = plan.info["num_items"], plan.info["num_runs"], plan.info["num_combine"]
+    recs = meta[16 + 16 * ni + 8 * nr:16 + 16 * ni + 8 * nr + 8 * nc].reshape(-1, 8).astype(np.int64)
+    pairs = recs[:, 1] * plan.info["heads_per_item"]          # (row, head) pairs per entry
+    d = p.head_dim
+    nbytes = int((pairs * (recs[:, 3] * (4 * d + 4) + 2 * d + 4)).sum())
+    tbs = nbytes / (ms * 1e-3) / 1e12
+    flops = 4.0 * d * p.heads_q * plan.info["visible_pairs"]
+    return {"workload": p.name, "split_tiles": split_tiles, "kernel": "ffa_combine", "bound": "hbm",
+            "value": round(tbs, 3), "unit": "TB/s", "achieved": round(tbs, 3), "peak": HBM_PEAK_TBS,
+            "frac": round(tbs / HBM_PEAK_TBS, 4), "ms_per_launch": round(ms, 4), "steps": args.steps,
+            "algorithmic_bytes_per_launch": nbytes, "num_combine": int(nc),
+            "num_split_items": int(plan.info["num_split_items"]),
+            "split_forward": {"ms_per_step": round(fwd_ms, 3), "value": round(flops / (fwd_ms * 1e-3) / 1e12, 2),
+                              "unit": "TFLOPS", "steps": n_fwd},
+            "data": "synthetic, drawn on the device"}
 
 
 def total_leg(args, p, qd, kd, lse, scale, sink=None):

@@ -213,6 +213,25 @@ def make_qkv(p: Problem, seed: Optional[int] = None, q_zero: bool = False, dtype
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
+def make_qkv_device(p: Problem, device, seed: Optional[int] = None, q_zero: bool = False, dtype=None):
+    """Draw q, k, v for problem `p` directly on `device` (a seeded device generator; for
+    full-size runs whose inputs are too large to draw on the CPU quickly).  The draws are
+    N(0,1) in the order q, k, v, rounded to bfloat16 (or `dtype`); they are not the same
+    numbers as make_qkv's CPU draws."""
+    import torch
+
+    dtype = torch.bfloat16 if dtype is None else dtype
+    g = torch.Generator(device=device).manual_seed(p.seed if seed is None else seed)
+    shape_q = (p.total_q, p.heads_q, p.head_dim)
+    if q_zero:
+        q = torch.zeros(shape_q, dtype=dtype, device=device)
+    else:
+        q = torch.randn(shape_q, generator=g, dtype=torch.float32, device=device).to(dtype)
+    k = torch.randn((p.total_k, p.heads_kv, p.head_dim), generator=g, dtype=torch.float32, device=device).to(dtype)
+    v = torch.randn((p.total_k, p.heads_kv, p.head_dim), generator=g, dtype=torch.float32, device=device).to(dtype)
+    return q, k, v
+
+
 def sliding_window_problem(T, w, docs, hq, hkv, d, seed):
     """Per-document sliding window of w keys: row i sees keys [max(s, i - w + 1), i + 1).
     The first w - 1 rows of a document are a causal slice; the rest a bi-causal band."""
