@@ -130,6 +130,13 @@ _SIGNATURES = [
                        _vp, _i64, _i64, _i64,
                        _vp, _i64, _i64, _i64,
                        _f32, ctypes.POINTER(AttnExtras), _vp, _sz, _vp]),
+    ("ffa_fwd_noalloc", _i32, [_vp, _vp, _i32,
+                               _vp, _i64, _i64, _i64,
+                               _vp, _i64, _i64, _i64,
+                               _vp, _i64, _i64, _i64,
+                               _vp, _i64, _i64, _i64,
+                               _vp, _i64, _i64, _i64,
+                               _f32, ctypes.POINTER(AttnExtras), _vp]),
     ("ffa_combine", _i32, [_vp, _vp, _i32,
                            _vp, _i64, _i64, _i64,
                            _vp, _i64, _i64, _i64,
@@ -405,6 +412,23 @@ def run_fwd(plan: Plan, q, k, v, out, lse, strides, batch: int, softmax_scale: f
                      float(softmax_scale), ctypes.byref(extras) if extras is not None else None,
                      ws.data_ptr() if ws is not None else None, ws_bytes, s.cuda_stream)
     _check(st, "ffa_fwd")
+
+
+def run_fwd_noalloc(plan: Plan, q, k, v, out, lse, strides, batch: int, softmax_scale: float, extras=None):
+    """Call ffa_fwd_noalloc: ffa_fwd without a workspace argument (split partials go to
+    the library's own device scratch; nothing is allocated by the call).  Raises
+    FFAError (status 7) when the plan's partials exceed that scratch."""
+    import torch
+
+    dev = q.device
+    s = torch.cuda.current_stream(dev)
+    meta = plan.device_meta(dev, s)
+    qs, ks, vs, os_, ls = strides["q"], strides["k"], strides["v"], strides["out"], strides["lse"]
+    st = load_library().ffa_fwd_noalloc(plan.handle, meta.data_ptr(), int(batch), q.data_ptr(), *qs,
+                                        k.data_ptr(), *ks, v.data_ptr(), *vs, out.data_ptr(), *os_,
+                                        lse.data_ptr(), *ls, float(softmax_scale),
+                                        ctypes.byref(extras) if extras is not None else None, s.cuda_stream)
+    _check(st, "ffa_fwd_noalloc")
 
 
 def run_combine(plan: Plan, out, lse, strides, batch: int, extras=None):

@@ -33,11 +33,19 @@
 #include <cstdlib>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <type_traits>
 
 #include "ffa_device.h"
+
+// Library-owned split-K workspace of ffa_fwd_noalloc (for callers that cannot
+// allocate device memory): FFA_NOALLOC_SCRATCH_BYTES of device memory per GPU,
+// held from the library's load until the process ends.  Host code never passes
+// `scratch` itself to a kernel or a copy (its host-side name is not a device
+// address); it uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[FFA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -987,6 +995,52 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch ffa_fwd_main");
   return launch_combine(p, meta, batch, out, o_sb, o_st, o_sh, lse, l_sb, l_st, l_sh, ex, fa.ws_o, s);
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept for the rest of the process.
+static ffa_status scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return ffa::set_error(FFA_ERR_ARG, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return ffa::set_error(FFA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return FFA_OK;
+}
+
+ffa_status ffa_fwd_noalloc(ffa_plan_t plan, const void* d_meta, int32_t batch, const void* q, int64_t q_sb,
+                           int64_t q_st, int64_t q_sh, const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh,
+                           const void* v, int64_t v_sb, int64_t v_st, int64_t v_sh, void* out, int64_t o_sb,
+                           int64_t o_st, int64_t o_sh, float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                           float softmax_scale, const ffa_attn_extras* extras, void* stream) {
+  ffa::clear_error();
+  if (!plan) return ffa::set_error(FFA_ERR_NULL, "plan is NULL");
+  if (batch < 1) return ffa::set_error(FFA_ERR_ARG, "batch must be >= 1");
+  const int64_t need = (int64_t)batch * plan->plan.workspace_bytes();
+  if (need > (int64_t)FFA_NOALLOC_SCRATCH_BYTES)
+    return ffa::set_error(FFA_ERR_WORKSPACE,
+                          "the plan's split-K partials need " + std::to_string(need) +
+                              " bytes, beyond the library scratch of " + std::to_string(FFA_NOALLOC_SCRATCH_BYTES) +
+                              " bytes (use ffa_fwd with a caller workspace, or plan with fewer splits)");
+  void* ws = nullptr;
+  if (need > 0) {
+    const ffa_status st = scratch_address(&ws);
+    if (st != FFA_OK) return st;
+  }
+  return ffa_fwd(plan, d_meta, batch, q, q_sb, q_st, q_sh, k, k_sb, k_st, k_sh, v, v_sb, v_st, v_sh, out, o_sb, o_st,
+                 o_sh, lse, l_sb, l_st, l_sh, softmax_scale, extras, ws, need > 0 ? (size_t)FFA_NOALLOC_SCRATCH_BYTES : 0,
+                 stream);
 }
 
 ffa_status ffa_combine(ffa_plan_t plan, const void* d_meta, int32_t batch, void* out, int64_t o_sb, int64_t o_st,

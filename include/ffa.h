@@ -224,6 +224,31 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch,
                    void* d_workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ffa_fwd with
+ * the same arguments and results, except that a plan's split-K partials go to
+ * a library-owned device array of FFA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU
+ * instead of a caller workspace.  Nothing is allocated: the array is part of
+ * the library's device image, held from its load until the process ends, and
+ * its address is looked up once per device (hipGetSymbolAddress) on the first
+ * call that needs it, with the stream's device current.  A plan whose
+ * batch * info.workspace_bytes exceeds the array is rejected with
+ * FFA_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU shares
+ * that GPU's array and the array keeps the last call's contents (every slot a
+ * call reads is written by the same call first, so nothing needs clearing);
+ * calls that overlap in time on one GPU (other streams, other threads) race on
+ * it and must be serialised by the caller.
+ */
+#define FFA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ffa_status ffa_fwd_noalloc(ffa_plan_t plan, const void* d_meta, int32_t batch,
+                           const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                           const void* k, int64_t k_sb, int64_t k_st, int64_t k_sh,
+                           const void* v, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                           void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                           float* lse, int64_t l_sb, int64_t l_st, int64_t l_sh,
+                           float softmax_scale, const ffa_attn_extras* extras, void* stream);
+
+/*
  * The merge step of a split plan on its own (FlagAttention user guide,
  * "Split-KV and paged attention": a second kernel merges the partial results
  * with a global logsumexp): for every split (row, head),
