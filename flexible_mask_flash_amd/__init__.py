@@ -22,6 +22,9 @@ API (names follow the pages):
       FlagAttention's dense contract on [B,H,M,D] tensors (GQA, bottom-right
       causal), differentiable; returns out, or the 5-tuple (out, lse [B,Hq,M],
       total [B,Hq,N], None, None) when an auxiliary flag is set.
+  flash_attention_split_kv(q, k, v, causal=False, sm_scale=None, num_splits=0, ...)
+      FlagAttention's forward-only long-KV entry: partial (out, lse) per key
+      chunk, merged by a second kernel with a global logsumexp.
   Plan(...)  a reusable host plan (ffa_plan) with its device metadata.
 
 Streams.  A plan may be used on several streams: its metadata is uploaded once
@@ -48,6 +51,7 @@ __all__ = [
     "flex_flash_attn_func",
     "flex_total_attention",
     "flash_attention",
+    "flash_attention_split_kv",
     "load_library",
     "library_path",
     "FULL",
@@ -325,11 +329,13 @@ _plan_cache: "OrderedDict[tuple, Plan]" = OrderedDict()
 _PLAN_CACHE_MAX = 16
 
 
-def _cached_plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles, backward: bool = False) -> Plan:
-    key = (qr.tobytes(), kr.tobytes(), ty.tobytes(), tq, tk, hq, hkv, d, split_tiles, bool(backward))
+def _cached_plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles, backward: bool = False,
+                 max_splits: int = 0) -> Plan:
+    key = (qr.tobytes(), kr.tobytes(), ty.tobytes(), tq, tk, hq, hkv, d, split_tiles, bool(backward), max_splits)
     p = _plan_cache.get(key)
     if p is None:
-        p = Plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles=split_tiles, backward=backward)
+        p = Plan(qr, kr, ty, tq, tk, hq, hkv, d, split_tiles=split_tiles, max_splits=max_splits,
+                 backward=backward)
         _plan_cache[key] = p
         if len(_plan_cache) > _PLAN_CACHE_MAX:
             _plan_cache.popitem(last=False)
@@ -741,3 +747,52 @@ def flash_attention(q, k, v, causal: bool = False, sm_scale: Optional[float] = N
                    "total": _bhmd_strides(total)}
         run_total(plan, q.detach(), k.detach(), lse, total, strides, b, scale, make_extras(dtype=q.dtype))
     return out, (lse if return_log_normalizer else None), total, None, None
+
+
+KEY_TILE = 64  # keys per key tile of the forward kernel (the unit of split_tiles)
+
+
+def flash_attention_split_kv(q, k, v, causal: bool = False, sm_scale: Optional[float] = None,
+                             num_splits: int = 0, return_log_normalizer: bool = False):
+    """Forward-only attention over a long key axis, on [B, H, M, D] tensors.
+
+    q [B,Hq,M,D], k/v [B,Hkv,N,D] bf16 or fp16; Hq % Hkv == 0; D in {16, 32, 64,
+    128}; causal is bottom-right aligned.  The key axis of each query tile is cut
+    into chunks; every chunk writes a float32 partial output and log-normalizer,
+    and a second kernel (ffa_combine) merges them with a global logsumexp
+    (FlagAttention user guide, "Split-KV and paged attention").  num_splits: 0
+    lets the planner choose (it splits only when the work cannot fill the
+    device), 1 never splits, n > 1 cuts the longest key range into n chunks of
+    ceil(N / 64 / n) key tiles of 64 keys (shorter causal ranges into fewer).
+    Returns out [B,Hq,M,D], or (out, lse [B,Hq,M]) with return_log_normalizer.
+    Nothing here is differentiable.
+    """
+    import torch
+
+    _require_bf16_cuda("q", q, 4)
+    _require_bf16_cuda("k", k, 4, q.dtype)
+    _require_bf16_cuda("v", v, 4, q.dtype)
+    b, hq, m, d = q.shape
+    bk, hkv, n, dk = k.shape
+    if v.shape != k.shape or bk != b or dk != d:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    num_splits = int(num_splits)
+    if num_splits < 0:
+        raise ValueError("num_splits must be >= 0")
+    if num_splits == 0:
+        split_tiles, max_splits = 0, 0
+    elif num_splits == 1:
+        split_tiles, max_splits = -1, 0
+    else:
+        n_tiles = max(1, -(-n // KEY_TILE))
+        split_tiles, max_splits = max(1, -(-n_tiles // num_splits)), num_splits
+    ty = CAUSAL if causal else FULL
+    plan = _cached_plan(np.array([[0, m]], np.int32), np.array([[0, n]], np.int32), np.array([ty], np.int32),
+                        m, n, hq, hkv, d, split_tiles, max_splits=max_splits)
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    with torch.no_grad():
+        out = torch.empty((b, hq, m, d), dtype=q.dtype, device=q.device)
+        lse = torch.empty((b, hq, m), dtype=torch.float32, device=q.device)
+        strides = {nm: _bhmd_strides(x) for nm, x in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))}
+        run_fwd(plan, q.detach(), k.detach(), v.detach(), out, lse, strides, b, scale, make_extras(dtype=q.dtype))
+    return (out, lse) if return_log_normalizer else out

@@ -390,6 +390,34 @@ def test_flag_attention_layout(gpu_lib, causal):
     assert torch.equal(o2, out)
 
 
+@pytest.mark.parametrize("d,causal,num_splits", [(128, True, 4), (128, False, 7), (64, True, 3),
+                                                  (32, False, 5), (16, True, 2), (128, True, 1), (64, False, 0)])
+def test_flash_attention_split_kv(gpu_lib, d, causal, num_splits):
+    # FlagAttention's explicit long-KV forward: a long key axis, split into chunks
+    # whose partial (out, lse) the combine kernel merges (num_splits 1: never split)
+    B, Hq, Hkv, M, N = 2, 8, 2, 100, 4100
+    g = torch.Generator().manual_seed(31 + d + num_splits)
+    q = torch.randn(B, Hq, M, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    dev = torch.device("cuda", 0)
+    out, lse = gpu_lib.flash_attention_split_kv(q.to(dev), k.to(dev), v.to(dev), causal=causal,
+                                                num_splits=num_splits, return_log_normalizer=True)
+    torch.cuda.synchronize()
+    plan = gpu_lib._plan_cache[next(reversed(gpu_lib._plan_cache))]
+    if num_splits > 1:
+        assert plan.info["num_split_items"] > 0 and plan.info["num_combine"] > 0
+    if num_splits == 1:
+        assert plan.info["num_split_items"] == 0
+    assert out.shape == (B, Hq, M, d) and lse.shape == (B, Hq, M)
+    t = W.CAUSAL if causal else W.FULL
+    for b in range(B):
+        ro, rl = oracle.attend(q[b].permute(1, 0, 2), k[b].permute(1, 0, 2), v[b].permute(1, 0, 2),
+                               [[0, M]], [[0, N]], [t])
+        compare(out[b].permute(1, 0, 2), lse[b].permute(1, 0), ro, rl,
+                what=f"split_kv D={d} causal={causal} splits={num_splits} b={b}")
+
+
 def test_product_path_has_no_fallback(gpu_lib):
     # the binding routes through libffa.so: its handle is loaded and no oracle module is imported by it
     import flexible_mask_flash_amd as ffa
