@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="only write profiles/traffic.json and profiles/clock.json from the rocprofv3 "
+                         "counter runs under DIR (no GPU needed)")
     return ap.parse_args()
 
 
@@ -147,6 +150,85 @@ def measured_traffic(workload: str):
     return None if w is None else w.get("hbm_bytes_per_launch")
 
 
+TRAFFIC_WORKLOADS = ("packed_docs", "hetero_mask_mix", "rect_causal_gqa", "long_context")
+CLOCK_WORKLOADS = ("packed_docs", "hetero_mask_mix", "long_context")
+CLOCK_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+                  "SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_INSTS_SALU GRBM_GUI_ACTIVE")
+
+
+def algorithmic_bytes(p) -> int:
+    """Bytes the forward must move at least: q, k, v read and out written (bf16), lse written (fp32)."""
+    d = p.head_dim
+    return 2 * d * (2 * p.total_q * p.heads_q + 2 * p.total_k * p.heads_kv) + 4 * p.total_q * p.heads_q
+
+
+def summarize_profiles(d: str):
+    """Write profiles/traffic.json and profiles/clock.json from rocprofv3 counter runs in d:
+    d/FETCH_SIZE_<w>, d/WRITE_SIZE_<w> (one counter per run, this file's --workload <w>),
+    d/FETCH_SIZE_copy, d/WRITE_SIZE_copy (--copy-calibration) and d/sq_<w> (the counters
+    of CLOCK_COUNTERS in one run), each holding rocprofv3's run_counter_collection.csv.
+    The last dispatch of the kernel in each run is used; both files carry the hash of
+    the kernel sources they were measured on, and bench lines use them only while the
+    sources are unchanged."""
+    import csv
+
+    def last(tag, counter, kernel):
+        with open(os.path.join(d, tag, "run_counter_collection.csv")) as f:
+            r = [x for x in csv.DictReader(f) if kernel in x["Kernel_Name"] and x["Counter_Name"] == counter]
+        if not r:
+            raise SystemExit(f"{tag}: no {counter} for {kernel}")
+        return r[-1]
+
+    import workloads as W
+
+    kib_per_gib = (1 << 30) / 1024
+    fcopy = float(last("FETCH_SIZE_copy", "FETCH_SIZE", "copyBuffer")["Counter_Value"])
+    wcopy = float(last("WRITE_SIZE_copy", "WRITE_SIZE", "copyBuffer")["Counter_Value"])
+    fs, ws = round(kib_per_gib / fcopy, 1), round(kib_per_gib / wcopy, 1)
+    tr = {"kernel": "ffa_fwd_main", "kernel_source_hash": kernel_source_hash(),
+          "method": ("rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in separate runs (KiB per dispatch, last "
+                     f"dispatch); scaled by a 1 GiB device copy (__amd_rocclr_copyBuffer): FETCH_SIZE read {fcopy} "
+                     f"KiB -> x{fs}, WRITE_SIZE read {wcopy} KiB -> x{ws}"),
+          "fetch_scale": fs, "write_scale": ws, "workloads": {}}
+    for w in TRAFFIC_WORKLOADS:
+        f = float(last(f"FETCH_SIZE_{w}", "FETCH_SIZE", "ffa_fwd_main")["Counter_Value"])
+        wr = float(last(f"WRITE_SIZE_{w}", "WRITE_SIZE", "ffa_fwd_main")["Counter_Value"])
+        p = W.workload(w)
+        ab = algorithmic_bytes(p)
+        outlse = 2 * p.head_dim * p.total_q * p.heads_q + 4 * p.total_q * p.heads_q
+        tr["workloads"][w] = {"fetch_kib": f, "write_kib": wr,
+                              "hbm_bytes_per_launch": int(round((f * fs + wr * ws) * 1024)),
+                              "algorithmic_bytes": ab, "write_bytes": int(wr * ws * 1024), "out_lse_bytes": outlse}
+        print(f"{w:16s} fetch {f * fs / 1024:9.1f} MiB write {wr * ws / 1024:9.1f} MiB  hbm/algo "
+              f"{(f * fs + wr * ws) * 1024 / ab:5.2f}  write/(out+lse) {wr * ws * 1024 / outlse:5.3f}")
+    ck = {"kernel": "ffa_fwd_main", "kernel_source_hash": kernel_source_hash(),
+          "method": (f"rocprofv3 --pmc {CLOCK_COUNTERS} (one run per workload, last dispatch); "
+                     "clock = GRBM_GUI_ACTIVE / 8 XCDs / (End - Start timestamp)"), "workloads": {}}
+    for w in CLOCK_WORKLOADS:
+        c = {}
+        with open(os.path.join(d, f"sq_{w}", "run_counter_collection.csv")) as f:
+            for x in csv.DictReader(f):
+                if "ffa_fwd_main" in x["Kernel_Name"]:
+                    c[x["Counter_Name"]] = (float(x["Counter_Value"]), int(x["Start_Timestamp"]),
+                                            int(x["End_Timestamp"]))
+        dur = (c["GRBM_GUI_ACTIVE"][2] - c["GRBM_GUI_ACTIVE"][1]) * 1e-9
+        grbm = c["GRBM_GUI_ACTIVE"][0]
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"][0]
+        valu, mfma, lds, salu = (c[k][0] for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"))
+        ck["workloads"][w] = {"mhz": round(grbm / 8 / dur / 1e6, 1), "duration_us": round(dur * 1e6, 1),
+                              "grbm_gui_active": grbm, "sq_busy_cycles": c["SQ_BUSY_CYCLES"][0],
+                              "mfma_busy_cycles": busy,
+                              # the SIMD cycles available: 1024 SIMDs x GRBM cycles per XCD
+                              "mfma_busy_frac_of_simd_cycles": round(busy / (1024 * grbm / 8), 4),
+                              "valu_per_mfma": round(valu / mfma, 3), "lds_per_mfma": round(lds / mfma, 3),
+                              "salu_per_mfma": round(salu / mfma, 3)}
+        print(w, ck["workloads"][w])
+    for path, obj in ((TRAFFIC_FILE, tr), (CLOCK_FILE, ck)):
+        with open(path, "w") as f:
+            json.dump(obj, f, indent=1)
+            f.write("\n")
+
+
 def copy_calibration():
     """A plain 1 GiB device copy: the reference kernel for scaling FETCH_SIZE / WRITE_SIZE
     (profile this command), and the HBM rate a streaming kernel reaches on this part
@@ -216,6 +298,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
