@@ -278,6 +278,7 @@ EXTRA_WORKLOADS = {
     # sliding windows of 1024 keys over the packed documents (bi-causal bands)
     "sliding_window": lambda: _named(sliding_window_problem(16384, 1024, [0] + list(np.cumsum(config(3).docs)),
                                                             32, 8, 128, 3), "sliding_window"),
+    "packed_docs_d64": lambda: _with_head_dim(config(3), 64, "packed_docs_d64"),
     "packed_docs_d32": lambda: _with_head_dim(config(3), 32, "packed_docs_d32"),
     "packed_docs_d16": lambda: _with_head_dim(config(3), 16, "packed_docs_d16"),
 }
