@@ -175,6 +175,11 @@ __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
 // 16-lane group): the XOR spreads both patterns over all bank groups, and it is
 // the same for rows r and r + 16, so tiles can be addressed with compile-time
 // row offsets in steps of 16 (the rows r + 8 get their own address).
+template <int OFF>
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, f32x4_t v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+
 template <int D>
 __device__ __forceinline__ int swz_b(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
@@ -182,18 +187,30 @@ __device__ __forceinline__ int swz_b(int r) {
                    : ((r >> 2) & 3);  // 64-byte rows: four rows per bank window already
 }
 
-// Occupancy: two waves per SIMD wherever the kernel fits 256 registers, so that one
-// wave's VALU work hides behind the other's MFMAs: the query-major kernel, total
-// attention (no accumulators) and the key-major kernel up to D = 64 (~240
-// registers).  At D = 128 the key-major kernel holds two fp32 accumulators of 64
-// registers each and the k, v fragments (~330 registers): one wave per SIMD.
+// Occupancy: two waves per SIMD, so that one wave's VALU work hides behind the
+// other's MFMAs.  The query-major kernel, total attention (no accumulators) and
+// the key-major kernel up to D = 64 fit 256 registers with one wave per 32 rows.
+// At D = 128 one key-major wave would hold both fp32 accumulators (dK and dV, 64
+// registers each) and both fragments (k and v, 32 each): ~330 registers, one wave
+// per SIMD.  There the 32 keys of a block are shared by a pair of waves instead
+// (PAIR), eight waves for the item's 128 keys: role 0 holds k and dV and computes
+// X1 = K Q^T, P and dV += P^T dO; role 1 holds v and dK and computes X2 = V dO^T
+// - Dd, takes P from its partner through LDS and computes dS and dK += dS^T Q.
+// Role 1 works one step behind role 0, so the hand-over needs no barrier of its
+// own and the two waves of a SIMD run their products and softmax work out of
+// phase (tiles triple-buffered; one barrier per step as elsewhere).  Roles
+// alternate over the wave index as (w ^ (w >> 2)) & 1, so that each SIMD holds
+// one wave of each role whether the hardware places waves w and w + 4 or waves
+// 2i and 2i + 1 on one SIMD; the key block is w >> 1.
 template <int D, bool KV, bool TOT>
-constexpr int kBwdWaves = (KV && !TOT && D > 64) ? 1 : 2;
+constexpr bool kPairBwd = KV && !TOT && D == 128;
+template <int D, bool KV, bool TOT>
+constexpr int kBwdWgWaves = kPairBwd<D, KV, TOT> ? 2 * ffa::kWaves : ffa::kWaves;
 
 // TOT (key-major only): FlagAttention's total attention, sum_i P[i,h,j] per key j and
 // query head h -- the same walk over the transposed worklist with only X1 and P.
 template <int D, bool KV, bool CAP, bool TOT, typename T>
-__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(kBwdWaves<D, KV, TOT>, kBwdWaves<D, KV, TOT>))) void ffa_bwd_main(BwdArgs a) {
+__global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_bwd_main(BwdArgs a) {
   using V8 = typename ElemT<T>::v8;
   using V4 = typename ElemT<T>::v4;
   using V2 = typename ElemT<T>::v2;
@@ -210,7 +227,8 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   constexpr int KSTEPS = D / 16;       // MFMA k-steps over the head dim
   constexpr int DBLK = DL / 32;        // 32-wide head-dim blocks of the accumulators
   constexpr int TILE = BN * ROWB;      // bytes of one streamed tile
-  constexpr int W = ffa::kWaves;
+  constexpr bool PAIR = kPairBwd<D, KV, TOT>;
+  constexpr int W = kBwdWgWaves<D, KV, TOT>;  // waves of the workgroup (they share the DMA)
   constexpr int NLD = TILE / (1024 * W);  // DMA instructions per thread per tile
   constexpr int RPL = 1024 * W / ROWB;    // rows between consecutive DMA instructions
   static_assert(NLD * 1024 * W == TILE, "DMA split");
@@ -219,9 +237,18 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   // the 64 streamed rows per buffer, 1 KiB each (one DMA instruction writes
   // 64 x 16 bytes; the first 256 count).  The L / Dd block has its own base
   // address so that every read offset fits the 16-bit immediate.
+  // PAIR (three buffers, the dS/dK wave one step behind): Q0 | Q1 | Q2, then
+  // dO0 | dO1 | dO2, then L / Dd of the three steps, then two P hand-over
+  // buffers of 4 KiB per 32-key block (lane l's 64 bytes as four 16-byte words
+  // 1 KiB apart, so each write or read instruction is one contiguous KiB).  Each
+  // role reads rows from one region and transposed tiles from the other, so its
+  // two address sets each have their own base and every offset fits 16 bits.
   constexpr int BUFB = 2 * TILE;
   constexpr int LDB = KV ? 2048 : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUFB + 2 * LDB];
+  constexpr int XB = PAIR ? 4 * 4096 : 0;
+  constexpr int QREG = 0, DREG = 3 * TILE, LDREG = 6 * TILE, XREG = 6 * TILE + 3 * LDB;
+  constexpr int SMEM = PAIR ? XREG + 2 * XB : 2 * BUFB + 2 * LDB;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int bid = blockIdx.x;
   const int item_idx = bid / a.batch;
@@ -235,7 +262,10 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int G = KV ? 1 : a.heads_per_item;
-  const int g = wave % G, rsub = wave / G;
+  // PAIR: role 0 (k, P, dV) or 1 (v, dS, dK) and the 32-key block of the wave
+  const int role = PAIR ? ((wave ^ (wave >> 2)) & 1) : 0;
+  const int kw = PAIR ? wave >> 1 : wave;
+  const int g = kw % G, rsub = kw / G;
   const int lrow = rsub * 32 + (lane & 31);
   const int row = r0 + lrow;
   const bool row_ok = lrow < nrows;
@@ -245,8 +275,9 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   // ---- the row's fragments (B operands, head-dim half hh): q and dO, or k and v
   V8 f1[KSTEPS], f2[KSTEPS];
   {
-    const __bf16* p1 = KV ? a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh + (int64_t)row * a.k_st
-                          : a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)row * a.q_st;
+    const __bf16* p1 = (PAIR && role) ? a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh + (int64_t)row * a.v_st
+                       : KV ? a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh + (int64_t)row * a.k_st
+                            : a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)row * a.q_st;
     const __bf16* p2 = KV ? a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh + (int64_t)row * a.v_st
                           : a.dout + (int64_t)b * a.d_sb + (int64_t)hq * a.d_sh + (int64_t)row * a.d_st;
     const bool load = row_ok && n_runs > 0;
@@ -272,13 +303,15 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     d_row = a.dw[idx];
   }
 
-  f32x16_t acc1[DBLK], acc2[KV ? DBLK : 1];
+  // acc1: dK (key-major), dQ (query-major), or the pair wave's own dV or dK
+  constexpr int NACC2 = (KV && !PAIR) ? DBLK : 1;
+  f32x16_t acc1[DBLK], acc2[NACC2];
 #pragma unroll
   for (int d = 0; d < DBLK; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc1[d][i] = 0.0f;
 #pragma unroll
-  for (int d = 0; d < (KV ? DBLK : 1); ++d)
+  for (int d = 0; d < NACC2; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc2[d][i] = 0.0f;
 
@@ -288,7 +321,8 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   uint32_t r_addr[KSTEPS];
   {
     const int r = lane & 31;
-    const uint32_t a0 = lds + r * ROWB + ((((D / 16) * hh) ^ swz_b<DL>(r)) << 4);
+    const uint32_t rbase = PAIR ? (role ? DREG : QREG) : 0;
+    const uint32_t a0 = lds + rbase + r * ROWB + ((((D / 16) * hh) ^ swz_b<DL>(r)) << 4);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) r_addr[s] = a0 ^ (s << 4);
   }
@@ -299,8 +333,9 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     const int grp = lane >> 4, jl = lane & 15;
     const int vr = 4 * hh + (jl >> 2);
     const int cl = 2 * (grp & 1) + ((jl & 3) >> 1);
-    const uint32_t lo = lds + vr * ROWB + ((cl ^ swz_b<DL>(vr)) << 4) + (jl & 1) * 8;
-    const uint32_t hi = lds + (vr + 8) * ROWB + ((cl ^ swz_b<DL>(vr + 8)) << 4) + (jl & 1) * 8;
+    const uint32_t tbase = PAIR ? (role ? QREG : DREG) : 0;
+    const uint32_t lo = lds + tbase + vr * ROWB + ((cl ^ swz_b<DL>(vr)) << 4) + (jl & 1) * 8;
+    const uint32_t hi = lds + tbase + (vr + 8) * ROWB + ((cl ^ swz_b<DL>(vr + 8)) << 4) + (jl & 1) * 8;
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
       t_lo[d] = lo ^ (d << 6);
@@ -308,7 +343,9 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     }
   }
   // key-major: L / Dd of rows 32 blk + 8 gq + 4 hh .. +3 are one 16-byte read
-  const uint32_t ld_addr = lds + 2 * BUFB + 16 * hh;
+  const uint32_t ld_addr = lds + (PAIR ? LDREG : 2 * BUFB) + 16 * hh;
+  // PAIR: the lane's 16-byte words of the P hand-over of its block (buffer 0)
+  const uint32_t x_addr = lds + XREG + kw * 4096 + lane * 16;
 
   // ---- DMA of a streamed tile: as in the forward, instruction i of wave w fills
   // LDS block (W i + w); lane l's 16 bytes are chunk (lin % CH) of row (lin / CH),
@@ -468,10 +505,12 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const int heads_per_step = KV ? a.kv_ratio : 1;
   const int steps = total_tiles * heads_per_step;
   auto load = [&](auto buf_tag, const Step& s) {
-    constexpr int OB = decltype(buf_tag)::value * BUFB;
-    dma(a_base(s.head), ast_b, OB, s.t.kstart(), total);
-    if constexpr (!TOT) dma(b_base(s.head), bst_b, OB + TILE, s.t.kstart(), total);
-    if constexpr (KV) dma_ld(2 * BUFB + decltype(buf_tag)::value * LDB, s.head, s.t.kstart());
+    constexpr int BI = decltype(buf_tag)::value;
+    constexpr int OA = PAIR ? QREG + BI * TILE : BI * BUFB;
+    constexpr int OB = PAIR ? DREG + BI * TILE : BI * BUFB + TILE;
+    dma(a_base(s.head), ast_b, OA, s.t.kstart(), total);
+    if constexpr (!TOT) dma(b_base(s.head), bst_b, OB, s.t.kstart(), total);
+    if constexpr (KV) dma_ld((PAIR ? LDREG : 2 * BUFB) + BI * LDB, s.head, s.t.kstart());
   };
   auto advance = [&](Step& s) {
     if (++s.jt >= total_tiles) {
@@ -490,34 +529,34 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   auto write_total = [&](int head, float v) {
     if (row_ok && hh == 0) a.tot[(int64_t)b * a.t_sb + (int64_t)row * a.t_st + (int64_t)head * a.t_sh] = v;
   };
+  // key-major: the tile's L (OL) or -Dd (OL + 1024) for the lane's 32 scores,
+  // element e of the pair (xa, xb) in word e % 4 of read e / 4
+  auto read_ld = [&](auto at_tag, f32x4_t(&w)[8]) {
+    static_for<8>([&](auto i_tag) {
+      constexpr int i = decltype(i_tag)::value;  // block i / 4, group i % 4
+      w[i] = lds_read_b128<decltype(at_tag)::value + ((i >> 2) * 32 + (i & 3) * 8) * 4>(ld_addr);
+    });
+  };
+  auto zero = [](f32x16_t& u, f32x16_t& w) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { u[i] = 0.0f; w[i] = 0.0f; }
+  };
+  auto from = [](f32x4_t(&r)[8]) {
+    return [&r](f32x16_t& u, f32x16_t& w) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fence(r[i]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        u[e] = r[e >> 2][e & 3];
+        w[e] = r[4 + (e >> 2)][e & 3];
+      }
+    };
+  };
   auto compute = [&](auto buf_tag, const Step& s) {
     constexpr int OA = decltype(buf_tag)::value * BUFB;
     constexpr int OB = OA + TILE;
     constexpr int OL = decltype(buf_tag)::value * LDB;  // relative to ld_addr
     f32x16_t xa, xb, ya, yb;
-    // key-major: the tile's L (OL) or -Dd (OL + 1024) for the lane's 32 scores,
-    // element e of the pair (xa, xb) in word e % 4 of read e / 4
-    auto read_ld = [&](auto at_tag, f32x4_t(&w)[8]) {
-      static_for<8>([&](auto i_tag) {
-        constexpr int i = decltype(i_tag)::value;  // block i / 4, group i % 4
-        w[i] = lds_read_b128<decltype(at_tag)::value + ((i >> 2) * 32 + (i & 3) * 8) * 4>(ld_addr);
-      });
-    };
-    auto zero = [](f32x16_t& u, f32x16_t& w) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { u[i] = 0.0f; w[i] = 0.0f; }
-    };
-    auto from = [](f32x4_t(&r)[8]) {
-      return [&r](f32x16_t& u, f32x16_t& w) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) fence(r[i]);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          u[e] = r[e >> 2][e & 3];
-          w[e] = r[4 + (e >> 2)][e & 3];
-        }
-      };
-    };
     // key-major uncapped, X1 starts at -lse / scale; soft-capped, the lane keeps
     // lse * log2 e of its 32 queries (lv) for the tanh path
     f32x4_t lv[8];
@@ -623,7 +662,145 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     }
   };
 
-  if (steps > 0) {
+  // PAIR, role 0, step s in buffer BI: X1 (from -L), the edge mask, P = exp2(X1 c2)
+  // -- soft-capped P = exp2(cap_log2 tanh - L) and the dS factor P (1 - tanh^2) --
+  // handed over in bf16 at xa (the step's parity buffer), then dV += P^T dO.
+  auto step_p = [&](auto buf_tag, const Step& s, uint32_t xa) {
+    constexpr int BI = decltype(buf_tag)::value;
+    f32x16_t pa, pb;
+    f32x4_t lv[8];
+    read_ld(std::integral_constant<int, BI * LDB>{}, lv);
+    if constexpr (!CAP) {
+      rowprod(std::integral_constant<int, BI * TILE>{}, f1, pa, pb, [](auto) {}, from(lv));
+    } else {
+      rowprod(std::integral_constant<int, BI * TILE>{}, f1, pa, pb, [](auto) {}, zero);
+      lds_wait<0>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fence(lv[i]);
+    }
+    if (s.t.edge()) mask(s.t, pa, pb);
+    V8 pf[4], kf[4];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float x = e < 16 ? pa[e] : pb[e - 16];
+      if constexpr (CAP) {
+        const float th = tanh_from_2ylog2e(x * a.cap_arg);
+        const float arg = x == -INFINITY ? -INFINITY : __builtin_fmaf(a.cap_log2, th, -lv[e >> 2][e & 3]);
+        const float pr = __builtin_amdgcn_exp2f(arg);
+        pf[e >> 3][e & 7] = (T)pr;
+        kf[e >> 3][e & 7] = (T)(pr * __builtin_fmaf(-th, th, 1.0f));
+      } else {
+        pf[e >> 3][e & 7] = (T)__builtin_amdgcn_exp2f(x * c2);
+      }
+    }
+    static_for<4>([&](auto t_tag) {
+      constexpr int t = decltype(t_tag)::value;
+      lds_write_b128<t * 1024>(xa, __builtin_bit_cast(f32x4_t, CAP ? kf[t] : pf[t]));
+    });
+    trprod(std::integral_constant<int, BI * TILE>{}, pf, acc1, [](auto) {});
+  };
+  // PAIR, role 1, the step before in buffer BI: X2 (from -Dd), then with the P its
+  // partner handed over at xa one step earlier, dS = P (X2 - Dd) and dK += dS^T Q.
+  auto step_ds = [&](auto buf_tag, uint32_t xa) {
+    constexpr int BI = decltype(buf_tag)::value;
+    f32x16_t ya, yb;
+    f32x4_t dv[8];
+    read_ld(std::integral_constant<int, BI * LDB + 1024>{}, dv);
+    f32x4_t kr[4];
+    rowprod(std::integral_constant<int, BI * TILE>{}, f1, ya, yb, [](auto) {}, from(dv));
+    static_for<4>([&](auto t_tag) {
+      constexpr int t = decltype(t_tag)::value;
+      kr[t] = lds_read_b128<t * 1024>(xa);
+    });
+    lds_wait<0>();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fence(kr[t]);
+    V8 sf[4];
+    auto make_ds = [&](int t) {
+      const V8 pk = as_v8<T>(kr[t]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = 8 * t + u;
+        sf[t][u] = (T)((float)pk[u] * (e < 16 ? ya[e] : yb[e - 16]));
+      }
+      fence(sf[t]);
+    };
+    make_ds(0);
+    trprod(std::integral_constant<int, BI * TILE>{}, sf, acc1, [&](auto t_tag) {
+      constexpr int t = decltype(t_tag)::value;
+      if constexpr (t + 1 < 4) make_ds(t + 1);
+    });
+  };
+
+  if constexpr (PAIR) {
+    // iteration j (0 .. steps): the tiles of step j + 1 are loaded, role 0 works on
+    // step j, role 1 on step j - 1.  Step j's tiles sit in buffer j % 3 from
+    // iteration j - 1 to iteration j + 1; its P in hand-over buffer j % 2 from
+    // iteration j to j + 1.  The barrier at the top of each iteration orders every
+    // reuse: buffer (j + 1) % 3 was last read by role 1 in iteration j - 1, hand-over
+    // buffer j % 2 by role 1 in iteration j - 1 (and role 0's writes have landed).
+    if (steps > 0) {
+      Step cur;
+      tile_first(cur.t, itp + 8);
+      cur.head = hk * a.kv_ratio;
+      cur.jt = 0;
+      load(std::integral_constant<int, 0>{}, cur);
+      // top of iteration j: every wave's tiles of step j have landed (and role 0's
+      // hand-over writes), then the DMA of step j + 1 into buffer (j + 1) % 3.
+      // Returns step j + 1; cur stays step j for the work of the iteration.
+      auto sync_load = [&](auto buf_tag, int j) {
+        constexpr int P = decltype(buf_tag)::value;
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        lds_wait<0>();
+        wg_barrier();
+        Step nxt = cur;
+        if (j + 1 < steps) {
+          advance(nxt);
+          load(std::integral_constant<int, (P + 1) % 3>{}, nxt);
+        }
+        return nxt;
+      };
+      // The two roles run separate loops with the same barriers and DMAs, so that
+      // neither carries the other's accumulator through a branch.
+      if (role == 0) {
+        auto it = [&](auto buf_tag, int j) {
+          const Step nxt = sync_load(buf_tag, j);
+          step_p(buf_tag, cur, x_addr + (uint32_t)((j & 1) * XB));
+          cur = nxt;
+        };
+        int j = 0;
+        for (; j + 3 <= steps; j += 3) {
+          it(std::integral_constant<int, 0>{}, j);
+          it(std::integral_constant<int, 1>{}, j + 1);
+          it(std::integral_constant<int, 2>{}, j + 2);
+        }
+        if (j < steps) it(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < steps) it(std::integral_constant<int, 1>{}, j + 1);
+        sync_load(std::integral_constant<int, 0>{}, steps);  // role 1's last step
+      } else {
+        cur = sync_load(std::integral_constant<int, 0>{}, 0);  // role 0's first step
+        auto it = [&](auto buf_tag, int j) {
+          constexpr int P = decltype(buf_tag)::value;
+          const Step nxt = sync_load(buf_tag, j);
+          // the dS / dK wave issues first when both waves of the SIMD are ready: its
+          // VALU work is the lighter, so the exponentials of role 0 fill behind its
+          // MFMAs rather than the other way round (+0.2 to +1.5% measured)
+          __builtin_amdgcn_s_setprio(1);
+          step_ds(std::integral_constant<int, (P + 2) % 3>{}, x_addr + (uint32_t)(((j - 1) & 1) * XB));
+          __builtin_amdgcn_s_setprio(0);
+          cur = nxt;
+        };
+        int j = 1;
+        for (; j + 2 <= steps; j += 3) {
+          it(std::integral_constant<int, 1>{}, j);
+          it(std::integral_constant<int, 2>{}, j + 1);
+          it(std::integral_constant<int, 0>{}, j + 2);
+        }
+        if (j <= steps) it(std::integral_constant<int, 1>{}, j);
+        if (j + 1 <= steps) it(std::integral_constant<int, 2>{}, j + 1);
+      }
+    }
+  } else if (steps > 0) {
     Step cur;
     tile_first(cur.t, itp + 8);
     cur.head = KV ? hk * a.kv_ratio : hq;
@@ -668,7 +845,10 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           *reinterpret_cast<V4*>(dst + 32 * d + 8 * gq + 4 * hh) = w;
         }
     };
-    if constexpr (KV) {
+    if constexpr (PAIR) {
+      if (role) store(a.dk + (int64_t)b * a.dk_sb + (int64_t)row * a.dk_st + (int64_t)hk * a.dk_sh, acc1, a.scale);
+      else store(a.dv + (int64_t)b * a.dv_sb + (int64_t)row * a.dv_st + (int64_t)hk * a.dv_sh, acc1, 1.0f);
+    } else if constexpr (KV) {
       store(a.dk + (int64_t)b * a.dk_sb + (int64_t)row * a.dk_st + (int64_t)hk * a.dk_sh, acc1, a.scale);
       store(a.dv + (int64_t)b * a.dv_sb + (int64_t)row * a.dv_st + (int64_t)hk * a.dv_sh, acc2, 1.0f);
     } else {
@@ -901,6 +1081,8 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   ba.cap_arg = cap ? (float)(2.0 * 1.4426950408889634074 * (double)softmax_scale / (double)ex.softcap) : 0.0f;
 
   const dim3 block(64 * ffa::kWaves);
+  // the key-major kernel at D = 128 runs its pairs of waves: eight per workgroup
+  const dim3 kv_block(64 * (p.head_dim == 128 ? 2 * ffa::kWaves : ffa::kWaves));
   if (p.num_dq_items > 0) {
     ba.items = dq_items;
     ba.runs = dq_runs;
@@ -924,8 +1106,9 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
       constexpr int D = decltype(d_tag)::value;
       dispatch_dtype(ex.dtype, [&](auto t_tag) {
         using T = decltype(t_tag);
-        if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true, false, T>), grid, block, 0, s, ba);
-        else hipLaunchKernelGGL((ffa_bwd_main<D, true, false, false, T>), grid, block, 0, s, ba);
+        static_assert(kBwdWgWaves<D, true, false> == (D == 128 ? 2 * ffa::kWaves : ffa::kWaves), "block shape");
+        if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true, false, T>), grid, kv_block, 0, s, ba);
+        else hipLaunchKernelGGL((ffa_bwd_main<D, true, false, false, T>), grid, kv_block, 0, s, ba);
       });
     });
     hipError_t e = hipGetLastError();
