@@ -124,6 +124,20 @@ def test_bwd_random_slices_all_mask_types(gpu_lib, seed):
     case(gpu_lib, p, f"random {seed}")
 
 
+@pytest.mark.parametrize("n_tiles", [1, 2, 3, 4, 5, 7])
+@pytest.mark.parametrize("ratio", [1, 2, 4])
+def test_bwd_key_major_step_counts(gpu_lib, n_tiles, ratio):
+    # D = 128, where the dK / dV kernel runs its wave pairs with the dS / dK wave one
+    # step behind over three tile buffers: a key block walks n_tiles query tiles once
+    # per query head of its kv head, so the step count n_tiles * ratio takes every
+    # remainder mod 3 and the one- and two-step cases; a 70-key tail block and a
+    # causal slice exercise the partial DMA and the edge mask on top
+    tq = 64 * n_tiles
+    p = W.make_problem("steps", tq, 198, 2 * ratio, 2, 128,
+                       [((0, tq), (0, 128), W.FULL), ((0, tq), (128, 198), W.CAUSAL)], seed=n_tiles + 10 * ratio)
+    case(gpu_lib, p, f"steps {n_tiles} x {ratio}")
+
+
 @pytest.mark.parametrize("cfg,div", [(2, 4), (3, 8), (4, 16)])
 def test_bwd_scaled_configs(gpu_lib, cfg, div):
     case(gpu_lib, W.scaled(cfg, div), f"config {cfg} / {div}")
