@@ -229,9 +229,11 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
   constexpr int TILE = BN * ROWB;      // bytes of one streamed tile
   constexpr bool PAIR = kPairBwd<D, KV, TOT>;
   constexpr int W = kBwdWgWaves<D, KV, TOT>;  // waves of the workgroup (they share the DMA)
-  constexpr int NLD = TILE / (1024 * W);  // DMA instructions per thread per tile
-  constexpr int RPL = 1024 * W / ROWB;    // rows between consecutive DMA instructions
-  static_assert(NLD * 1024 * W == TILE, "DMA split");
+  // PAIR: only the four role-0 waves issue the tile DMAs (role 1 keeps no step state)
+  constexpr int WD = PAIR ? ffa::kWaves : W;  // waves that share the DMA of a tile
+  constexpr int NLD = TILE / (1024 * WD);     // DMA instructions per thread per tile
+  constexpr int RPL = 1024 * WD / ROWB;       // rows between consecutive DMA instructions
+  static_assert(NLD * 1024 * WD == TILE, "DMA split");
   static_assert(BN == 64 && (D == 16 || D == 32 || D == 64 || D == 128), "tile shape");
   // LDS: A0 | B0 | A1 | B1 (double-buffered tiles), then (key-major) L and Dd of
   // the 64 streamed rows per buffer, 1 KiB each (one DMA instruction writes
@@ -351,7 +353,8 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
   // LDS block (W i + w); lane l's 16 bytes are chunk (lin % CH) of row (lin / CH),
   // loaded from the swizzled global chunk.  Rows past `total` re-read the last
   // row (their scores are masked).
-  const int lin0 = wave * 64 + lane;
+  const int dwv = PAIR ? kw : wave;  // the wave's index among the DMA waves
+  const int lin0 = dwv * 64 + lane;
   const int dr0 = lin0 / CH, dp = lin0 % CH;
   const int sw0 = swz_b<DL>(dr0);
   // D = 16: lanes whose chunk is padding load zeros (an offset past the buffer's end,
@@ -362,19 +365,19 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kstart * st_b), (short)0, 0x7fffffff, kBufferFlags);
       const uint32_t goff = pad_lane ? 0x80000000u : (uint32_t)(dr0 * st_b) + ((dp ^ sw0) << 4);
-      uint32_t ldst = (uint32_t)(uintptr_t)(FFA_LDS char*)smem + dst_off + wave * 1024;
+      uint32_t ldst = (uint32_t)(uintptr_t)(FFA_LDS char*)smem + dst_off + dwv * 1024;
       int32_t rstep = (int32_t)(RPL * st_b);
       asm volatile("" : "+s"(ldst), "+s"(rstep));
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(uintptr_t)(ldst + i * W * 1024), 16, goff,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FFA_LDS void*)(uintptr_t)(ldst + i * WD * 1024), 16, goff,
                                                  i * rstep, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int r = min(kstart + dr0 + i * RPL, total - 1);
         __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)r * st_b + (pad_lane ? 0 : (dp ^ sw0) << 4)),
-                                         (FFA_LDS void*)(smem + dst_off + (i * W + wave) * 1024), 16, 0, 0);
+                                         (FFA_LDS void*)(smem + dst_off + (i * WD + dwv) * 1024), 16, 0, 0);
       }
     }
   };
@@ -744,7 +747,7 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
       tile_first(cur.t, itp + 8);
       cur.head = hk * a.kv_ratio;
       cur.jt = 0;
-      load(std::integral_constant<int, 0>{}, cur);
+      if (role == 0) load(std::integral_constant<int, 0>{}, cur);
       // top of iteration j: every wave's tiles of step j have landed (and role 0's
       // hand-over writes), then the DMA of step j + 1 into buffer (j + 1) % 3.
       // Returns step j + 1; cur stays step j for the work of the iteration.
@@ -778,17 +781,21 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
         if (j + 1 < steps) it(std::integral_constant<int, 1>{}, j + 1);
         sync_load(std::integral_constant<int, 0>{}, steps);  // role 1's last step
       } else {
-        cur = sync_load(std::integral_constant<int, 0>{}, 0);  // role 0's first step
+        // role 1 issues no DMA: its iterations only wait at the barrier
+        auto sync = [&]() {
+          lds_wait<0>();
+          wg_barrier();
+        };
+        sync();  // role 0's first step
         auto it = [&](auto buf_tag, int j) {
           constexpr int P = decltype(buf_tag)::value;
-          const Step nxt = sync_load(buf_tag, j);
+          sync();
           // the dS / dK wave issues first when both waves of the SIMD are ready: its
           // VALU work is the lighter, so the exponentials of role 0 fill behind its
           // MFMAs rather than the other way round (+0.2 to +1.5% measured)
           __builtin_amdgcn_s_setprio(1);
           step_ds(std::integral_constant<int, (P + 2) % 3>{}, x_addr + (uint32_t)(((j - 1) & 1) * XB));
           __builtin_amdgcn_s_setprio(0);
-          cur = nxt;
         };
         int j = 1;
         for (; j + 2 <= steps; j += 3) {
