@@ -418,6 +418,37 @@ def test_flash_attention_split_kv(gpu_lib, d, causal, num_splits):
                 what=f"split_kv D={d} causal={causal} splits={num_splits} b={b}")
 
 
+@pytest.mark.parametrize("m,n,num_splits", [(300, 40, 4), (64, 1000, 64), (130, 129, 2), (1, 5000, 3)])
+def test_flash_attention_split_kv_edges(gpu_lib, m, n, num_splits):
+    # more query rows than keys under bottom-right causal (the first m - n rows see
+    # nothing: out 0, lse -inf), more splits than key tiles, ragged tails, one row
+    B, Hq, Hkv, d = 1, 4, 2, 128
+    g = torch.Generator().manual_seed(m + n + num_splits)
+    q = torch.randn(B, Hq, m, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16)
+    dev = torch.device("cuda", 0)
+    for causal in (True, False):
+        out, lse = gpu_lib.flash_attention_split_kv(q.to(dev), k.to(dev), v.to(dev), causal=causal,
+                                                    num_splits=num_splits, return_log_normalizer=True)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attend(q[0].permute(1, 0, 2), k[0].permute(1, 0, 2), v[0].permute(1, 0, 2),
+                               [[0, m]], [[0, n]], [W.CAUSAL if causal else W.FULL])
+        compare(out[0].permute(1, 0, 2), lse[0].permute(1, 0), ro, rl,
+                what=f"split_kv edges m={m} n={n} splits={num_splits} causal={causal}")
+
+
+def test_flash_attention_split_kv_rejects_bad_arguments(gpu_lib):
+    dev = torch.device("cuda", 0)
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 3, 8, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(Exception):
+        gpu_lib.flash_attention_split_kv(q, k, k)  # Hq % Hkv != 0
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        gpu_lib.flash_attention_split_kv(q, k, k, num_splits=-1)
+
+
 def test_product_path_has_no_fallback(gpu_lib):
     # the binding routes through libffa.so: its handle is loaded and no oracle module is imported by it
     import flexible_mask_flash_amd as ffa
