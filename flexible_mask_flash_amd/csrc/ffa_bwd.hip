@@ -229,7 +229,8 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
   constexpr int TILE = BN * ROWB;      // bytes of one streamed tile
   constexpr bool PAIR = kPairBwd<D, KV, TOT>;
   constexpr int W = kBwdWgWaves<D, KV, TOT>;  // waves of the workgroup (they share the DMA)
-  // PAIR: only the four role-0 waves issue the tile DMAs (role 1 keeps no step state)
+  // PAIR: only the four role-1 waves issue the tile DMAs, so that role 0, whose
+  // exponentials dominate the VALU work, spends no issue slots on the DMA setup
   constexpr int WD = PAIR ? ffa::kWaves : W;  // waves that share the DMA of a tile
   constexpr int NLD = TILE / (1024 * WD);     // DMA instructions per thread per tile
   constexpr int RPL = 1024 * WD / ROWB;       // rows between consecutive DMA instructions
@@ -385,7 +386,7 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
   // (wave 0; lanes 16-63 repeat lanes 0-15 into padding).  Reads past total_q
   // return zeros (the buffer's size ends there).
   auto dma_ld = [&](int dst_off, int head, int kstart) {
-    if (wave == 0) {
+    if (dwv == 0) {
       const int64_t rowoff = ((int64_t)b * a.heads_q + head) * a.total_q + kstart;
       const int nrec = max(0, a.total_q - kstart) * 4;
       const __amdgpu_buffer_rsrc_t rl =
@@ -747,7 +748,7 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
       tile_first(cur.t, itp + 8);
       cur.head = hk * a.kv_ratio;
       cur.jt = 0;
-      if (role == 0) load(std::integral_constant<int, 0>{}, cur);
+      if (role == 1) load(std::integral_constant<int, 0>{}, cur);
       // top of iteration j: every wave's tiles of step j have landed (and role 0's
       // hand-over writes), then the DMA of step j + 1 into buffer (j + 1) % 3.
       // Returns step j + 1; cur stays step j for the work of the iteration.
@@ -759,7 +760,7 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
         Step nxt = cur;
         if (j + 1 < steps) {
           advance(nxt);
-          load(std::integral_constant<int, (P + 1) % 3>{}, nxt);
+          if (role == 1) load(std::integral_constant<int, (P + 1) % 3>{}, nxt);
         }
         return nxt;
       };
@@ -781,18 +782,14 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
         if (j + 1 < steps) it(std::integral_constant<int, 1>{}, j + 1);
         sync_load(std::integral_constant<int, 0>{}, steps);  // role 1's last step
       } else {
-        // role 1 issues no DMA: its iterations only wait at the barrier
-        auto sync = [&]() {
-          lds_wait<0>();
-          wg_barrier();
-        };
-        sync();  // role 0's first step
+        cur = sync_load(std::integral_constant<int, 0>{}, 0);  // role 0's first step
         auto it = [&](auto buf_tag, int j) {
           constexpr int P = decltype(buf_tag)::value;
-          sync();
+          cur = sync_load(buf_tag, j);
           // the dS / dK wave issues first when both waves of the SIMD are ready: its
           // VALU work is the lighter, so the exponentials of role 0 fill behind its
-          // MFMAs rather than the other way round (+0.2 to +1.5% measured)
+          // MFMAs rather than the other way round (measured: without the priority
+          // -1 to -3.5%, with role 0 raised instead -5 to -7%)
           __builtin_amdgcn_s_setprio(1);
           step_ds(std::integral_constant<int, (P + 2) % 3>{}, x_addr + (uint32_t)(((j - 1) & 1) * XB));
           __builtin_amdgcn_s_setprio(0);
