@@ -18,17 +18,19 @@
 //                        kv head and walks the query tiles of the transposed
 //                        slices once per query head of that kv head
 // Both main kernels are one template: a lane owns one "row" (a query for dQ, a
-// key for dK/dV) whose two operand fragments stay in registers (q and dO, or k
-// and v), and 64-row tiles of the other side stream through LDS (k and v, or q
-// and dO), double-buffered and filled by global_load_lds.  Per tile:
+// key for dK/dV) whose operand fragments stay in registers (q and dO, or k or v),
+// and 64-row tiles of the other side stream through LDS (k and v, or q and dO),
+// filled by global_load_lds (double-buffered query-major, triple-buffered
+// key-major).  Per tile:
 //   X1 = A F1^T, X2 = B F2^T       (v_mfma_f32_32x32x16_bf16, A/B rows from LDS)
 //   P = exp2(X1 c2 - L), dS = P (X2 - Dd)   (fp32)
 // Key-major, the lane's 32 scores belong to 32 different queries, each with its own
 // L and Dd: rather than holding those in registers, the MFMAs start their
 // accumulators from them (X1 from -lse / scale, X2 from -Dd, read from LDS), so that
 // P = exp2(c2 X1) and dS = P X2 directly.
-//   acc1 += A^T dS  (dQ^T or dK^T),  acc2 += B^T P  (dV^T, key-major only)
-// with A^T / B^T read from LDS by ds_read_b64_tr_b16.
+//   dQ^T += K^T dS (query-major); dV^T += dO^T P and dK^T += Q^T dS (key-major, one
+//   product in each wave of a pair)
+// with the transposed operands read from LDS by ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -187,23 +189,21 @@ __device__ __forceinline__ int swz_b(int r) {
                    : ((r >> 2) & 3);  // 64-byte rows: four rows per bank window already
 }
 
-// Occupancy: two waves per SIMD, so that one wave's VALU work hides behind the
-// other's MFMAs.  The query-major kernel, total attention (no accumulators) and
-// the key-major kernel up to D = 64 fit 256 registers with one wave per 32 rows.
-// At D = 128 one key-major wave would hold both fp32 accumulators (dK and dV, 64
-// registers each) and both fragments (k and v, 32 each): ~330 registers, one wave
-// per SIMD.  There the 32 keys of a block are shared by a pair of waves instead
-// (PAIR), eight waves for the item's 128 keys: role 0 holds k and dV and computes
-// X1 = K Q^T, P and dV += P^T dO; role 1 holds v and dK and computes X2 = V dO^T
-// - Dd, takes P from its partner through LDS and computes dS and dK += dS^T Q.
-// Role 1 works one step behind role 0, so the hand-over needs no barrier of its
-// own and the two waves of a SIMD run their products and softmax work out of
-// phase (tiles triple-buffered; one barrier per step as elsewhere).  Roles
-// alternate over the wave index as (w ^ (w >> 2)) & 1, so that each SIMD holds
-// one wave of each role whether the hardware places waves w and w + 4 or waves
-// 2i and 2i + 1 on one SIMD; the key block is w >> 1.
+// Occupancy: two waves per SIMD (or more), so that one wave's VALU work hides behind
+// another's MFMAs.  The query-major kernel and total attention run one wave per 32
+// rows.  The key-major kernel (dK and dV) runs a pair of waves per 32-key block
+// (PAIR), eight waves for the item's 128 keys: one wave per block would hold both fp32
+// accumulators and both fragments (~330 registers at D = 128, one wave per SIMD).
+// Role 0 holds k and dV and computes X1 = K Q^T, P and dV += P^T dO; role 1 holds v
+// and dK and computes X2 = V dO^T - Dd, takes P from its partner through LDS and
+// computes dS and dK += dS^T Q.  Role 1 works one step behind role 0, so the
+// hand-over needs no barrier of its own and the two waves of a SIMD run their
+// products and softmax work out of phase (tiles triple-buffered; one barrier per
+// step as elsewhere).  Roles alternate over the wave index as (w ^ (w >> 2)) & 1, so
+// that each SIMD holds one wave of each role whether the hardware places waves w
+// and w + 4 or waves 2i and 2i + 1 on one SIMD; the key block is w >> 1.
 template <int D, bool KV, bool TOT>
-constexpr bool kPairBwd = KV && !TOT && D == 128;
+constexpr bool kPairBwd = KV && !TOT;
 template <int D, bool KV, bool TOT>
 constexpr int kBwdWgWaves = kPairBwd<D, KV, TOT> ? 2 * ffa::kWaves : ffa::kWaves;
 
@@ -306,17 +306,12 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
     d_row = a.dw[idx];
   }
 
-  // acc1: dK (key-major), dQ (query-major), or the pair wave's own dV or dK
-  constexpr int NACC2 = (KV && !PAIR) ? DBLK : 1;
-  f32x16_t acc1[DBLK], acc2[NACC2];
+  // acc1: dQ (query-major) or the pair wave's own dV or dK (key-major)
+  f32x16_t acc1[DBLK];
 #pragma unroll
   for (int d = 0; d < DBLK; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc1[d][i] = 0.0f;
-#pragma unroll
-  for (int d = 0; d < NACC2; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc2[d][i] = 0.0f;
 
   // ---- per-lane LDS read addresses (the low 10 bits of the LDS base are zero)
   const uint32_t lds = (uint32_t)(uintptr_t)(FFA_LDS char*)smem;
@@ -556,13 +551,14 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
       }
     };
   };
+  // query-major step, or (TOT) a total-attention step: X1 and P only
   auto compute = [&](auto buf_tag, const Step& s) {
     constexpr int OA = decltype(buf_tag)::value * BUFB;
     constexpr int OB = OA + TILE;
     constexpr int OL = decltype(buf_tag)::value * LDB;  // relative to ld_addr
     f32x16_t xa, xb, ya, yb;
-    // key-major uncapped, X1 starts at -lse / scale; soft-capped, the lane keeps
-    // lse * log2 e of its 32 queries (lv) for the tanh path
+    // total attention, uncapped: X1 starts at -lse / scale; soft-capped, the lane
+    // keeps lse * log2 e of its 32 queries (lv) for the tanh path
     f32x4_t lv[8];
     if constexpr (KV) read_ld(std::integral_constant<int, OL>{}, lv);
     if constexpr (KV && !CAP)
@@ -592,72 +588,44 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
         write_total(s.head, partner_sum(tsum));
         tsum = 0.0f;
       }
-      return;
-    }
-    // P = exp2(X1 c2 - L) in place, between the MFMAs of X2 (key-major uncapped,
-    // L is already in X1).  Soft-capped: P = exp2(cap_log2 tanh - L) (masked scores
-    // stay at P = 0), and what stays in place is P (1 - tanh^2), the factor of dS;
-    // P itself goes to bf16 at once.  Key-major, X2 starts at -Dd.
-    auto lval = [&](int e) -> float { return KV ? lv[e >> 2][e & 3] : l_row; };
-    constexpr int EPQ = 32 / (2 * KSTEPS);  // score elements per MFMA of X2
-    V8 pf[4], sf[4];
-    f32x4_t dv[8];
-    if constexpr (KV) read_ld(std::integral_constant<int, OL + 1024>{}, dv);
-    auto x2_init = [&](f32x16_t& u, f32x16_t& w) {
-      if constexpr (KV) from(dv)(u, w);
-      else zero(u, w);
-    };
-    rowprod(std::integral_constant<int, OB>{}, f2, ya, yb, [&](auto m_tag) {
-      constexpr int m = decltype(m_tag)::value;
+    } else {
+      // query-major: P = exp2(X1 c2 - L) in place, between the MFMAs of X2.
+      // Soft-capped: P = exp2(cap_log2 tanh - L) (masked scores stay at P = 0), and
+      // what stays in place is P (1 - tanh^2), the factor of dS.
+      constexpr int EPQ = 32 / (2 * KSTEPS);  // score elements per MFMA of X2
+      V8 sf[4];
+      rowprod(std::integral_constant<int, OB>{}, f2, ya, yb, [&](auto m_tag) {
+        constexpr int m = decltype(m_tag)::value;
 #pragma unroll
-      for (int e = EPQ * m; e < EPQ * (m + 1); ++e) {
-        if constexpr (CAP) {
-          const float x = e < 16 ? xa[e] : xb[e - 16];
-          const float th = tanh_from_2ylog2e(x * a.cap_arg);
-          const float arg = x == -INFINITY ? -INFINITY : __builtin_fmaf(a.cap_log2, th, -lval(e));
-          const float pr = __builtin_amdgcn_exp2f(arg);
-          if constexpr (KV) pf[e >> 3][e & 7] = (T)pr;
-          const float keep = pr * __builtin_fmaf(-th, th, 1.0f);
-          if (e < 16) xa[e] = keep;
-          else xb[e - 16] = keep;
-        } else if constexpr (KV) {
-          if (e < 16) xa[e] = __builtin_amdgcn_exp2f(xa[e] * c2);
-          else xb[e - 16] = __builtin_amdgcn_exp2f(xb[e - 16] * c2);
-        } else {
-          if (e < 16) xa[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xa[e], c2, -l_row));
-          else xb[e - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(xb[e - 16], c2, -l_row));
+        for (int e = EPQ * m; e < EPQ * (m + 1); ++e) {
+          if constexpr (CAP) {
+            const float x = e < 16 ? xa[e] : xb[e - 16];
+            const float th = tanh_from_2ylog2e(x * a.cap_arg);
+            const float arg = x == -INFINITY ? -INFINITY : __builtin_fmaf(a.cap_log2, th, -l_row);
+            const float pr = __builtin_amdgcn_exp2f(arg);
+            const float keep = pr * __builtin_fmaf(-th, th, 1.0f);
+            if (e < 16) xa[e] = keep;
+            else xb[e - 16] = keep;
+          } else {
+            if (e < 16) xa[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xa[e], c2, -l_row));
+            else xb[e - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(xb[e - 16], c2, -l_row));
+          }
         }
-      }
-      fence(xa);
-      fence(xb);
-    }, x2_init);
-    // dS = P (X2 - Dd) and the bf16 operands of the transposed products, one
-    // 16-row step t at a time, so that the VALU work of a step runs behind MFMAs:
-    // key-major, all of dS behind the dV product (which needs only P); query-
-    // major, step t + 1 behind the MFMAs of step t.
-    auto make_ds = [&](int t) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = 8 * t + u;
-        const float p = e < 16 ? xa[e] : xb[e - 16];
-        const float y = e < 16 ? ya[e] : yb[e - 16];
-        sf[t][u] = (T)(KV ? p * y : p * (y + d_row));
-      }
-      fence(sf[t]);
-    };
-    if constexpr (!CAP && KV) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
+        fence(xa);
+        fence(xb);
+      }, zero);
+      // dS = P (X2 - Dd) and its bf16 operand, one 16-row step t at a time: step
+      // t + 1 behind the MFMAs of step t
+      auto make_ds = [&](int t) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int e = 8 * t + u;
-          pf[t][u] = (T)(e < 16 ? xa[e] : xb[e - 16]);
+          const float p = e < 16 ? xa[e] : xb[e - 16];
+          const float y = e < 16 ? ya[e] : yb[e - 16];
+          sf[t][u] = (T)(p * (y + d_row));
         }
-    }
-    if constexpr (KV) {
-      trprod(std::integral_constant<int, OB>{}, pf, acc2, [&](auto t_tag) { make_ds(decltype(t_tag)::value); });
-      trprod(std::integral_constant<int, OA>{}, sf, acc1, [](auto) {});
-    } else {
+        fence(sf[t]);
+      };
       make_ds(0);
       trprod(std::integral_constant<int, OA>{}, sf, acc1, [&](auto t_tag) {
         constexpr int t = decltype(t_tag)::value;
@@ -852,9 +820,6 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
     if constexpr (PAIR) {
       if (role) store(a.dk + (int64_t)b * a.dk_sb + (int64_t)row * a.dk_st + (int64_t)hk * a.dk_sh, acc1, a.scale);
       else store(a.dv + (int64_t)b * a.dv_sb + (int64_t)row * a.dv_st + (int64_t)hk * a.dv_sh, acc1, 1.0f);
-    } else if constexpr (KV) {
-      store(a.dk + (int64_t)b * a.dk_sb + (int64_t)row * a.dk_st + (int64_t)hk * a.dk_sh, acc1, a.scale);
-      store(a.dv + (int64_t)b * a.dv_sb + (int64_t)row * a.dv_st + (int64_t)hk * a.dv_sh, acc2, 1.0f);
     } else {
       store(a.dq + (int64_t)b * a.dq_sb + (int64_t)row * a.dq_st + (int64_t)hq * a.dq_sh, acc1, a.scale);
     }
@@ -1085,8 +1050,8 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   ba.cap_arg = cap ? (float)(2.0 * 1.4426950408889634074 * (double)softmax_scale / (double)ex.softcap) : 0.0f;
 
   const dim3 block(64 * ffa::kWaves);
-  // the key-major kernel at D = 128 runs its pairs of waves: eight per workgroup
-  const dim3 kv_block(64 * (p.head_dim == 128 ? 2 * ffa::kWaves : ffa::kWaves));
+  // the key-major kernel runs its pairs of waves: eight per workgroup
+  const dim3 kv_block(64 * 2 * ffa::kWaves);
   if (p.num_dq_items > 0) {
     ba.items = dq_items;
     ba.runs = dq_runs;
@@ -1110,7 +1075,7 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
       constexpr int D = decltype(d_tag)::value;
       dispatch_dtype(ex.dtype, [&](auto t_tag) {
         using T = decltype(t_tag);
-        static_assert(kBwdWgWaves<D, true, false> == (D == 128 ? 2 * ffa::kWaves : ffa::kWaves), "block shape");
+        static_assert(kBwdWgWaves<D, true, false> == 2 * ffa::kWaves, "block shape");
         if (cap) hipLaunchKernelGGL((ffa_bwd_main<D, true, true, false, T>), grid, kv_block, 0, s, ba);
         else hipLaunchKernelGGL((ffa_bwd_main<D, true, false, false, T>), grid, kv_block, 0, s, ba);
       });
