@@ -40,6 +40,10 @@
  * workspace, q/k/v/out/lse) belongs to the caller.  The library never allocates
  * or frees device memory and never synchronises a stream; ffa_fwd only enqueues
  * kernels, so a device fault surfaces at the caller's next synchronisation.
+ * ffa_fwd, ffa_combine, ffa_bwd and ffa_total_attention enqueue kernels only (no
+ * copies, no memory clears), so they may be captured into a HIP graph once the
+ * plan's metadata has been uploaded (ffa_plan_upload copies from host memory and
+ * belongs outside the capture).
  *
  * Errors.  Every call returns an ffa_status.  Arguments are validated before
  * anything is enqueued, so a non-OK return means nothing was written.
