@@ -296,3 +296,16 @@ def test_bwd_head_dim_16(gpu_lib, seed):
     hq = hkv * int(rng.choice([1, 2, 4]))
     p = W.random_problem(3000 + seed, tq, tk, hq, hkv, 16, n_types=4)
     case(gpu_lib, p, f"D 16 random {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_bwd_wave_pairs_random_shapes(gpu_lib, seed):
+    # the key-major wave pairs at every head dim, over random sizes (ragged key
+    # blocks and query tiles), GQA ratios up to 8 and all four mask types
+    rng = np.random.default_rng(5100 + seed)
+    d = int((16, 32, 64, 128)[seed % 4])
+    tq, tk = int(rng.integers(1, 900)), int(rng.integers(1, 900))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    p = W.random_problem(5100 + seed, tq, tk, hq, hkv, d, n_types=4)
+    case(gpu_lib, p, f"pairs D {d} random {seed}")
