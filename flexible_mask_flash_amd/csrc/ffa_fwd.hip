@@ -132,8 +132,15 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? ((r & 3) << 2) : D == 64 ? (((r >> 1) & 1) << 2) : 0;
 }
 
+// Waves per SIMD the compiler budgets registers for: two at D = 128 (256 VGPRs), more
+// below, where O and the fragments shrink but the per-score softmax work does not, so a
+// third or fourth wave hides more of it (+4.5% at D = 64 with three, +4 to +6% at
+// D = 32 and 16 with four; the few spills this costs sit outside the tile loop).
+template <int D>
+constexpr int kFwdWaves = D <= 32 ? 4 : D <= 64 ? 3 : 2;
+
 template <int D, bool CAP, typename T>
-__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_fwd_main(FwdArgs a) {
+__global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(kFwdWaves<D>, kFwdWaves<D>))) void ffa_fwd_main(FwdArgs a) {
   using V8 = typename ElemT<T>::v8;
   using V4 = typename ElemT<T>::v4;
   using V2 = typename ElemT<T>::v2;
