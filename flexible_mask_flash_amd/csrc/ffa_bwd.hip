@@ -207,10 +207,15 @@ constexpr bool kPairBwd = KV && !TOT;
 template <int D, bool KV, bool TOT>
 constexpr int kBwdWgWaves = kPairBwd<D, KV, TOT> ? 2 * ffa::kWaves : ffa::kWaves;
 
+// Register budget: two waves per SIMD, three for the query-major kernel at D = 64
+// (167 VGPRs; +1.4% on that backward).  At D <= 32 both kernels fit four anyway.
+template <int D, bool KV>
+constexpr int kBwdWavesEU = (!KV && D == 64) ? 3 : 2;
+
 // TOT (key-major only): FlagAttention's total attention, sum_i P[i,h,j] per key j and
 // query head h -- the same walk over the transposed worklist with only X1 and P.
 template <int D, bool KV, bool CAP, bool TOT, typename T>
-__global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_bwd_main(BwdArgs a) {
+__global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdgpu_waves_per_eu(kBwdWavesEU<D, KV>, kBwdWavesEU<D, KV>))) void ffa_bwd_main(BwdArgs a) {
   using V8 = typename ElemT<T>::v8;
   using V4 = typename ElemT<T>::v4;
   using V2 = typename ElemT<T>::v2;
