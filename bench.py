@@ -156,6 +156,24 @@ CLOCK_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INS
                   "SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_INSTS_SALU GRBM_GUI_ACTIVE")
 
 
+def plan_balance(plan, slots: int) -> dict:
+    """Load balance of the forward worklist: each item's cost in key tiles (+3 for its
+    prologue and epilogue, +1 for an item with no runs), dispatched longest-first in
+    list order onto `slots` resident workgroups; the makespan against the mean."""
+    import heapq
+
+    meta = plan.meta_host()
+    n = int(plan.info["num_items"])
+    recs = meta[16:16 + 16 * n].reshape(n, 16)  # item records after the 16-word header
+    costs = [int(t) + (3 if int(r) > 0 else 1) for t, r in zip(recs[:, 6], recs[:, 4])]
+    heap = [0] * slots
+    for c in costs:
+        heapq.heapreplace(heap, heap[0] + c)
+    mean = sum(costs) / slots
+    return {"slots": slots, "mean_tiles_per_slot": round(mean, 2), "makespan_tiles": max(heap),
+            "makespan_over_mean": round(max(heap) / mean, 3) if mean else None}
+
+
 def algorithmic_bytes(p) -> int:
     """Bytes the forward must move at least: q, k, v read and out written (bf16), lse written (fp32)."""
     d = p.head_dim
@@ -397,6 +415,7 @@ def main():
             "flops_per_step": flops,
             "plan": {k_: int(v_) for k_, v_ in plan.info.items()},
             "plan_ms": round(plan_ms, 2),
+            "plan_balance": plan_balance(plan, 2 * torch.cuda.get_device_properties(dev).multi_processor_count),
             "split_tiles": args.split_tiles,
             "softcap": args.softcap,
             "sinks": args.sinks,
