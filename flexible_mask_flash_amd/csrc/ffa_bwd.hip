@@ -9,11 +9,12 @@
 // MagiAttention quickstart, "Single-GPU Flex-Flash-Attention"; FlagAttention
 // user guide, "FlashAttention").
 //
-// Three kernels, all on the caller's stream, no atomics (results are bitwise
+// Two kernels, both on the caller's stream, no atomics (results are bitwise
 // reproducible):
-//   ffa_bwd_pre          -Dd and L per (head, row) into the workspace
 //   ffa_bwd_main<D, 0>   dQ, query-major: a workgroup owns the rows of one
-//                        forward item (unsplit) and walks its key tiles
+//                        forward item (unsplit) and walks its key tiles; it
+//                        first forms -Dd and L of its rows and stores them into
+//                        the workspace (every (row, head) is in one such item)
 //   ffa_bwd_main<D, 1>   dK and dV, key-major: a workgroup owns 128 keys of one
 //                        kv head and walks the query tiles of the transposed
 //                        slices once per query head of that kv head
@@ -55,7 +56,7 @@ struct PreArgs {
   const __bf16* out;
   const __bf16* dout;
   const float* lse;
-  float* lw;  // [batch][heads_q][total_q]: L (see ffa_bwd_pre)
+  float* lw;  // [batch][heads_q][total_q]: L (see below)
   float* dw;  // [batch][heads_q][total_q]: -Dd
   int64_t o_sb, o_st, o_sh;
   int64_t d_sb, d_st, d_sh;
@@ -82,8 +83,12 @@ struct BwdArgs {
   int64_t dq_sb, dq_st, dq_sh;
   int64_t dk_sb, dk_st, dk_sh;
   int64_t dv_sb, dv_st, dv_sh;
-  const float* lw;
-  const float* dw;
+  float* lw;  // L and -Dd per (batch, head, row): read by the key-major kernel; the
+  float* dw;  // query-major kernel writes them (from out, dout and lse) before it
+  const __bf16* out;  // query-major: the forward's output and lse (for Dd and L)
+  int64_t o_sb, o_st, o_sh;
+  const float* lse;
+  int64_t l_sb, l_st, l_sh;
   float scale_log2;  // softmax_scale * log2(e)
   float scale;
   int32_t total_q, total_k, heads_q, batch;
@@ -136,7 +141,9 @@ __global__ __launch_bounds__(256) void ffa_bwd_dsink(SinkArgs a) {
 
 // -Dd[b,h,t] with Dd = sum_d dO[b,t,h,d] O[b,t,h,d] (fp32 from the bf16 values), and
 // L[b,h,t] = -lse / scale (fold) or lse * log2 e: either way a row that sees no key
-// (lse = -inf) gets the value that makes its P zero.
+// (lse = -inf) gets the value that makes its P zero.  Total attention launches it
+// for L alone (no out); the gradient's query-major kernel forms both itself, with
+// the same sums in the same order.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void ffa_bwd_pre(PreArgs a) {
   using V8 = typename ElemT<T>::v8;
@@ -289,26 +296,63 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
     const __bf16* p2 = KV ? a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh + (int64_t)row * a.v_st
                           : a.dout + (int64_t)b * a.d_sb + (int64_t)hq * a.d_sh + (int64_t)row * a.d_st;
     const bool load = row_ok && n_runs > 0;
+    // query-major: dO is read for every row of the item, those without keys included,
+    // since its Dd is computed below
+    const bool load2 = KV ? load : row_ok;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       if (load) {
         f1[s] = reinterpret_cast<const V8*>(p1 + hh * (D / 2))[s];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f1[s][j] = (T)0.0f;
+      }
+      if (load2) {
         f2[s] = reinterpret_cast<const V8*>(p2 + hh * (D / 2))[s];
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          f1[s][j] = (T)0.0f;
-          f2[s][j] = (T)0.0f;
-        }
+        for (int j = 0; j < 8; ++j) f2[s][j] = (T)0.0f;
       }
     }
   }
-  // query-major: the row's lse * log2 e and -Dd are per lane
+  // query-major: the row's L (lse * log2 e) and -Dd are per lane.  The dQ worklist
+  // holds every (row, head) exactly once, rows without keys included, so this kernel
+  // also stores both into the workspace for the key-major kernel and the sink
+  // gradient that run after it.  Dd = sum_d dO[d] out[d]: 16-byte chunks of 8 values
+  // summed in order by FMA, then the chunk sums in a butterfly whose first level
+  // pairs chunk s of the lower head-dim half with chunk s of the upper one.
   float l_row = 0.0f, d_row = 0.0f;
-  if (!KV && row_ok && n_runs > 0) {
-    const int64_t idx = ((int64_t)b * a.heads_q + hq) * a.total_q + row;
-    l_row = CAP ? a.lw[idx] : -(a.lw[idx] * a.scale_log2);
-    d_row = a.dw[idx];
+  if constexpr (!KV) {
+    if (row_ok) {
+      const V8* po = reinterpret_cast<const V8*>(a.out + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh +
+                                                 (int64_t)row * a.o_st + hh * (D / 2));
+      float cs[KSTEPS];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const V8 o = po[s];
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)f2[s][e], acc);
+        cs[s] = acc;
+      }
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) cs[s] = partner_sum(cs[s]);
+#pragma unroll
+      for (int m = KSTEPS / 2; m >= 1; m >>= 1)
+#pragma unroll
+        for (int s = 0; s < m; ++s) cs[s] += cs[s + m];
+      const float l = a.lse[(int64_t)b * a.l_sb + (int64_t)row * a.l_st + (int64_t)hq * a.l_sh];
+      // L: -lse / scale (the K Q^T accumulators start from it), or lse * log2 e when
+      // soft-capped; rows that see nothing get the value that makes P = 0
+      const float lw = CAP ? (l == -INFINITY ? INFINITY : l * kLog2e) : (l == -INFINITY ? -INFINITY : -l / a.scale);
+      if (hh == 0) {
+        const int64_t idx = ((int64_t)b * a.heads_q + hq) * a.total_q + row;
+        a.lw[idx] = lw;
+        a.dw[idx] = -cs[0];
+      }
+      l_row = CAP ? lw : -(lw * a.scale_log2);
+      d_row = -cs[0];
+    }
   }
 
   // acc1: dQ (query-major) or the pair wave's own dV or dK (key-major)
@@ -992,32 +1036,8 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   hipStream_t s = (hipStream_t)stream;
   float* lw = static_cast<float*>(d_workspace);
   float* dwp = lw ? lw + (size_t)batch * p.heads_q * p.total_q : nullptr;
-  if (has_q) {
-    PreArgs pa;
-    pa.out = static_cast<const __bf16*>(out);
-    pa.dout = static_cast<const __bf16*>(dout);
-    pa.lse = lse;
-    pa.lw = lw;
-    pa.dw = dwp;
-    pa.o_sb = o_sb; pa.o_st = o_st; pa.o_sh = o_sh;
-    pa.d_sb = d_sb; pa.d_st = d_st; pa.d_sh = d_sh;
-    pa.l_sb = l_sb; pa.l_st = l_st; pa.l_sh = l_sh;
-    pa.total_q = p.total_q;
-    pa.heads_q = p.heads_q;
-    pa.scale = softmax_scale;
-    pa.fold = ex.softcap > 0.0f ? 0 : 1;
-    const int ppb = 256 / (p.head_dim / 8);
-    const int64_t pairs = (int64_t)p.total_q * p.heads_q;
-    const dim3 grid((unsigned)((pairs + ppb - 1) / ppb), (unsigned)batch);
-    dispatch_head_dim(p.head_dim, [&](auto d_tag) {
-      dispatch_dtype(ex.dtype, [&](auto t_tag) {
-        hipLaunchKernelGGL((ffa_bwd_pre<decltype(d_tag)::value, decltype(t_tag)>), grid, dim3(256), 0, s, pa);
-      });
-    });
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail_b(e, "launch ffa_bwd_pre");
-  }
-
+  // L and -Dd of every (row, head) come from the query-major kernel, which runs
+  // first: the key-major kernel and the sink gradient read them from the workspace.
   const int32_t* meta = static_cast<const int32_t*>(d_meta);
   const int32_t* bw = meta + p.bwd_off + ffa::kBwdHdr;
   const int32_t* dq_items = bw;
@@ -1025,7 +1045,7 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   const int32_t* kv_items = dq_runs + (size_t)p.num_dq_runs * kRec;
   const int32_t* kv_runs = kv_items + (size_t)p.num_kv_items * kItemRec;
 
-  BwdArgs ba;
+  BwdArgs ba = {};
   ba.q = static_cast<const __bf16*>(q);
   ba.k = static_cast<const __bf16*>(k);
   ba.v = static_cast<const __bf16*>(v);
@@ -1042,6 +1062,10 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   ba.dv_sb = dv_sb; ba.dv_st = dv_st; ba.dv_sh = dv_sh;
   ba.lw = lw;
   ba.dw = dwp;
+  ba.out = static_cast<const __bf16*>(out);
+  ba.o_sb = o_sb; ba.o_st = o_st; ba.o_sh = o_sh;
+  ba.lse = lse;
+  ba.l_sb = l_sb; ba.l_st = l_st; ba.l_sh = l_sh;
   ba.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   ba.scale = softmax_scale;
   ba.total_q = p.total_q;
