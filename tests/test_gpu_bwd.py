@@ -309,3 +309,54 @@ def test_bwd_wave_pairs_random_shapes(gpu_lib, seed):
     hq = hkv * int(rng.choice([1, 2, 4, 8]))
     p = W.random_problem(5100 + seed, tq, tk, hq, hkv, d, n_types=4)
     case(gpu_lib, p, f"pairs D {d} random {seed}")
+
+
+@pytest.mark.parametrize("d,cap,f16", [(64, 0.0, False), (128, 0.0, False), (32, 30.0, False), (16, 0.0, True)])
+def test_bwd_workspace_holds_l_and_dd_of_every_row(gpu_lib, d, cap, f16):
+    # The query-major kernel stores L and -Dd of every (batch, head, row) into the
+    # workspace for the key-major kernel and the sink gradient, rows that see no key
+    # included.  Checked against their definitions on seeded out / dout / lse (any
+    # values will do: neither depends on out being the forward's):
+    # Dd = sum_d dout * out (fp64 of the same 16-bit values), and L = -lse / scale, or
+    # lse * log2 e when soft-capped (fp32, as specified: bit for bit), with lse = -inf
+    # mapped to the value that makes P zero.
+    ffa = gpu_lib
+    dt = torch.float16 if f16 else torch.bfloat16
+    B, tq, tk, hq, hkv = 2, 200, 150, 4, 2
+    # rows 80-129 and 170-199 are in no slice
+    p = W.make_problem("ws", tq, tk, hq, hkv, d, [((0, 80), (0, 150), W.CAUSAL), ((130, 170), (20, 90), W.FULL)],
+                       seed=11)
+    g = torch.Generator().manual_seed(900 + d)
+    rnd = lambda *s: torch.randn(*s, generator=g).to(dt)
+    host = {"q": rnd(B, tq, hq, d), "k": rnd(B, tk, hkv, d), "v": rnd(B, tk, hkv, d), "out": rnd(B, tq, hq, d),
+            "dout": rnd(B, tq, hq, d)}
+    lse = torch.randn(B, tq, hq, generator=g) * 3.0
+    lse[:, 80:130] = -float("inf")  # no key and no sink; rows 170-199 keep finite values (as with sinks)
+    dev = torch.device("cuda", 0)
+    t = {n: x.to(dev) for n, x in host.items()}
+    t["lse"] = lse.to(dev)
+    for n, like in (("dq", "q"), ("dk", "k"), ("dv", "v")):
+        t[n] = torch.empty_like(t[like])
+    st = {n: (x.stride(0), x.stride(1), x.stride(2)) for n, x in t.items()}
+    plan = ffa.Plan(p.q_ranges, p.k_ranges, p.mask_types, tq, tk, hq, hkv, d, backward=True)
+    ex = ffa.make_extras(None, "sh", cap, total_q=tq, heads_q=hq, dtype=dt)
+    scale = 0.125
+    log(f"workspace L / -Dd: D {d} softcap {cap} fp16 {f16} batch {B}")
+    ffa.run_bwd(plan, t, st, B, scale, ex)
+    torch.cuda.synchronize()
+    ws, nbytes = plan.bwd_workspace(dev, B)
+    w = ws[:nbytes].view(torch.float32).cpu().numpy()
+    half = B * hq * tq
+    lw, dw = w[:half].reshape(B, hq, tq), w[half:].reshape(B, hq, tq)
+    l32 = lse.numpy().astype(np.float32).transpose(0, 2, 1)
+    with np.errstate(invalid="ignore"):
+        if cap:
+            want_l = np.where(l32 == -np.inf, np.float32(np.inf), l32 * np.float32(1.4426950408889634))
+        else:
+            want_l = np.where(l32 == -np.inf, np.float32(-np.inf), -l32 / np.float32(scale))
+    np.testing.assert_array_equal(lw, want_l.astype(np.float32))
+    prod = host["out"].double() * host["dout"].double()
+    dd = prod.sum(-1).numpy().transpose(0, 2, 1)
+    mag = prod.abs().sum(-1).numpy().transpose(0, 2, 1)
+    err = np.abs(-dw.astype(np.float64) - dd)
+    assert (err <= 1e-6 * mag + 1e-30).all(), f"-Dd off by {(err / np.maximum(mag, 1e-30)).max():.2e} of sum|out dout|"
