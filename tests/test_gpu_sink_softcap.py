@@ -177,8 +177,43 @@ def test_backward_sink_softcap(gpu_lib, seed, layout, n, cap):
         allow = 1e-3 * max(np.abs(r).max(), 1e-2)
         log(f"  seed {seed} sink {layout}/{n} cap {cap} {name}: max {err.max():.3e} (torch bf16 {et.max():.3e}) "
             f"mean {err.mean():.3e} (torch bf16 {et.mean():.3e})")
+        if name == "dsink":
+            check_dsink(xn, r, out, lse, dout, sink, lay, p, q, k, v, cap, err, et, allow)
+            continue
         assert err.max() <= 2.0 * et.max() + allow, name
         assert err.mean() <= 2.0 * et.mean() + allow, name
+
+
+def check_dsink(got, ref, out, lse, dout, sink, layout, p, q, k, v, cap, err, et, allow):
+    """d sink = -sum_i exp(sink - lse_i) Dd_i with Dd_i = rowsum(dout_i * out_i) formed from
+    the stored (bf16) out, as the backward defines it (test_dsink_follows_its_definition
+    pins that sum).  PyTorch's autograd reaches the sink gradient without the rounded
+    out, so on some seeds (3 of 100 in a sweep) the kernel's error exceeds twice
+    PyTorch's while being the forward's output rounding carried into Dd.  Accepted when
+    either (a) the same-precision rule holds, or (b) the distance to the oracle stays
+    within the forward's output error propagated through that sum:
+    sum_i exp(sink - lse_i) sum_d |dout_id| |out_id - out_exact_id|."""
+    if err.max() <= 2.0 * et.max() + allow and err.mean() <= 2.0 * et.mean() + allow:
+        return
+    o = out.double().cpu().numpy()
+    l = lse.double().cpu().numpy()
+    do = dout.double().numpy()
+    ref_o, ref_l = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink, sink_layout=layout,
+                                 softcap=cap)
+    sk = sink.double().numpy()
+    if layout == "sh":    # sk [S, Hq]; weights [Tq, S, Hq], gradients summed over rows
+        w_gpu, w_ref = np.exp(sk[None] - l[:, None, :]), np.exp(sk[None] - ref_l[:, None, :])
+        red = lambda x: x.sum(0)
+    else:                 # sk [Tq, S, Hq]; one gradient per row
+        w_gpu, w_ref = np.exp(sk - l[:, None, :]), np.exp(sk - ref_l[:, None, :])
+        red = lambda x: x
+    dd_gpu = (do * o).sum(-1)[:, None, :]
+    term = red(w_gpu * np.abs(dd_gpu)) + 1e-30
+    prop = red(w_ref * (np.abs(do) * np.abs(o - ref_o)).sum(-1)[:, None, :])
+    # the weights themselves move with lse (<= 1e-3 absolute) and the sum with fp32
+    slack = red(np.abs(w_gpu - w_ref) * np.abs(dd_gpu)) + 1e-5 * term
+    log(f"    d sink: error {err.max():.3e} against the propagated output error {prop.max():.3e}")
+    assert (err <= 1.01 * prop + slack).all(), "d sink error beyond the forward's output error"
 
 
 def test_autograd_with_sink_and_cap(gpu_lib):
@@ -207,3 +242,36 @@ def test_head_dim_32_sink_and_cap(gpu_lib):
     out, lse = fwd(gpu_lib, p, q, k, v, sink, "sh", 6.0)
     ref = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink, softcap=6.0)
     check_fwd(out, lse, *ref, "D 32 sink + cap")
+
+
+@pytest.mark.parametrize("layout,d,f16", [("sh", 128, False), ("ssh", 64, False), ("sh", 32, True)])
+def test_dsink_follows_its_definition(gpu_lib, layout, d, f16):
+    # d sink = -sum_i exp(sink - lse_i) * rowsum(dout_i * out_i) (per row for "ssh"),
+    # checked on seeded out / dout / lse / sink (the sum does not need out to be the
+    # forward's), rows that see no key included; fp64 of the same 16-bit values.
+    ffa = gpu_lib
+    dt = torch.float16 if f16 else torch.bfloat16
+    tq, tk, hq, hkv, ns = 300, 200, 4, 2, 3
+    p = W.make_problem("dsink_def", tq, tk, hq, hkv, d,
+                       [((0, 120), (0, 200), W.CAUSAL), ((180, 260), (40, 150), W.FULL)], seed=21)
+    g = torch.Generator().manual_seed(40 + d)
+    q, k, v = (torch.randn(*s_, generator=g).to(dt) for s_ in ((tq, hq, d), (tk, hkv, d), (tk, hkv, d)))
+    out, dout = (torch.randn(tq, hq, d, generator=g).to(dt) for _ in range(2))
+    lse = 2.0 + torch.rand(tq, hq, generator=g) * 3.0
+    sink = torch.randn((ns, hq) if layout == "sh" else (tq, ns, hq), generator=g)
+    dev = torch.device("cuda", 0)
+    res = ffa.flex_flash_attn_bwd(dout.to(dev), q.to(dev), k.to(dev), v.to(dev), out.to(dev), lse.to(dev),
+                                  p.q_ranges, p.k_ranges, p.mask_types, sink=sink.to(dev), sink_layout=layout)
+    torch.cuda.synchronize()
+    got = res[3].double().cpu().numpy()
+    prod = dout.double() * out.double()
+    dd, dd_abs = prod.sum(-1).numpy(), prod.abs().sum(-1).numpy()  # [Tq, Hq]
+    sk, l = sink.double().numpy(), lse.double().numpy()
+    w = np.exp(sk[None] - l[:, None, :]) if layout == "sh" else np.exp(sk - l[:, None, :])
+    terms, scale = w * dd[:, None, :], w * dd_abs[:, None, :]
+    want = -terms.sum(0) if layout == "sh" else -terms
+    mag = scale.sum(0) if layout == "sh" else scale  # fp32 sums are good to a few ulp of this
+    err = np.abs(got - want)
+    log(f"  d sink definition {layout} D {d} fp16 {f16}: max error {err.max():.3e} (of sum |terms| "
+        f"{(err / (mag + 1e-30)).max():.2e})")
+    assert (err <= 2e-5 * mag + 1e-30).all()
