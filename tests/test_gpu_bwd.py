@@ -360,3 +360,40 @@ def test_bwd_workspace_holds_l_and_dd_of_every_row(gpu_lib, d, cap, f16):
     mag = prod.abs().sum(-1).numpy().transpose(0, 2, 1)
     err = np.abs(-dw.astype(np.float64) - dd)
     assert (err <= 1e-6 * mag + 1e-30).all(), f"-Dd off by {(err / np.maximum(mag, 1e-30)).max():.2e} of sum|out dout|"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_flag_attention_layout_random_forward_and_backward(gpu_lib, seed):
+    # FlagAttention's [B, H, M, D] entry point through autograd: batch, GQA, every head
+    # dim, causal (bottom-right) or full, ragged M and N; each batch element against the
+    # oracle (forward bounds, then the same-precision rule for the gradients)
+    from tests.test_gpu_parity import compare as compare_fwd
+
+    rng = np.random.default_rng(93000 + seed)
+    B = int(rng.integers(1, 4))
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    M, N = int(rng.integers(1, 700)), int(rng.integers(1, 700))
+    D = int((16, 32, 64, 128)[seed % 4])
+    causal = bool(rng.integers(0, 2))
+    g = torch.Generator().manual_seed(93000 + seed)
+    q = torch.randn(B, hq, M, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, hkv, N, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, hkv, N, D, generator=g).to(torch.bfloat16)
+    dout = torch.randn(B, hq, M, D, generator=g).to(torch.bfloat16)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (x.to(dev).requires_grad_(True) for x in (q, k, v))
+    what = f"flash_attention {seed} B={B} H=({hq},{hkv}) M={M} N={N} D={D} causal={causal}"
+    log(f"  {what}")
+    out, lse, _, _, _ = gpu_lib.flash_attention(qd, kd, vd, causal=causal, return_log_normalizer=True)
+    (out.float() * dout.to(dev).float()).sum().backward()
+    torch.cuda.synchronize()
+    t = W.CAUSAL if causal else W.FULL
+    for b in range(B):
+        qb, kb, vb, db = (x[b].permute(1, 0, 2).contiguous() for x in (q, k, v, dout))
+        ro, rl = oracle.attend(qb, kb, vb, [[0, M]], [[0, N]], [t])
+        compare_fwd(out[b].detach().permute(1, 0, 2), lse[b].detach().permute(1, 0), ro, rl, what=f"{what} b={b}")
+        p = W.make_problem("flag", M, N, hq, hkv, D, [((0, M), (0, N), t)])
+        refs = oracle.attend_backward(qb, kb, vb, db, p.q_ranges, p.k_ranges, p.mask_types)
+        grads = [x.grad[b].permute(1, 0, 2).cpu() for x in (qd, kd, vd)]
+        compare(grads, refs, f"{what} b={b}", torch_bf16_grads(p, qb, kb, vb, db))

@@ -349,6 +349,27 @@ def test_random_slices_all_mask_types(gpu_lib, seed):
             what=f"random all types {seed} T=({tq},{tk}) H=({hq},{hkv}) D={d} types={p.mask_types.tolist()}")
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_slices_every_head_dim(gpu_lib, seed):
+    # every head dim, GQA ratios up to 8 with three kv heads, all four slice types, sizes
+    # up to 2500 (many tiles and ragged tails) and every split setting
+    rng = np.random.default_rng(91000 + seed)
+    d = int((16, 32, 64, 128)[seed % 4])
+    hkv = int(rng.choice([1, 2, 3]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    tq, tk = int(rng.integers(1, 2500)), int(rng.integers(1, 2500))
+    p = W.random_problem(91000 + seed, tq, tk, hq, hkv, d, n_types=4)
+    q, k, v = W.make_qkv(p)
+    split = int(rng.choice([0, -1, 1, 2, 5]))
+    scale = float(rng.choice([0.0, 0.02]))
+    kw = {"split_tiles": split}
+    if scale:
+        kw["softmax_scale"] = scale
+    out, lse = run(gpu_lib, p, q, k, v, **kw)
+    compare(out, lse, *oracle_ref(p, q, k, v, scale=scale or None),
+            what=f"every D {seed} T=({tq},{tk}) H=({hq},{hkv}) D={d} split={split} slices={p.num_slices}")
+
+
 @pytest.mark.parametrize("w,split", [(1, 0), (200, 0), (513, 0), (513, 3)])
 def test_sliding_window(gpu_lib, w, split):
     T = 3000
