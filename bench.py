@@ -613,7 +613,7 @@ def total_leg(args, p, qd, kd, lse, scale, sink=None):
 
 
 def backward_leg(args, p, qd, kd, vd, out, lse, strides, scale, sink=None):
-    """Time ffa_bwd (preprocess, dQ kernel, dK/dV kernel) on the same workload, with the
+    """Time ffa_bwd (dQ kernel, dK/dV kernel) on the same workload, with the
     forward's out and lse.  FLOPs counted as 10 * D * Hq * visible pairs: the five products
     of the gradient (dP, dV, dQ, dK and the recomputed scores), none of the recomputation."""
     import torch
