@@ -397,3 +397,48 @@ def test_flag_attention_layout_random_forward_and_backward(gpu_lib, seed):
         refs = oracle.attend_backward(qb, kb, vb, db, p.q_ranges, p.k_ranges, p.mask_types)
         grads = [x.grad[b].permute(1, 0, 2).cpu() for x in (qd, kd, vd)]
         compare(grads, refs, f"{what} b={b}", torch_bf16_grads(p, qb, kb, vb, db))
+
+
+def _odd_ratio_problem(seed):
+    # GQA ratios 3, 5, 6 and 7 (query heads per kv head not a power of two) on three
+    # mask families: many tiny documents of random slice types, per-document sliding
+    # windows, and block-sparse masks with small blocks
+    rng = np.random.default_rng(94000 + seed)
+    d = int((16, 32, 64, 128)[seed % 4])
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([3, 5, 6, 7]))
+    kind = seed % 3
+    if kind == 0:
+        T = int(rng.integers(1, 900))
+        cuts, s = [0], 0
+        while s < T:
+            s = min(T, s + int(rng.integers(1, 40)))
+            cuts.append(s)
+        sl = [((a, b), (a, b), int(rng.integers(0, 4))) for a, b in zip(cuts[:-1], cuts[1:])]
+        return W.make_problem(f"tiny{seed}", T, T, hq, hkv, d, sl, seed=94000 + seed)
+    if kind == 1:
+        T = int(rng.integers(1, 1500))
+        docs = sorted(set([0, T] + rng.integers(0, T + 1, size=int(rng.integers(1, 6))).tolist()))
+        return W.sliding_window_problem(T, int(rng.integers(1, 300)), docs, hq, hkv, d, 94000 + seed)
+    T = int(rng.integers(64, 1200))
+    return W.block_sparse_problem(T, int(rng.choice([8, 16, 64])), int(rng.choice([1, 16, 64])),
+                                  float(rng.choice([0.1, 0.5])), hq, hkv, d, 94000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_odd_gqa_ratios_forward(gpu_lib, seed):
+    from tests.test_gpu_parity import compare as compare_fwd, run as run_fwd
+
+    p = _odd_ratio_problem(seed)
+    q, k, v = W.make_qkv(p)
+    split = int(np.random.default_rng(seed).choice([0, -1, 2]))
+    out, lse = run_fwd(gpu_lib, p, q, k, v, split_tiles=split)
+    compare_fwd(out, lse, *oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types),
+                what=f"odd GQA {seed} {p.name} T={p.total_q} H=({p.heads_q},{p.heads_kv}) D={p.head_dim} "
+                     f"slices={p.num_slices} split={split}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_odd_gqa_ratios_backward(gpu_lib, seed):
+    p = _odd_ratio_problem(seed)
+    case(gpu_lib, p, f"odd GQA backward {seed} {p.name} H=({p.heads_q},{p.heads_kv}) D={p.head_dim}")
