@@ -113,7 +113,7 @@ class PlanInfo(ctypes.Structure):
 class AttnExtras(ctypes.Structure):
     """ffa_attn_extras: optional sink logits (and their gradient) and softcap."""
     _fields_ = [("sink", _vp), ("dsink", _vp), ("sink_sb", _i64), ("sink_st", _i64), ("sink_ss", _i64),
-                ("sink_sh", _i64), ("n_sink", _i32), ("softcap", _f32), ("dtype", _i32)]
+                ("sink_sh", _i64), ("n_sink", _i32), ("softcap", _f32), ("dtype", _i32), ("flags", _i32)]
 
 
 # (name, restype, argtypes) of every function in include/ffa.h
@@ -165,7 +165,8 @@ _SIGNATURES = [
     ("ffa_plan_destroy", None, [_vp]),
 ]
 
-ABI_VERSION = 2
+ABI_VERSION = 3
+EXTRAS_ROUNDED_NORM = 1
 PLAN_NATURAL_ORDER = 1
 PLAN_BACKWARD = 2
 
@@ -363,18 +364,19 @@ def _require_bf16_cuda(name, t, ndim, dtype=None):
 
 
 def make_extras(sink=None, sink_layout: str = "sh", softcap: float = 0.0, dsink=None, total_q=None, heads_q=None,
-                dtype=None):
+                dtype=None, rounded_norm: bool = False):
     """ffa_attn_extras for a sink tensor (fp32 device; layout "sh" [S, Hq] or "ssh" [Tq, S, Hq]),
-    a softcap and the element dtype (torch.float16 selects the fp16 kernels); None for plain
-    bfloat16 attention."""
+    a softcap, the element dtype (torch.float16 selects the fp16 kernels) and the forward's
+    rounded-weight normalisation (FFA_EXTRAS_ROUNDED_NORM); None for plain bfloat16 attention."""
     import torch
 
     f16 = dtype == torch.float16
-    if sink is None and not softcap and not f16:
+    if sink is None and not softcap and not f16 and not rounded_norm:
         return None
     ex = AttnExtras()
     ex.softcap = float(softcap or 0.0)
     ex.dtype = 1 if f16 else 0
+    ex.flags = EXTRAS_ROUNDED_NORM if rounded_norm else 0
     if sink is not None:
         if not isinstance(sink, torch.Tensor) or sink.dtype != torch.float32 or not sink.is_cuda:
             raise TypeError("sink must be a float32 device tensor")
@@ -455,7 +457,8 @@ def run_combine(plan: Plan, out, lse, strides, batch: int, extras=None):
 
 def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
                         softmax_scale: Optional[float] = None, softcap: float = 0.0,
-                        plan: Optional[Plan] = None, split_tiles: int = 0, sink_layout: str = "sh"):
+                        plan: Optional[Plan] = None, split_tiles: int = 0, sink_layout: str = "sh",
+                        rounded_norm: bool = False):
     """Forward of flexible-mask attention on packed THD tensors -> (out, lse).
 
     q [Tq,Hq,D], k/v [Tk,Hkv,D] bf16 or fp16 device tensors (head_dim contiguous);
@@ -465,7 +468,9 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
     ("sh") or [Tq, S_sink, Hq] ("ssh") that join each row's softmax denominator
     without a value; softcap > 0 maps a scaled score s to softcap*tanh(s/softcap).
     Returns out [Tq,Hq,D] bf16 and lse [Tq,Hq] fp32 (natural log, sinks included;
-    -inf and a zero output for rows that see no key and no sink).
+    -inf and a zero output for rows that see no key and no sink).  rounded_norm: divide
+    out by the sum of the 16-bit rounded weights its P.V uses (a convex combination of
+    value rows; ~6-9% slower), see FFA_EXTRAS_ROUNDED_NORM.
     """
     import torch
 
@@ -493,7 +498,7 @@ def flex_flash_attn_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, sink=None,
         "out": (0, out.stride(0), out.stride(1)),
         "lse": (0, lse.stride(0), lse.stride(1)),
     }
-    ex = make_extras(sink, sink_layout, softcap, total_q=tq, heads_q=hq, dtype=q.dtype)
+    ex = make_extras(sink, sink_layout, softcap, total_q=tq, heads_q=hq, dtype=q.dtype, rounded_norm=rounded_norm)
     run_fwd(plan, q, k, v, out, lse, strides, 1, scale, ex)
     return out, lse
 

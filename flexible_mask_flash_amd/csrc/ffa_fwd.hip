@@ -132,6 +132,16 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? ((r & 3) << 2) : D == 64 ? (((r >> 1) & 1) << 2) : 0;
 }
 
+// c + a.x + a.y of a 16-bit pair (one dot-product instruction against (1, 1))
+template <typename T>
+__device__ __forceinline__ float dot2_ones(typename ElemT<T>::v2 a, float c) {
+  const typename ElemT<T>::v2 ones = {(T)1.0f, (T)1.0f};
+  if constexpr (std::is_same<T, _Float16>::value)
+    return __builtin_amdgcn_fdot2(a, ones, c, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(a, ones, c, false);
+}
+
 // Waves per SIMD the compiler budgets registers for: two at D = 128 (256 VGPRs), more
 // below, where O and the fragments shrink but the per-score softmax work does not, so a
 // third or fourth wave hides more of it (+4.5% at D = 64 with three, +4 to +6% at
@@ -139,7 +149,10 @@ __device__ __forceinline__ int swz_v(int r) {
 template <int D>
 constexpr int kFwdWaves = D <= 32 ? 4 : D <= 64 ? 3 : 2;
 
-template <int D, bool CAP, typename T>
+// RN: out is divided by the sum of the 16-bit rounded weights that P V multiplies
+// (lse keeps the sum of the fp32 weights), so the output is a convex combination of
+// value rows up to fp32 accumulation (FFA_EXTRAS_ROUNDED_NORM).
+template <int D, bool CAP, bool RN, typename T>
 __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_eu(kFwdWaves<D>, kFwdWaves<D>))) void ffa_fwd_main(FwdArgs a) {
   using V8 = typename ElemT<T>::v8;
   using V4 = typename ElemT<T>::v4;
@@ -221,6 +234,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     for (int i = 0; i < 16; ++i) o[d][i] = 0.0f;
   float m_run = -INFINITY;  // running max, log2 units (already scaled)
   float l_run = 0.0f;       // this lane's part of the row sum
+  float lr_run = 0.0f;      // RN: the same sum of the rounded weights
 
   // ---- per-lane LDS read addresses (the low 10 bits of the LDS base are zero)
   const uint32_t lds = (uint32_t)(uintptr_t)(FFA_LDS char*)smem;
@@ -503,6 +517,7 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         m_run = m_new;
         l_run *= alpha;
+        if constexpr (RN) lr_run *= alpha;
 #pragma unroll
         for (int d = 0; d < DBLK; ++d)
 #pragma unroll
@@ -519,6 +534,19 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
         }
       }
       l_run += ps;
+      // RN: the sum of the rounded weights, formed between the P V MFMAs (the K Q^T
+      // section's VALU slots are taken by the exponentials)
+      float pr_s = 0.0f;
+      auto rs_hook = [&](auto slot_tag) {
+        if constexpr (RN) {
+          constexpr int sl = decltype(slot_tag)::value;
+          constexpr int PPS = 16 / (4 * DBLK);
+#pragma unroll
+          for (int q = sl * PPS; q < (sl + 1) * PPS; ++q)
+            pr_s = dot2_ones<T>(__builtin_bit_cast(V2, pu[q]), pr_s);
+          fence(pr_s);
+        }
+      };
       V8 pf[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -539,12 +567,14 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
           prep(na, nb, sl * EPP, (sl + 1) * EPP);
           fence(na);
           fence(nb);
+          rs_hook(slot_tag);
         });
         tA = tB;
         tile_next(tB, rp, n_runs);
       } else {
-        pv(std::integral_constant<int, P>{}, pf, [](auto) {});
+        pv(std::integral_constant<int, P>{}, pf, rs_hook);
       }
+      if constexpr (RN) lr_run += pr_s;
     };
 
     // steady state: pairs of iterations that both have a next tile
@@ -569,7 +599,8 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
   const FFA_CONST FwdArgs* ea = (const FFA_CONST FwdArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+s"(ea));
   const float lsum = partner_sum(l_run);
-  float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  const float lnorm = RN ? partner_sum(lr_run) : lsum;  // what out is divided by
+  float inv = lsum > 0.0f ? 1.0f / lnorm : 0.0f;
   float lse_v = lsum > 0.0f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
   const int n_sink = ea->n_sink;
   if (n_sink > 0 && slot < 0 && row_ok) {
@@ -582,9 +613,13 @@ __global__ __launch_bounds__(64 * ffa::kWaves) __attribute__((amdgpu_waves_per_e
     const float mt = fmaxf(mk, ms);
     if (mt != -INFINITY) {
       const float fk = __builtin_amdgcn_exp2f(mk - mt);  // 0 when the row sees no key
-      float lt = lsum * fk;
-      for (int s = 0; s < n_sink; ++s) lt += __builtin_amdgcn_exp2f(sp[s * ss] * kLog2e - mt);
-      inv = fk / lt;
+      float lt = lsum * fk, ln = lnorm * fk;
+      for (int s = 0; s < n_sink; ++s) {
+        const float e = __builtin_amdgcn_exp2f(sp[s * ss] * kLog2e - mt);
+        lt += e;
+        if constexpr (RN) ln += e;
+      }
+      inv = fk / (RN ? ln : lt);
       lse_v = (mt + __log2f(lt)) * kLn2;
     }
   }
@@ -988,6 +1023,8 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
   fa.sk_sb = ex.sink_sb; fa.sk_st = ex.sink_st; fa.sk_ss = ex.sink_ss; fa.sk_sh = ex.sink_sh;
   fa.n_sink = ex.n_sink;
 
+  const bool rn = (ex.flags & FFA_EXTRAS_ROUNDED_NORM) != 0;
+
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)((int64_t)p.num_items * batch));
   const dim3 blk(64 * ffa::kWaves);
@@ -995,8 +1032,13 @@ ffa_status ffa_fwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
     dispatch_dtype(ex.dtype, [&](auto t_tag) {
       constexpr int D = decltype(d_tag)::value;
       using T = decltype(t_tag);
-      if (cap) hipLaunchKernelGGL((ffa_fwd_main<D, true, T>), grid, blk, 0, s, fa);
-      else hipLaunchKernelGGL((ffa_fwd_main<D, false, T>), grid, blk, 0, s, fa);
+      if (rn) {
+        if (cap) hipLaunchKernelGGL((ffa_fwd_main<D, true, true, T>), grid, blk, 0, s, fa);
+        else hipLaunchKernelGGL((ffa_fwd_main<D, false, true, T>), grid, blk, 0, s, fa);
+      } else {
+        if (cap) hipLaunchKernelGGL((ffa_fwd_main<D, true, false, T>), grid, blk, 0, s, fa);
+        else hipLaunchKernelGGL((ffa_fwd_main<D, false, false, T>), grid, blk, 0, s, fa);
+      }
     });
   });
   hipError_t e = hipGetLastError();

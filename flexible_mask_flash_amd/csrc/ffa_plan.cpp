@@ -247,6 +247,7 @@ ffa_status check_extras(const ffa_attn_extras* ex, bool has_rows) {
   if (ex->dtype != FFA_DTYPE_BF16 && ex->dtype != FFA_DTYPE_F16)
     return set_error(FFA_ERR_ARG, "dtype must be FFA_DTYPE_BF16 or FFA_DTYPE_F16");
   if (ex->n_sink > 65536) return set_error(FFA_ERR_ARG, "n_sink must be at most 65536");
+  if (ex->flags & ~FFA_EXTRAS_ROUNDED_NORM) return set_error(FFA_ERR_ARG, "unknown bits in extras flags");
   if (ex->n_sink > 0 && has_rows && !ex->sink) return set_error(FFA_ERR_NULL, "n_sink > 0 but sink is NULL");
   return FFA_OK;
 }

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FFA_ABI_VERSION 2
+#define FFA_ABI_VERSION 3
 
 #define FFA_MASK_FULL 0
 #define FFA_MASK_CAUSAL 1
@@ -103,7 +103,15 @@ typedef enum {
  * h*sink_sh] (sink_st = 0: the same logits for every row).  ffa_bwd writes
  * d sink to dsink with the same strides when dsink is not NULL (summed over
  * rows when sink_st == 0, in a fixed order).
+ * flags: 0 or FFA_EXTRAS_ROUNDED_NORM (any other bit: FFA_ERR_ARG).  With it the
+ * forward divides each row's output by the sum of the 16-bit rounded weights
+ * that its P.V product multiplies, instead of the sum of their fp32 values (lse
+ * still comes from the fp32 sum): out is then a convex combination of value rows
+ * up to fp32 accumulation, which keeps a row dominated by one key met past the
+ * row's first key tile within the output's own rounding (default: within that
+ * plus up to 2^-9 of the value row).  About 6-9% slower.  ffa_bwd ignores it.
  */
+#define FFA_EXTRAS_ROUNDED_NORM 1
 typedef struct {
   const float* sink;
   float* dsink;
@@ -112,6 +120,7 @@ typedef struct {
   float softcap;    /* 0: off; must be finite and >= 0 */
   int32_t dtype;    /* element type of q, k, v, out, dout and the gradients:
                        FFA_DTYPE_BF16 (0, also when extras is NULL) or FFA_DTYPE_F16 */
+  int32_t flags;    /* 0 or FFA_EXTRAS_ROUNDED_NORM (forward only) */
 } ffa_attn_extras;
 
 /* Opaque host plan; immutable after ffa_plan, safe to share between threads. */

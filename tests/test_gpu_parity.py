@@ -283,6 +283,47 @@ def test_peaky_softmax_within_twice_same_precision(gpu_lib, seed, tq, tk, hq, hk
     assert lerr <= LSE_ABS
 
 
+@pytest.mark.parametrize("seed,tq,tk,hq,hkv,d,split", [(92365, 1924, 1315, 2, 1, 128, 2),
+                                                       (92385, 1513, 2446, 8, 1, 128, -1),
+                                                       (91569, 675, 1694, 24, 3, 64, 2)])
+def test_rounded_norm_keeps_peaky_rows_within_the_fixed_bound(gpu_lib, seed, tq, tk, hq, hkv, d, split):
+    # The same peaked problems with FFA_EXTRAS_ROUNDED_NORM: out divided by the sum of the
+    # rounded weights its P V used, so the dominant value row is kept up to the output's
+    # own rounding and the fixed bounds hold; lse comes from the same fp32 sum as without it.
+    p = W.random_problem(seed, tq, tk, hq, hkv, d, n_types=4)
+    q, k, v = W.make_qkv(p)
+    out, lse = run(gpu_lib, p, q, k, v, split_tiles=split, softmax_scale=0.4, rounded_norm=True)
+    compare(out, lse, *oracle_ref(p, q, k, v, scale=0.4), what=f"rounded norm, peaky {seed} D={d} split={split}")
+    _, lse0 = run(gpu_lib, p, q, k, v, split_tiles=split, softmax_scale=0.4)
+    assert torch.equal(lse, lse0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_rounded_norm_random(gpu_lib, seed):
+    # rounded-weight normalisation across head dims, GQA, all slice types, split-K, sinks
+    # (which join the divisor) and fp16
+    rng = np.random.default_rng(95000 + seed)
+    d = int((16, 32, 64, 128)[seed % 4])
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    tq, tk = int(rng.integers(1, 1200)), int(rng.integers(1, 1200))
+    p = W.random_problem(95000 + seed, tq, tk, hq, hkv, d, n_types=4)
+    f16 = seed in (3, 6)
+    q, k, v = W.make_qkv(p, dtype=torch.float16 if f16 else None)
+    split = int(rng.choice([0, -1, 2]))
+    sink = None
+    if seed % 2:
+        sink = torch.randn((2, hq), generator=torch.Generator().manual_seed(seed)) * 2.0
+    dev = torch.device("cuda", 0)
+    out, lse = gpu_lib.flex_flash_attn_fwd(q.to(dev), k.to(dev), v.to(dev), p.q_ranges, p.k_ranges, p.mask_types,
+                                           sink=sink.to(dev) if sink is not None else None, split_tiles=split,
+                                           rounded_norm=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, sink=sink)
+    compare(out, lse, ro, rl, what=f"rounded norm {seed} T=({tq},{tk}) H=({hq},{hkv}) D={d} split={split} "
+                                   f"sink={sink is not None} fp16={f16}")
+
+
 # ---------------------------------------------------------------- properties
 
 def test_bitwise_deterministic(gpu_lib):

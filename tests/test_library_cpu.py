@@ -48,8 +48,18 @@ def test_exports_every_declared_function(lib):
     assert set(names) == bound, "binding and header disagree"
 
 
+def test_extras_layout_matches_the_header():
+    # ffa_attn_extras as include/ffa.h declares it (the binding's ctypes mirror): two
+    # pointers, four int64 strides, n_sink, softcap, dtype and flags
+    import ctypes as ct
+    assert ct.sizeof(ffa.AttnExtras) == 2 * 8 + 4 * 8 + 4 * 4
+    assert [f[0] for f in ffa.AttnExtras._fields_] == ["sink", "dsink", "sink_sb", "sink_st", "sink_ss", "sink_sh",
+                                                       "n_sink", "softcap", "dtype", "flags"]
+    assert ffa.EXTRAS_ROUNDED_NORM == 1
+
+
 def test_abi_version_and_status_strings(lib):
-    assert lib.ffa_abi_version() == 2
+    assert lib.ffa_abi_version() == 3
     for code in range(12):
         assert lib.ffa_status_string(code).decode() not in ("", "unknown status")
     assert lib.ffa_status_string(99).decode() == "unknown status"
@@ -356,6 +366,9 @@ def test_fwd_rejects_bad_arguments_without_launching(lib):
     assert call(ex=ctypes.byref(ex)) == 11
     ex.n_sink, ex.dtype, ex.sink = 70000, 0, fake  # too many sink logits
     assert call(ex=ctypes.byref(ex)) == 11
+    ex.n_sink, ex.sink, ex.flags = 0, None, 2  # unknown flag bit
+    assert call(ex=ctypes.byref(ex)) == 11
+    assert "flags" in lib.ffa_last_error().decode()
     # a split plan without workspace
     ps = ffa.Plan([[0, 32]], [[0, 8192]], [0], 32, 8192, 4, 1, 128, num_cus=NCU, split_tiles=16)
     assert ps.info["workspace_bytes"] > 0
