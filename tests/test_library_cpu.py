@@ -452,3 +452,18 @@ def test_head_groups_of_a_kv_head_share_a_dispatch_lane():
     # every (q tile, head group) pair appears exactly once
     pairs = {(int(a), int(b)) for a, b in zip(m["items"][:, 0], m["items"][:, 2])}
     assert len(pairs) == len(kv) == (4096 // 32) * 16
+
+
+def test_make_extras_fields():
+    # the binding's extras builder: None for plain bf16 attention, the dtype code for fp16,
+    # and the rounded-weight flag (no device tensors needed for these fields)
+    import torch
+
+    assert ffa.make_extras() is None
+    assert ffa.make_extras(dtype=torch.bfloat16) is None
+    ex = ffa.make_extras(dtype=torch.float16)
+    assert ex.dtype == 1 and ex.flags == 0 and ex.n_sink == 0
+    ex = ffa.make_extras(rounded_norm=True)
+    assert ex.flags == ffa.EXTRAS_ROUNDED_NORM and ex.dtype == 0 and ex.softcap == 0.0
+    ex = ffa.make_extras(softcap=5.0, rounded_norm=True, dtype=torch.float16)
+    assert (ex.flags, ex.dtype, ex.softcap) == (1, 1, 5.0)
