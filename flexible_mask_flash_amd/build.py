@@ -36,6 +36,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libffa.so)")
 
 
+def asm_command(src: str, out_path: str) -> list:
+    """hipcc command writing the gfx950 device assembly of a .hip source, with the flags
+    the library is built with."""
+    common = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
+    return [hipcc(), *common, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-S",
+            os.path.join(CSRC, src), "-o", out_path]
+
+
 def build(verbose: bool = False, asm: bool = False) -> str:
     """Compile every source and link libffa.so; returns the library path."""
     cc = hipcc()
@@ -56,9 +64,7 @@ def build(verbose: bool = False, asm: bool = False) -> str:
         jobs.append(cmd)
         objs.append(obj)
         if asm and src.endswith(".hip"):
-            s_out = os.path.join(bdir, src + f".{ARCH}.s")
-            jobs.append([cc, *common, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-S", path, "-o",
-                         s_out])
+            jobs.append(asm_command(src, os.path.join(bdir, src + f".{ARCH}.s")))
     # the sources compile independently
     with ThreadPoolExecutor(max_workers=min(len(jobs), 4)) as ex:
         for f in [ex.submit(_run, cmd, verbose) for cmd in jobs]:
