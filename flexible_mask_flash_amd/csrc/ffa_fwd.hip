@@ -24,6 +24,10 @@
 //     key row so that both the K row reads and the V transposed reads are
 //     free of bank conflicts.
 //   * causal / ragged edges are masked only on tiles past the item's n_full.
+//   * out is divided by the row sum of the fp32 probabilities, or, with
+//     FFA_EXTRAS_ROUNDED_NORM, by the sum of the 16-bit rounded ones that P V
+//     multiplies (a second sum, 16 dot-product instructions per tile); lse
+//     always comes from the fp32 sum.
 //   * the epilogue writes bf16 out and fp32 lse, or -- for split items --
 //     fp32 partial (out, lse) that ffa_combine merges with a global logsumexp
 //     (FlagAttention user guide, "Split-KV and paged attention").
