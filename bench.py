@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--total", action="store_true", help="also time the total-attention pass")
     ap.add_argument("--fp16", action="store_true", help="float16 inputs and outputs instead of bfloat16")
     ap.add_argument("--sinks", type=int, default=0, help="sink logits per head (layout sh; 0: none)")
+    ap.add_argument("--rounded-norm", action="store_true",
+                    help="forward legs with FFA_EXTRAS_ROUNDED_NORM (out divided by the sum of the rounded weights)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
@@ -365,7 +367,8 @@ def main():
     if args.sinks > 0:
         g = torch.Generator().manual_seed(17)
         sink = torch.randn((args.sinks, p.heads_q), generator=g, dtype=torch.float32).to(dev)
-    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q, dtype=qd.dtype)
+    extras = ffa.make_extras(sink, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q, dtype=qd.dtype,
+                             rounded_norm=args.rounded_norm)
 
     def step():
         ffa.run_fwd(plan, qd, kd, vd, out, lse, strides, 1, scale, extras)
@@ -430,6 +433,7 @@ def main():
             "split_tiles": args.split_tiles,
             "softcap": args.softcap,
             "sinks": args.sinks,
+            "rounded_norm": args.rounded_norm,
         },
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_median": round(med, 4),
@@ -487,7 +491,8 @@ def also_leg(args, name: str):
     strides = {"q": (0, qd.stride(0), qd.stride(1)), "k": (0, kd.stride(0), kd.stride(1)),
                "v": (0, vd.stride(0), vd.stride(1)), "out": (0, out.stride(0), out.stride(1)),
                "lse": (0, lse.stride(0), lse.stride(1))}
-    extras = ffa.make_extras(None, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q, dtype=qd.dtype)
+    extras = ffa.make_extras(None, "sh", args.softcap, total_q=p.total_q, heads_q=p.heads_q, dtype=qd.dtype,
+                             rounded_norm=args.rounded_norm)
     scale = 1.0 / math.sqrt(p.head_dim)
 
     def step():
