@@ -27,8 +27,8 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-f
 # compiler gives every MFMA of a one-wave-per-SIMD kernel an AGPR destination and
 # then copies each score out and back (v_accvgpr_read / write around every exp2).
 # The backward also takes the max-ILP machine scheduler: the same instructions and results
-# (bitwise), +0.2 to +1.9% on the backward workloads in same-process A/B runs; the forward
-# measured slower with it (-0.1 to -1.1%) and keeps the default.
+# (bitwise), +0.2 to +1.9% on the D >= 64 backward workloads in same-process A/B runs (-3% at
+# D = 32 and 16); the forward measured slower with it (-0.1 to -1.1%) and keeps the default.
 SOURCE_FLAGS = {"ffa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
