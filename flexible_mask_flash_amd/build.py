@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libffa.so")
 ARCH = "gfx950"
 
-SOURCES = ["ffa_plan.cpp", "ffa_fwd.hip", "ffa_bwd.hip"]
+SOURCES = ["ffa_plan.cpp", "ffa_fwd.hip", "ffa_bwd.hip", "ffa_bwd_small.hip"]
 
 # Packed fp32 VALU ops are disabled: the compiler must not form v_pk_{add,mul,fma}_f32.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans"]
@@ -26,10 +26,16 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-f
 # dS) directly, so their MFMAs must write arch VGPRs: left to its heuristic, the
 # compiler gives every MFMA of a one-wave-per-SIMD kernel an AGPR destination and
 # then copies each score out and back (v_accvgpr_read / write around every exp2).
-# The backward also takes the max-ILP machine scheduler: the same instructions and results
-# (bitwise), +0.2 to +1.9% on the D >= 64 backward workloads in same-process A/B runs (-3% at
-# D = 32 and 16); the forward measured slower with it (-0.1 to -1.1%) and keeps the default.
-SOURCE_FLAGS = {"ffa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# The backward's D >= 64 kernels also take the max-ILP machine scheduler: the same
+# instructions and results (bitwise), +0.2 to +1.9% on the D >= 64 backward workloads in
+# same-process A/B runs; at D = 32 and 16 it measured -3%, so those instances are compiled
+# in ffa_bwd_small.hip under the default scheduler.  The forward measured slower with it
+# (-0.1 to -1.1%) and keeps the default.
+_BWD_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCE_FLAGS = {
+    "ffa_bwd.hip": _BWD_FLAGS + ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "ffa_bwd_small.hip": _BWD_FLAGS,
+}
 
 
 def hipcc() -> str:

@@ -43,7 +43,10 @@
 
 #include "ffa_device.h"
 
-namespace {
+// A named namespace: the D <= 32 instances of ffa_bwd_main are compiled in
+// ffa_bwd_small.hip (which includes this file with FFA_BWD_KERNELS_ONLY set), with
+// other scheduler flags, and must be the same entities in both objects.
+namespace ffa::bwd {
 
 using namespace ffa::dev;
 using ffa::kBlockN;
@@ -115,6 +118,7 @@ __device__ __forceinline__ float tanh_from_2ylog2e(float z) {
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
+#ifndef FFA_BWD_KERNELS_ONLY
 // d sink[b, s, h] = -sum_i exp(sink - lse[i,h]) Dd[i,h]   (shared logits, sink_st == 0)
 // d sink[b, i, s, h] = -exp(sink[i] - lse[i,h]) Dd[i,h]     (per-row logits)
 // One workgroup per (sink, head, batch element); the sum runs in a fixed order.
@@ -138,6 +142,7 @@ __global__ __launch_bounds__(256) void ffa_bwd_dsink(SinkArgs a) {
   __syncthreads();
   if (threadIdx.x == 0) *dp = (part[0] + part[1]) + (part[2] + part[3]);
 }
+#endif  // FFA_BWD_KERNELS_ONLY
 
 // -Dd[b,h,t] with Dd = sum_d dO[b,t,h,d] O[b,t,h,d] (fp32 from the bf16 values), and
 // L[b,h,t] = -lse / scale (fold) or lse * log2 e: either way a row that sees no key
@@ -875,7 +880,26 @@ __global__ __launch_bounds__((64 * kBwdWgWaves<D, KV, TOT>)) __attribute__((amdg
   }
 }
 
-}  // namespace
+}  // namespace ffa::bwd
+
+#ifndef FFA_BWD_KERNELS_ONLY
+using namespace ffa::bwd;
+
+// Compiled in ffa_bwd_small.hip: the instances for D = 16 and 32.
+#define FFA_BWD_SMALL(D, T)                                                \
+  extern template __global__ void ffa_bwd_main<D, false, false, false, T>(BwdArgs); \
+  extern template __global__ void ffa_bwd_main<D, false, true, false, T>(BwdArgs);  \
+  extern template __global__ void ffa_bwd_main<D, true, false, false, T>(BwdArgs);  \
+  extern template __global__ void ffa_bwd_main<D, true, true, false, T>(BwdArgs);   \
+  extern template __global__ void ffa_bwd_main<D, true, false, true, T>(BwdArgs);   \
+  extern template __global__ void ffa_bwd_main<D, true, true, true, T>(BwdArgs);
+namespace ffa::bwd {
+FFA_BWD_SMALL(16, __bf16)
+FFA_BWD_SMALL(16, _Float16)
+FFA_BWD_SMALL(32, __bf16)
+FFA_BWD_SMALL(32, _Float16)
+}  // namespace ffa::bwd
+#undef FFA_BWD_SMALL
 
 static ffa_status hip_fail_b(hipError_t e, const char* what) {
   return ffa::set_error(FFA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -1132,3 +1156,5 @@ ffa_status ffa_bwd(ffa_plan_t plan, const void* d_meta, int32_t batch, const voi
 }
 
 }  // extern "C"
+
+#endif  // FFA_BWD_KERNELS_ONLY

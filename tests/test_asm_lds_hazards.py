@@ -108,14 +108,14 @@ def test_checker_flags_a_read_used_before_its_wait():
 
 
 def test_kernels_never_touch_an_asm_lds_read_before_its_wait(tmp_path):
-    srcs = ["ffa_fwd.hip", "ffa_bwd.hip"]
+    srcs = [s for s in build.SOURCES if s.endswith(".hip")]
     outs = [str(tmp_path / (s + ".s")) for s in srcs]
 
     def run(cmd):
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
 
-    with ThreadPoolExecutor(max_workers=2) as ex:
+    with ThreadPoolExecutor(max_workers=3) as ex:
         list(ex.map(run, [build.asm_command(s, o) for s, o in zip(srcs, outs)]))
     n_kernels, bad = 0, []
     for path in outs:
