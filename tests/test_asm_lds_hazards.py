@@ -4,7 +4,7 @@ The forward and backward kernels read LDS through inline asm (`ds_read_b128`,
 `ds_read_b64_tr_b16`) and wait for the results with explicit `s_waitcnt lgkmcnt(N)`.
 The compiler takes an asm output as written when the asm statement ends, so it may
 copy, spill or reuse that register while the read is still in flight; only the
-kernel's own waits keep that from happening.  This test compiles both sources to
+kernel's own waits keep that from happening.  This test compiles every .hip source to
 device assembly with the library's flags and walks every kernel:
 
 - an asm LDS read is complete once `lgkmcnt(N)` has been waited with at least N LDS
@@ -107,9 +107,12 @@ def test_checker_flags_a_read_used_before_its_wait():
     assert len(lds_asm_hazards(late)) == 1
 
 
-def test_kernels_never_touch_an_asm_lds_read_before_its_wait(tmp_path):
+@pytest.fixture(scope="module")
+def device_asm(tmp_path_factory):
+    """{source: gfx950 assembly text} of every .hip source, built with the library's flags."""
+    tmp = tmp_path_factory.mktemp("asm")
     srcs = [s for s in build.SOURCES if s.endswith(".hip")]
-    outs = [str(tmp_path / (s + ".s")) for s in srcs]
+    outs = [str(tmp / (s + ".s")) for s in srcs]
 
     def run(cmd):
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -117,10 +120,29 @@ def test_kernels_never_touch_an_asm_lds_read_before_its_wait(tmp_path):
 
     with ThreadPoolExecutor(max_workers=3) as ex:
         list(ex.map(run, [build.asm_command(s, o) for s, o in zip(srcs, outs)]))
+    return {s: open(o).read() for s, o in zip(srcs, outs)}
+
+
+def test_kernels_never_touch_an_asm_lds_read_before_its_wait(device_asm):
     n_kernels, bad = 0, []
-    for path in outs:
-        for name, body in _kernels(open(path).read()):
+    for src, text in device_asm.items():
+        for name, body in _kernels(text):
             n_kernels += 1
-            bad += [(os.path.basename(path), name, f) for f in lds_asm_hazards(body)]
+            bad += [(src, name, f) for f in lds_asm_hazards(body)]
     assert n_kernels >= 40
     assert not bad, bad[:5]
+
+
+def test_backward_main_kernels_are_split_between_the_two_objects(device_asm):
+    """ffa_bwd.hip (max-ILP scheduler) holds the D = 64 and 128 instances of ffa_bwd_main
+    and declares the D = 16 and 32 ones extern; ffa_bwd_small.hip compiles those.  Each of
+    the 48 instances (4 head dims x 2 element types x dQ, dK/dV, total attention, each
+    with and without the soft cap) must be in exactly one object, the one of its head dim."""
+    def mains(src):
+        names = [n for n, _ in _kernels(device_asm[src]) if "ffa_bwd_main" in n]
+        return {n: int(re.search(r"ffa_bwd_mainILi(\d+)E", n).group(1)) for n in names}
+
+    big, small = mains("ffa_bwd.hip"), mains("ffa_bwd_small.hip")
+    assert sorted(set(big.values())) == [64, 128] and len(big) == 24
+    assert sorted(set(small.values())) == [16, 32] and len(small) == 24
+    assert not set(big) & set(small)
