@@ -275,3 +275,44 @@ def test_dsink_follows_its_definition(gpu_lib, layout, d, f16):
     log(f"  d sink definition {layout} D {d} fp16 {f16}: max error {err.max():.3e} (of sum |terms| "
         f"{(err / (mag + 1e-30)).max():.2e})")
     assert (err <= 2e-5 * mag + 1e-30).all()
+
+
+@pytest.mark.parametrize("cap", [0.0, 6.0])
+@pytest.mark.parametrize("f16", [False, True])
+@pytest.mark.parametrize("d", [16, 32])
+def test_small_head_dims_every_backward_instance(gpu_lib, d, f16, cap):
+    # The D = 16 and 32 backward kernels live in an object of their own; together these
+    # eight cases launch each of them once: dQ, dK/dV and total attention, for bf16 and
+    # fp16, with and without the soft cap.  Gradients: the same-precision rule against
+    # the fp64 oracle; total attention: 1e-3 relative.
+    from tests.test_gpu_total import check_total
+
+    dt = torch.float16 if f16 else torch.bfloat16
+    seed = 3100 + 8 * (d == 32) + 4 * f16 + 2 * (cap > 0)
+    rng = np.random.default_rng(seed)
+    tq, tk = int(rng.integers(150, 400)), int(rng.integers(150, 400))
+    p = W.random_problem(seed, tq, tk, 4, 2, d, n_types=4)
+    q, k, v = W.make_qkv(p, dtype=dt)
+    q = q * 3 if cap else q
+    dout = W.make_dout(p, dtype=dt)
+    what = f"D {d} {'fp16' if f16 else 'bf16'} cap {cap}"
+    log(f"  {what}: Tq {tq} Tk {tk} slices {p.num_slices}")
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dd = q.to(dev), k.to(dev), v.to(dev), dout.to(dev)
+    out, lse = gpu_lib.flex_flash_attn_fwd(qd, kd, vd, p.q_ranges, p.k_ranges, p.mask_types, softcap=cap)
+    g = gpu_lib.flex_flash_attn_bwd(dd, qd, kd, vd, out, lse, p.q_ranges, p.k_ranges, p.mask_types, softcap=cap)
+    tot = gpu_lib.flex_total_attention(qd, kd, lse, p.q_ranges, p.k_ranges, p.mask_types, softcap=cap)
+    torch.cuda.synchronize()
+    assert all(x.dtype == dt for x in g)
+    ref = oracle.attend_backward(q, k, v, dout, p.q_ranges, p.k_ranges, p.mask_types, softcap=cap)
+    tb = torch_bf16_grads(p, q, k, v, dout, None, "sh", cap)
+    for name, x, r, t in zip(("dq", "dk", "dv"), g, ref, tb):
+        xn = x.double().cpu().numpy()
+        assert not np.isnan(xn).any(), name
+        err, et = np.abs(xn - r), np.abs(t - r)
+        allow = 1e-3 * max(np.abs(r).max(), 1e-2)
+        log(f"  {what} {name}: max {err.max():.3e} (same precision {et.max():.3e}) "
+            f"mean {err.mean():.3e} (same precision {et.mean():.3e})")
+        assert err.max() <= 2.0 * et.max() + allow, name
+        assert err.mean() <= 2.0 * et.mean() + allow, name
+    check_total(tot, oracle.total_attention(q, k, p.q_ranges, p.k_ranges, p.mask_types, softcap=cap), what)
