@@ -33,9 +33,10 @@ def test_block_sparse_backward(gpu_lib, qb, kb):
     p = W.block_sparse_problem(512, qb, kb, 0.25, 4, 2, 64, seed=qb * 1000 + kb + 1)
     q, k, v = W.make_qkv(p)
     dout = W.make_dout(p)
-    grads = run_bwd(gpu_lib, p, q, k, v, dout)
+    grads, out = run_bwd(gpu_lib, p, q, k, v, dout, return_out=True)
     refs = oracle.attend_backward(q, k, v, dout, p.q_ranges, p.k_ranges, p.mask_types)
-    compare_grads(grads, refs, f"block sparse q{qb} k{kb}", torch_bf16_grads(p, q, k, v, dout))
+    compare_grads(grads, refs, f"block sparse q{qb} k{kb}", torch_bf16_grads(p, q, k, v, dout),
+                  stored=(p, q, k, v, dout, out, None))
 
 
 @pytest.mark.parametrize("name", ["block_sparse", "block_sparse_k16", "block_sparse_q16"])

@@ -16,6 +16,12 @@ tolerance relative to the gradient's own size alone would not be meaningful
 there; where PyTorch cannot run the case (full sizes) the bound is
 max-abs <= 2e-2 * max|ref| and mean-abs <= 1e-2 * mean|ref|, on workloads
 where the gradients do not cancel.
+
+Where the same-precision rule fails for dq or dk, the case is judged elementwise
+by stored_out_bounds: like every flash-attention backward, the kernel forms
+Dd = rowsum(dout * out) from the stored 16-bit output, which PyTorch's autograd
+never sees, so the forward's output rounding reaches dS; on a key seen by one or
+two rows nothing averages it out.
 """
 import sys
 
@@ -36,14 +42,52 @@ def log(*a):
     sys.stdout.flush()
 
 
-def run_bwd(ffa, p, q, k, v, dout, scale=None):
+def run_bwd(ffa, p, q, k, v, dout, scale=None, return_out=False):
     dev = torch.device("cuda", 0)
     qd, kd, vd, dd = q.to(dev), k.to(dev), v.to(dev), dout.to(dev)
     out, lse = ffa.flex_flash_attn_fwd(qd, kd, vd, p.q_ranges, p.k_ranges, p.mask_types, softmax_scale=scale)
     dq, dk, dv = ffa.flex_flash_attn_bwd(dd, qd, kd, vd, out, lse, p.q_ranges, p.k_ranges, p.mask_types,
                                          softmax_scale=scale)
     torch.cuda.synchronize()
-    return dq.cpu(), dk.cpu(), dv.cpu()
+    grads = (dq.cpu(), dk.cpu(), dv.cpu())
+    return (grads, out.cpu()) if return_out else grads
+
+
+def stored_out_bounds(p, q, k, v, dout, out, scale=None):
+    """Elementwise error bounds of dq and dk for a backward that, as flash-attention
+    backwards do, forms Dd = rowsum(dout * out) from the stored 16-bit forward output
+    (the exact O is not kept) and rounds P and dS to 16 bits for its products.
+
+    With Dd' = Dd + e (e_i = sum_d dout_id (out_id - O_id), the forward's output error
+    carried into Dd), dS' = P (dP - Dd') = dS - P e, so to first order
+    dK' - dK = -scale sum_i P_ij e_i q_i and dQ' - dQ = -scale e_i sum_j P_ij k_j.
+    The bound is the magnitude of that propagated term plus 2^-7 scale sum |dS| |q|
+    (resp. |k|) for the 16-bit roundings of P and dS (each at most 2^-9 relative,
+    with a factor-2 margin).  Only `out` comes from the library, as a measured input
+    error; P, dP and the exact O are formed here in fp64 from the same bf16 inputs."""
+    sc = (1.0 / p.head_dim ** 0.5) if scale is None else scale
+    mask = oracle.dense_mask(p.q_ranges, p.k_ranges, p.mask_types, p.total_q, p.total_k)
+    o_exact, _ = oracle.attend(q, k, v, p.q_ranges, p.k_ranges, p.mask_types, softmax_scale=scale)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    dn, on = dout.double().numpy(), out.double().numpy()
+    rep = p.heads_q // p.heads_kv
+    bq, bk = np.zeros_like(qn), np.zeros_like(kn)
+    for h in range(p.heads_q):
+        hk = h // rep
+        s = sc * (qn[:, h] @ kn[:, hk].T)
+        s[~mask] = -np.inf
+        m = s.max(1, keepdims=True)
+        m[~np.isfinite(m)] = 0.0
+        e = np.exp(s - m)
+        den = e.sum(1, keepdims=True)
+        pr = e / np.where(den > 0, den, 1.0)
+        dp = dn[:, h] @ vn[:, hk].T
+        dd = (dn[:, h] * on[:, h]).sum(1, keepdims=True)
+        err_dd = (dn[:, h] * (on[:, h] - o_exact[:, h])).sum(1, keepdims=True)
+        ds = np.abs(pr * (dp - dd))
+        bk[:, hk] += np.abs(sc * (pr * err_dd).T @ qn[:, h]) + 2.0 ** -7 * sc * (ds.T @ np.abs(qn[:, h]))
+        bq[:, h] = np.abs(sc * err_dd * (pr @ kn[:, hk])) + 2.0 ** -7 * sc * (ds @ np.abs(kn[:, hk]))
+    return bq, bk
 
 
 def rel_errors(g, ref):
@@ -54,9 +98,13 @@ def rel_errors(g, ref):
     return err.max() / scale_max, err.mean() / scale_mean, err.max()
 
 
-def compare(grads, refs, what, same_precision=None):
+def compare(grads, refs, what, same_precision=None, stored=None):
     """same_precision: PyTorch bf16 gradients of the same case (the FlagAttention rule);
-    None: the size-relative bound."""
+    None: the size-relative bound.  stored: (p, q, k, v, dout, out, scale) of the case;
+    where the same-precision rule fails for dq or dk, those are judged by
+    stored_out_bounds instead (PyTorch's autograd never sees the rounded output that a
+    flash-attention backward forms Dd from)."""
+    bounds = None
     for i, (name, g, r) in enumerate(zip(("dq", "dk", "dv"), grads, refs)):
         gn = g.double().numpy()
         assert not np.isnan(gn).any(), f"{what}: NaN in {name}"
@@ -72,8 +120,17 @@ def compare(grads, refs, what, same_precision=None):
             allow = 1e-3 * max(np.abs(r).max(), 1e-2)  # a floor for gradients that are exactly 0
             log(f"  {what} {name}: max-abs {abs_mx:.3e} (torch bf16 {et.max():.3e}), mean {err.mean():.3e} "
                 f"(torch bf16 {et.mean():.3e}), |ref| max {np.abs(r).max():.3e}")
-            assert err.max() <= 2.0 * et.max() + allow, f"{what}: {name} max error {err.max():.3e}"
-            assert err.mean() <= 2.0 * et.mean() + allow, f"{what}: {name} mean error {err.mean():.3e}"
+            if err.max() <= 2.0 * et.max() + allow and err.mean() <= 2.0 * et.mean() + allow:
+                continue
+            assert stored is not None and i < 2, f"{what}: {name} max error {err.max():.3e}"
+            if bounds is None:
+                bounds = stored_out_bounds(*stored)
+            lim = 1.01 * bounds[i] + allow
+            at = np.unravel_index(np.argmax(err), err.shape)
+            log(f"    {name}: beyond the same-precision rule; judged by the stored-out bound: max error "
+                f"{err[at]:.3e} at {tuple(int(x) for x in at)} against {lim[at]:.3e} there; "
+                f"largest error / bound {(err / lim).max():.2f}")
+            assert (err <= lim).all(), f"{what}: {name} error beyond the stored-out bound"
 
 
 def torch_bf16_grads(p, q, k, v, dout, scale=None):
@@ -104,8 +161,9 @@ def case(ffa, p, what, scale=None):
         f"slices {p.num_slices}")
     q, k, v = W.make_qkv(p)
     dout = W.make_dout(p)
-    grads = run_bwd(ffa, p, q, k, v, dout, scale)
-    compare(grads, oracle_grads(p, q, k, v, dout, scale), what, torch_bf16_grads(p, q, k, v, dout, scale))
+    grads, out = run_bwd(ffa, p, q, k, v, dout, scale, return_out=True)
+    compare(grads, oracle_grads(p, q, k, v, dout, scale), what, torch_bf16_grads(p, q, k, v, dout, scale),
+            stored=(p, q, k, v, dout, out, scale))
     return q, k, v, dout, grads
 
 
@@ -162,6 +220,17 @@ def test_bwd_rows_and_keys_that_see_nothing(gpu_lib):
     q, k, v, dout, (dq, dk, dv) = case(gpu_lib, p, "holes")
     assert (dq[:40] == 0).all() and (dq[130:] == 0).all()
     assert (dk[150:] == 0).all() and (dv[150:] == 0).all()
+
+
+def test_bwd_key_seen_by_one_row(gpu_lib):
+    # An inverse-causal slice q[0, 244) x k[274, 276): key 274 is seen by row 0 alone,
+    # so its dk is one term, scale * dS[0, 274] * q[0], and the output rounding that
+    # enters Dd (and the 16-bit P and dS) is not averaged over rows.  The same-precision
+    # rule fails on dk here (about 3.8e-3 against PyTorch's 8.6e-4, max|dk| 0.35); the
+    # stored-output bound holds.
+    p = W.random_problem(95117, 1165, 674, 1, 1, 32, n_types=4)
+    assert [list(r) for r in p.q_ranges[:1]] == [[0, 244]] and list(p.mask_types[:1]) == [2]
+    case(gpu_lib, p, "key seen by one row")
 
 
 def test_bwd_no_slices(gpu_lib):

@@ -83,7 +83,7 @@ def test_fp16_backward(gpu_lib, seed):
     assert dq.dtype == F16
     refs = oracle.attend_backward(q, k, v, dout, p.q_ranges, p.k_ranges, p.mask_types)
     compare_grads([x.cpu() for x in (dq, dk, dv)], refs, f"fp16 backward {seed}",
-                  torch_bf16_grads(p, q, k, v, dout))
+                  torch_bf16_grads(p, q, k, v, dout), stored=(p, q, k, v, dout, out.cpu(), None))
 
 
 def test_flag_attention_fp16_example_shape(gpu_lib):
